@@ -1,0 +1,484 @@
+"""Pins of the CPU oracle to facts other than itself.
+
+Each pin compares the oracle with something the pages or the mathematics
+fix: the dense XOR-masked form of the attention (LIME notes, Key design 2,
+XORA equation), library routines (torch's scaled_dot_product_attention,
+layer_norm, softmax, silu, linear in float64 on the CPU), exact identities
+(SiLU(s) - SiLU(-s) = s), closed-form special cases, brute force over
+scalars on tiny inputs, and the cache-size arithmetic of the LIME summary
+page, Table 12.  The mutation tests at the end plant plausible mistakes in
+the oracle and check that some pin fails for each.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle.lime_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _qkv(rng, rows, d, std=1.0):
+    return [rng.standard_normal((rows, d)) * std for _ in range(3)]
+
+
+def _weights(rng, d, dff, std=None):
+    s = d ** -0.5 if std is None else std
+    return {
+        "w_qkv": rng.standard_normal((3 * d, d)) * s,
+        "w_o": rng.standard_normal((d, d)) * s,
+        "w_gate": rng.standard_normal((dff, d)) * s,
+        "w_up": rng.standard_normal((dff, d)) * s,
+        "w_down": rng.standard_normal((d, dff)) * s,
+    }
+
+
+# ---------------------------------------------------------------- pin functions
+
+def pin_dense_equals_decoupled(seed=0):
+    """max |decoupled - dense| over several tiny shapes, both phis."""
+    rng = _rng(seed)
+    err = 0.0
+    for ell in (1, 3, 8):
+        for n in (0, 1, 2, 7):
+            for heads, d in ((1, 4), (2, 8)):
+                for phi in ("softmax", "silu_mean"):
+                    q, k, v = _qkv(rng, ell + n, d)
+                    a = O.xor_attention(q, k, v, ell, heads, 0.7, phi)
+                    b = O.xor_attention_dense(q, k, v, ell, heads, 0.7, phi)
+                    err = max(err, float(np.abs(a - b).max()))
+    return err
+
+
+def pin_stack_dense_equals_decoupled(seed=1):
+    """Whole multi-layer encoder: decoupled == dense-masked attention inside."""
+    rng = _rng(seed)
+    B, ell, d, heads = 3, 4, 8, 2
+    lens = np.array([5, 0, 3])
+    off = np.concatenate([[0], np.cumsum(lens)])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((int(off[-1]), d))
+    W = [_weights(rng, d, d) for _ in range(2)]
+    err = 0.0
+    for phi in ("softmax", "silu_mean"):
+        a, ha = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi)
+        b, hb = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi, dense=True)
+        err = max(err, float(np.abs(a - b).max()))
+        for x, y in zip(ha, hb):
+            if x.size:
+                err = max(err, float(np.abs(x - y).max()))
+    return err
+
+
+def pin_softmax_branches_vs_sdpa(seed=2):
+    """Each branch with softmax equals torch's scaled_dot_product_attention."""
+    rng = _rng(seed)
+    ell, n, d, heads, scale = 5, 11, 12, 3, 0.37
+    dh = d // heads
+    q, k, v = _qkv(rng, ell + n, d)
+    y = O.xor_attention(q, k, v, ell, heads, scale, "softmax")
+    err = 0.0
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+        ye = F.scaled_dot_product_attention(t(q[ell:, c]), t(k[:ell, c]), t(v[:ell, c]), scale=scale)
+        yl = F.scaled_dot_product_attention(t(q[:ell, c]), t(k[ell:, c]), t(v[ell:, c]), scale=scale)
+        err = max(err, float(np.abs(y[ell:, c] - ye.numpy()).max()))
+        err = max(err, float(np.abs(y[:ell, c] - yl.numpy()).max()))
+    return err
+
+
+def pin_silu_odd_identity(seed=3):
+    """SiLU(s) - SiLU(-s) = s, so for silu_mean each branch satisfies
+    att(Q) - att(-Q) = scale * Q K^T V / |A| (a plain linear-algebra form)."""
+    rng = _rng(seed)
+    ell, n, d, heads, scale = 4, 9, 8, 2, 0.8
+    dh = d // heads
+    q, k, v = _qkv(rng, ell + n, d, std=1.5)
+    diff = (O.xor_attention(q, k, v, ell, heads, scale, "silu_mean")
+            - O.xor_attention(-q, k, v, ell, heads, scale, "silu_mean"))
+    ref = np.zeros_like(diff)
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        ref[ell:, c] = scale * q[ell:, c] @ k[:ell, c].T @ v[:ell, c] / ell
+        ref[:ell, c] = scale * q[:ell, c] @ k[ell:, c].T @ v[ell:, c] / n
+    return float(np.abs(diff - ref).max())
+
+
+def _torch_layer(x, lw, ell, heads, scale, phi):
+    """One layer from torch library routines (float64, CPU)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    x = t(x)
+    d = x.shape[1]
+    dh = d // heads
+    h = F.layer_norm(x, (d,), eps=1e-5)
+    qkv = F.linear(h, t(lw["w_qkv"]))
+    q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
+    y = torch.zeros_like(x)
+    for hd in range(heads):
+        c = slice(hd * dh, (hd + 1) * dh)
+        for rows, keys in ((slice(ell, None), slice(0, ell)), (slice(0, ell), slice(ell, None))):
+            qq, kk, vv = q[rows, c], k[keys, c], v[keys, c]
+            if kk.shape[0] == 0:
+                continue
+            if phi == "softmax":
+                y[rows, c] = F.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+            else:
+                y[rows, c] = F.silu(scale * qq @ kk.T) @ vv / kk.shape[0]
+    x = x + F.linear(y, t(lw["w_o"]))
+    g = F.layer_norm(x, (d,), eps=1e-5)
+    x = x + F.linear(F.silu(F.linear(g, t(lw["w_gate"]))) * F.linear(g, t(lw["w_up"])), t(lw["w_down"]))
+    return x.numpy()
+
+
+def pin_layer_vs_torch(seed=4):
+    rng = _rng(seed)
+    err = 0.0
+    for ell, n, d, dff, heads in ((3, 6, 8, 8, 2), (2, 0, 4, 8, 1), (4, 1, 12, 6, 3)):
+        x = rng.standard_normal((ell + n, d))
+        lw = _weights(rng, d, dff)
+        for phi in ("softmax", "silu_mean"):
+            a = O.xor_layer(x, lw, ell, heads, 0.6, phi)
+            b = _torch_layer(x, lw, ell, heads, 0.6, phi)
+            err = max(err, float(np.abs(a - b).max()))
+    return err
+
+
+def _brute_layer(x, lw, ell, heads, scale, phi):
+    """One layer by scalar loops (tiny inputs only)."""
+    rows, d = len(x), len(x[0])
+    dh = d // heads
+
+    def ln(r):
+        mu = sum(r) / d
+        var = sum((u - mu) ** 2 for u in r) / d
+        return [(u - mu) / math.sqrt(var + 1e-5) for u in r]
+
+    def mv(W, r):
+        return [sum(W[o][i] * r[i] for i in range(len(r))) for o in range(len(W))]
+
+    def sig(u):
+        return 1.0 / (1.0 + math.exp(-u))
+
+    h = [ln(list(r)) for r in x]
+    qkv = [mv(lw["w_qkv"], r) for r in h]
+    y = [[0.0] * d for _ in range(rows)]
+    for i in range(rows):
+        allowed = [j for j in range(rows) if (i < ell) != (j < ell)]
+        if not allowed:
+            continue
+        for hd in range(heads):
+            cs = range(hd * dh, (hd + 1) * dh)
+            s = [scale * sum(qkv[i][c] * qkv[j][d + c] for c in cs) for j in allowed]
+            if phi == "softmax":
+                m = max(s)
+                e = [math.exp(u - m) for u in s]
+                w = [u / sum(e) for u in e]
+            else:
+                w = [u * sig(u) / len(allowed) for u in s]
+            for c in cs:
+                y[i][c] = sum(w[t] * qkv[allowed[t]][2 * d + c] for t in range(len(allowed)))
+    x2 = [[x[i][c] + mv(lw["w_o"], y[i])[c] for c in range(d)] for i in range(rows)]
+    out = []
+    for r in x2:
+        g = ln(r)
+        gate, up = mv(lw["w_gate"], g), mv(lw["w_up"], g)
+        mid = [gate[t] * sig(gate[t]) * up[t] for t in range(len(gate))]
+        dn = mv(lw["w_down"], mid)
+        out.append([r[c] + dn[c] for c in range(d)])
+    return np.array(out)
+
+
+def pin_layer_brute_force(seed=5):
+    rng = _rng(seed)
+    err = 0.0
+    for ell, n, d, dff, heads in ((2, 3, 4, 4, 2), (3, 2, 6, 4, 3)):
+        x = rng.standard_normal((ell + n, d))
+        lw = _weights(rng, d, dff)
+        lwl = {k: v.tolist() for k, v in lw.items()}
+        for phi in ("softmax", "silu_mean"):
+            a = O.xor_layer(x, lw, ell, heads, 0.9, phi)
+            b = _brute_layer(x.tolist(), lwl, ell, heads, 0.9, phi)
+            err = max(err, float(np.abs(a - b).max()))
+    return err
+
+
+def pin_cache_vs_torch(seed=6):
+    """softmax cache == torch.softmax of the per-head logits; silu_mean
+    cache == F.silu(logits) / ell; logits from an einsum over d."""
+    rng = _rng(seed)
+    n, d, H, ell, scale = 37, 16, 3, 5, 0.45
+    T = rng.standard_normal((n, d))
+    K = rng.standard_normal((H, ell, d))
+    logits = torch.einsum("nd,hkd->nhk", torch.from_numpy(T), torch.from_numpy(K)) * scale
+    err = float(np.abs(O.qk_cache_build(T, K, scale, "softmax") - torch.softmax(logits, -1).numpy()).max())
+    err = max(err, float(np.abs(O.qk_cache_build(T, K, scale, "silu_mean")
+                                - (F.silu(logits) / ell).numpy()).max()))
+    return err
+
+
+def pin_cache_silu_odd(seed=7):
+    rng = _rng(seed)
+    n, d, H, ell, scale = 20, 8, 2, 6, 0.9
+    T = rng.standard_normal((n, d)) * 2
+    K = rng.standard_normal((H, ell, d))
+    diff = O.qk_cache_build(T, K, scale, "silu_mean") - O.qk_cache_build(-T, K, scale, "silu_mean")
+    ref = np.stack([scale * T @ K[h].T / ell for h in range(H)], axis=1)
+    return float(np.abs(diff - ref).max())
+
+
+def _brute_cand(cache, lp, ids, off, n_items):
+    B, ell, d = lp.shape
+    H = cache.shape[1]
+    dh = d // H
+    out = np.zeros((len(ids), d))
+    bad = 0
+    for b in range(B):
+        for i in range(off[b], off[b + 1]):
+            m = int(ids[i])
+            if not 0 <= m < n_items:
+                bad += 1
+                continue
+            for c in range(d):
+                h = c // dh
+                out[i, c] = sum(cache[m, h, k] * lp[b, k, c] for k in range(ell))
+    return out, bad
+
+
+def pin_cand_brute_force(seed=8):
+    rng = _rng(seed)
+    n, B, ell, d, H = 50, 3, 4, 6, 2
+    cache = rng.standard_normal((n, H, ell))
+    lp = rng.standard_normal((B, ell, d))
+    ids = rng.integers(-3, n + 3, size=23)
+    off = np.array([0, 9, 9, 23])
+    a, ba = O.cand_score(cache, lp, ids, off)
+    b, bb = _brute_cand(cache, lp, ids, off, n)
+    return float(np.abs(a - b).max()) + abs(ba - bb)
+
+
+ALL_PINS = {
+    "dense_equals_decoupled": (pin_dense_equals_decoupled, 1e-12),
+    "stack_dense_equals_decoupled": (pin_stack_dense_equals_decoupled, 1e-11),
+    "softmax_branches_vs_sdpa": (pin_softmax_branches_vs_sdpa, 1e-12),
+    "silu_odd_identity": (pin_silu_odd_identity, 1e-11),
+    "layer_vs_torch": (pin_layer_vs_torch, 1e-11),
+    "layer_brute_force": (pin_layer_brute_force, 1e-11),
+    "cache_vs_torch": (pin_cache_vs_torch, 1e-12),
+    "cache_silu_odd": (pin_cache_silu_odd, 1e-12),
+    "cand_brute_force": (pin_cand_brute_force, 1e-12),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ALL_PINS))
+def test_pin(name):
+    fn, tol = ALL_PINS[name]
+    err = fn()
+    assert err <= tol, f"{name}: {err}"
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_cache_uniform_when_all_keys_equal():
+    rng = _rng(10)
+    T = rng.standard_normal((9, 8))
+    K = np.repeat(rng.standard_normal((2, 1, 8)), 5, axis=1)
+    c = O.qk_cache_build(T, K, 0.5, "softmax")
+    assert np.abs(c - 1 / 5).max() < 1e-15
+    s = O.qk_cache_build(T, K, 0.5, "silu_mean")
+    assert np.abs(s - s[:, :, :1]).max() == 0.0
+
+
+def test_softmax_rows_sum_to_one():
+    rng = _rng(11)
+    c = O.qk_cache_build(rng.standard_normal((30, 8)) * 3, rng.standard_normal((3, 7, 8)), 1.0, "softmax")
+    assert np.abs(c.sum(-1) - 1).max() < 1e-14 and (c >= 0).all()
+
+
+def test_single_link_softmax_returns_links():
+    """ell = 1 with softmax: every cached weight is 1, so O_i = L^P_b."""
+    rng = _rng(12)
+    cache = O.qk_cache_build(rng.standard_normal((40, 6)), rng.standard_normal((3, 1, 6)), 0.7, "softmax")
+    assert np.all(cache == 1.0)
+    lp = rng.standard_normal((2, 1, 6))
+    ids = rng.integers(0, 40, size=10)
+    out, bad = O.cand_score(cache, lp, ids, np.array([0, 4, 10]))
+    assert bad == 0
+    assert np.abs(out[:4] - lp[0, 0]).max() < 1e-15 and np.abs(out[4:] - lp[1, 0]).max() < 1e-15
+
+
+def test_single_history_row_softmax():
+    """N_b = 1 with softmax: each link's attention output is v of that row."""
+    rng = _rng(13)
+    q, k, v = _qkv(rng, 6, 8)
+    y = O.xor_attention(q, k, v, 5, 2, 0.3, "softmax")
+    assert np.abs(y[:5] - v[5]).max() < 1e-15
+
+
+def test_empty_history_branch_is_zero():
+    rng = _rng(14)
+    q, k, v = _qkv(rng, 4, 8)
+    for phi in ("softmax", "silu_mean"):
+        assert np.all(O.xor_attention(q, k, v, 4, 2, 0.3, phi) == 0.0)
+        assert np.all(O.xor_attention_dense(q, k, v, 4, 2, 0.3, phi) == 0.0)
+
+
+def test_xor_mask_blocks():
+    m = O.xor_mask(2, 5)
+    assert not m[:2, :2].any() and not m[2:, 2:].any() and m[:2, 2:].all() and m[2:, :2].all()
+
+
+def test_layer_identity_when_projections_zero():
+    """W_o = 0 and W_down = 0 make the layer the identity (residual only)."""
+    rng = _rng(15)
+    lw = _weights(rng, 8, 8)
+    lw["w_o"][:] = 0
+    lw["w_down"][:] = 0
+    x = rng.standard_normal((7, 8))
+    assert np.all(O.xor_layer(x, lw, 3, 2, 0.5, "silu_mean") == x)
+
+
+def test_history_permutation_invariance():
+    """No history<->history and no positional term: permuting one user's
+    history leaves L^P unchanged and permutes the history outputs."""
+    rng = _rng(16)
+    B, ell, d, heads = 2, 3, 8, 2
+    off = np.array([0, 6, 10])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((10, d))
+    W = [_weights(rng, d, d) for _ in range(2)]
+    perm = np.concatenate([rng.permutation(6), 6 + rng.permutation(4)])
+    for phi in ("softmax", "silu_mean"):
+        a, ha = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi)
+        b, hb = O.xor_fwd(lc, hs[perm], off, W, heads, 0.5, phi)
+        assert np.abs(a - b).max() < 1e-12
+        assert np.abs(ha[0][perm[:6]] - hb[0]).max() < 1e-12
+
+
+def test_users_independent():
+    rng = _rng(17)
+    B, ell, d = 3, 2, 4
+    off = np.array([0, 3, 5, 9])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((9, d))
+    W = [_weights(rng, d, d)]
+    a, _ = O.xor_fwd(lc, hs, off, W, 1, 0.5, "softmax")
+    b, _ = O.xor_fwd(lc[1:2], hs[3:5], np.array([0, 2]), W, 1, 0.5, "softmax")
+    assert np.array_equal(a[1], b[0])
+
+
+def test_candidate_independence_and_bad_ids():
+    rng = _rng(18)
+    n, B, ell, d, H = 30, 2, 4, 8, 2
+    cache = rng.standard_normal((n, H, ell))
+    lp = rng.standard_normal((B, ell, d))
+    ids = rng.integers(0, n, size=12)
+    off = np.array([0, 5, 12])
+    full, bad = O.cand_score(cache, lp, ids, off)
+    assert bad == 0
+    # one candidate alone
+    one, _ = O.cand_score(cache, lp[1:2], ids[7:8], np.array([0, 1]))
+    assert np.array_equal(one[0], full[7])
+    # permuted and duplicated candidate lists
+    p = rng.permutation(7) + 5
+    dup = np.concatenate([ids[p], ids[p[:3]]])
+    pd, _ = O.cand_score(cache, lp[1:2], dup, np.array([0, len(dup)]))
+    assert np.array_equal(pd[:7], full[p]) and np.array_equal(pd[7:], full[p[:3]])
+    # out-of-range ids: zero rows, counted
+    bad_ids = ids.copy()
+    bad_ids[[1, 8]] = [-1, n]
+    o2, nb = O.cand_score(cache, lp, bad_ids, off)
+    assert nb == 2 and np.all(o2[[1, 8]] == 0) and np.array_equal(np.delete(o2, [1, 8], 0), np.delete(full, [1, 8], 0))
+
+
+def test_cached_equals_recomputed():
+    """Cached weights of a sampled id equal phi(scale K_L T_m) computed fresh
+    for that item alone."""
+    rng = _rng(19)
+    T = rng.standard_normal((100, 8))
+    K = rng.standard_normal((2, 4, 8))
+    c = O.qk_cache_build(T, K, 0.5, "silu_mean")
+    for m in (0, 17, 99):
+        # equal up to the BLAS kernel's summation order
+        assert np.abs(c[m] - O.qk_cache_build(T[m:m + 1], K, 0.5, "silu_mean")[0]).max() < 1e-15
+
+
+def test_cache_size_matches_table12():
+    """Cache bytes = items * heads * ell * bytes/elem reproduce the int8 cache
+    sizes printed in the LIME summary page, Table 12 (100M items, 4 heads)."""
+    with open(os.path.join(GOLDEN, "table12_int8_cache_size.json")) as f:
+        g = json.load(f)
+    rng = _rng(20)
+    for ell_s, gb in g["int8_cache_gb_by_links"].items():
+        ell = int(ell_s)
+        c = O.qk_cache_build(rng.standard_normal((3, 8)), rng.standard_normal((g["heads"], ell, 8)), 1.0, "softmax")
+        per_item = c.shape[1] * c.shape[2]  # one weight per (head, link)
+        assert per_item * g["items"] * g["bytes_per_weight"] / 1e9 == pytest.approx(gb, rel=1e-9)
+
+
+# ---------------------------------------------------------------- mutation tests
+
+def _mutations():
+    def silu_norm_off(s, phi):
+        n = s.shape[-1]
+        if phi == "silu_mean" and n:
+            return O.silu(s) / (n + 1)
+        return ORIG["phi_weights"](s, phi)
+
+    def no_max_shift_wrong_sum(s, phi):
+        if phi == "softmax" and s.shape[-1]:
+            e = np.exp(s)
+            return e / (e.sum(axis=-1, keepdims=True) + 1e-3)
+        return ORIG["phi_weights"](s, phi)
+
+    def ln_unbiased(x, eps=1e-5):
+        mu = x.mean(axis=-1, keepdims=True)
+        return (x - mu) / np.sqrt(x.var(axis=-1, ddof=1, keepdims=True) + eps)
+
+    def attend_wrong_scale(q, k, v, scale, phi):
+        return ORIG["attend"](q, k, v, 1.0, phi)
+
+    def attend_transposed_v(q, k, v, scale, phi):
+        if k.shape[0] == 0:
+            return np.zeros((q.shape[0], v.shape[1]))
+        w = ORIG["phi_weights"](scale * (q @ k.T), phi)
+        return w @ v[::-1]
+
+    def silu_sign(s):
+        return -s * O._sigmoid(-s)
+
+    return {
+        "silu normaliser off by one": ("phi_weights", silu_norm_off),
+        "softmax denominator perturbed": ("phi_weights", no_max_shift_wrong_sum),
+        "LayerNorm with unbiased variance": ("layer_norm", ln_unbiased),
+        "attention scale dropped": ("attend", attend_wrong_scale),
+        "values taken from the wrong rows": ("attend", attend_transposed_v),
+        "SiLU sign error": ("silu", silu_sign),
+    }
+
+
+ORIG = {k: getattr(O, k) for k in ("phi_weights", "layer_norm", "attend", "silu")}
+
+
+@pytest.mark.parametrize("name", sorted(_mutations()))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = _mutations()[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin, (f, tol) in ALL_PINS.items():
+        try:
+            err = f()
+        except Exception:
+            err = float("inf")
+        if not err <= tol:
+            failed.append(pin)
+    assert failed, f"no pin caught: {name}"
