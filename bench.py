@@ -1,0 +1,227 @@
+"""Benchmark of the LIME inference hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  lime_xor_fwd        (user encoder, all B users, all layers)
+  lime_qk_cache_build (QK cache over the whole catalogue)
+  lime_cand_score     (all B*M candidates)
+Inputs are resident in HBM before the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload ctr] [--no-cpu-baseline]
+
+Prints ONE JSON line.  `value` = candidates scored per second of whole-step
+time; users encoded/s and items cached/s are reported alongside.  The
+`roofline` object is for the kernel with the largest share of step time,
+measured with HIP events on the launch stream over a second pass of the
+same K steps; `cpu_baseline` is the CPU oracle timed on a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ctr")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards users and catalogue rows with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import decoupled_linear_link_amd as L
+
+    w = W.workload(args.workload)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
+    es = 4 if w.dtype == "f32" else 2
+    scale = W.scale_for(w)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    # ---- inputs, resident in HBM
+    ui = W.user_inputs(w)
+    ci = W.cache_inputs(w)
+    ids = W.candidate_ids(w)
+    coff = W.candidate_offsets(w)
+    off = ui["hist_offsets"]
+    total_N = int(off[-1])
+    max_N = int(np.diff(off).max())
+    lc, hs, hoff = dev(ui["links_ctx"]), dev(ui["hist"]), dev(off)
+    wts = [{k: dev(v) for k, v in lw.items()} for lw in ui["weights"]]
+    items, keys = dev(ci["items"]), dev(ci["link_keys"])
+    ids_d, coff_d = dev(ids), dev(coff)
+    lp = torch.empty_like(lc)
+    cache = torch.empty((w.n_items, w.heads, w.ell), dtype=dt, device="cuda")
+    out = torch.empty((len(ids), w.d), dtype=dt, device="cuda")
+    ws_bytes = L.xor_fwd_workspace_size(dt, w.B, w.ell, w.d, w.heads, w.dff, total_N, max_N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def user():
+        L.xor_fwd(lc, hs, hoff, wts, heads=w.heads, phi=w.phi, scale=scale, max_N=max_N,
+                  links_pers=lp, workspace=ws, stream=stream)
+
+    def build():
+        L.qk_cache_build(items, keys, phi=w.phi, scale=scale, cache=cache, stream=stream)
+
+    def score():
+        L.cand_score(cache, lp, ids_d, coff_d, out=out, stream=stream)
+
+    def step():
+        user()
+        build()
+        score()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    # ---- per-call breakdown with HIP events on the launch stream
+    calls = {"lime_xor_fwd": user, "lime_qk_cache_build": build, "lime_cand_score": score}
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for k in calls}
+    for i in range(args.steps):
+        for k, fn in calls.items():
+            ev[k][i][0].record(stream)
+            fn()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in calls}
+
+    # algorithmic bytes / flops per launch of the single-kernel calls
+    n_cand = len(ids)
+    algo = {
+        "lime_qk_cache_build": dict(kernel="qk_cache_build", bytes=w.n_items * (w.d + w.heads * w.ell) * es,
+                                    flops=2.0 * w.n_items * w.d * w.heads * w.ell),
+        "lime_cand_score": dict(kernel="cand_score", bytes=n_cand * (w.heads * w.ell * es + w.d * es + 8),
+                                flops=2.0 * n_cand * w.ell * w.d),
+    }
+    single = {k: v for k, v in call_ms.items() if k in algo}
+    dom = max(single, key=single.get)
+    a = algo[dom]
+    t = single[dom] * 1e-3
+    achieved = a["bytes"] / t / 1e9
+    roofline = {"kernel": a["kernel"], "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_launch_us": round(single[dom] * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(a["bytes"])}
+
+    res = {
+        "metric": "candidates scored/sec + user histories encoded/sec; % HBM/MFMA roofline",
+        "value": n_cand / (ms_step * 1e-3),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and id law of the workload)",
+        "config": {"workload": f"{w.name}: B={w.B} users, N={w.N}, ell={w.ell}, d={w.d}, "
+                               f"heads={w.heads}, layers={w.layers}, catalogue={w.n_items}, "
+                               f"M={w.M}/user, zipf={w.zipf}, phi={w.phi}",
+                   "users": w.B, "history_rows": total_N, "catalogue_items": w.n_items,
+                   "candidates": n_cand},
+        "users_per_s": w.B / (ms_step * 1e-3),
+        "items_per_s": w.n_items / (ms_step * 1e-3),
+        "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, ui, ci, ids, coff, scale, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload;
+    per-part rates are scaled to one whole step."""
+    import oracle.lime_oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    off = ui["hist_offsets"]
+    frac = 1.0 / 3.0
+    # users: a prefix of users
+    nu = max(1, min(w.B, 8))
+    t0 = time.perf_counter()
+    O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, scale, w.phi, users=range(nu))
+    t_user = (time.perf_counter() - t0) / nu
+    nu2 = int(min(w.B, max(nu, budget_s * frac / max(t_user, 1e-9))))
+    if nu2 > nu:
+        t0 = time.perf_counter()
+        O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, scale, w.phi, users=range(nu2))
+        t_user = (time.perf_counter() - t0) / nu2
+        nu = nu2
+    # items: a prefix of the catalogue
+    ni = min(w.n_items, 20000)
+    t0 = time.perf_counter()
+    O.qk_cache_build(ci["items"][:ni], ci["link_keys"], scale, w.phi)
+    t_item = (time.perf_counter() - t0) / ni
+    ni2 = int(min(w.n_items, max(ni, budget_s * frac / max(t_item, 1e-12))))
+    if ni2 > ni:
+        t0 = time.perf_counter()
+        c = O.qk_cache_build(ci["items"][:ni2], ci["link_keys"], scale, w.phi)
+        t_item = (time.perf_counter() - t0) / ni2
+        ni = ni2
+    else:
+        c = O.qk_cache_build(ci["items"][:ni], ci["link_keys"], scale, w.phi)
+    # candidates: the first users' candidates, ids folded into the sampled rows
+    lp = W.links_pers(w)
+    nc_users = max(1, min(w.B, int(budget_s * frac / 1e-3 / max(1, w.M)) or 1))
+    t0 = time.perf_counter()
+    O.cand_score(c, lp[:nc_users], ids[: coff[nc_users]] % ni, coff[: nc_users + 1])
+    t_cand = (time.perf_counter() - t0) / max(1, int(coff[nc_users]))
+    n_cand = len(ids)
+    t_step = t_user * w.B + t_item * w.n_items + t_cand * n_cand
+    return {"value": n_cand / t_step, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{nu} users, {ni} catalogue items, {int(coff[nc_users])} candidates; "
+                      "per-part times scaled to one whole step",
+            "users_per_s": 1.0 / t_user, "items_per_s": 1.0 / t_item,
+            "candidates_per_s": 1.0 / t_cand}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+"""Python binding of liblime.so, the LIME inference hot path for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of liblime.so.  Tensors are torch device tensors; calls enqueue on
+torch's current stream and return without synchronising.  The functions
+mirror the C ABI in include/lime.h:
+
+    xor_fwd          -> lime_xor_fwd          (user side, LIME-XOR layers)
+    qk_cache_build   -> lime_qk_cache_build   (offline QK cache)
+    cand_score       -> lime_cand_score       (online candidate scoring)
+
+Importing works without a GPU (the library loads); calling needs one.
+There is no fallback: if the library is missing the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "qk_cache_build",
+    "cand_score", "PHI", "DTYPE", "EXPORTED",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "_lib", "liblime.so")
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        f"{lib_path} is missing: build it first with "
+        "`python -m decoupled_linear_link_amd.build` (hipcc, gfx950)")
+
+lib = ctypes.CDLL(lib_path)
+
+PHI = {"softmax": 0, "silu_mean": 1}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
+          3: "LIME_ERR_WORKSPACE", 4: "LIME_ERR_HIP"}
+
+# every symbol include/lime.h declares
+EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_workspace_size", "lime_qk_cache_build",
+            "lime_cand_score", "lime_status_string", "lime_last_error")
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+lib.lime_status_string.restype = ctypes.c_char_p
+lib.lime_status_string.argtypes = [ctypes.c_int]
+lib.lime_last_error.restype = ctypes.c_char_p
+lib.lime_last_error.argtypes = []
+lib.lime_xor_fwd_workspace_size.restype = ctypes.c_size_t
+lib.lime_xor_fwd_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i64, _i32]
+lib.lime_xor_fwd.restype = ctypes.c_int
+lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32, _i32, _i32, _i32,
+                             _vp, _vp, _vp, _i64, _i32, ctypes.POINTER(LayerWeights), _vp, _vp,
+                             _vp, ctypes.c_size_t, _vp]
+lib.lime_qk_cache_build.restype = ctypes.c_int
+lib.lime_qk_cache_build.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i64, _i32, _i32, _i32,
+                                    _vp, _vp, _vp, _vp]
+lib.lime_cand_score.restype = ctypes.c_int
+lib.lime_cand_score.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp,
+                                _i64, _vp, _vp, _vp]
+
+
+class LimeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.lime_last_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise LimeError(st, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype(t):
+    try:
+        return DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _want(t, name, dtype=None, dims=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {t.dim()}")
+
+
+def xor_fwd_workspace_size(dtype, B, ell, d, heads, d_ff, total_N, max_N) -> int:
+    return int(lib.lime_xor_fwd_workspace_size(DTYPE[dtype], B, ell, d, heads, d_ff, total_N, max_N))
+
+
+def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
+            scale: float | None = None, max_N: int | None = None, want_hist: bool = False,
+            links_pers=None, hist_out=None, workspace=None, stream=None):
+    """Stacked LIME-XOR layers.  links_ctx [B, ell, d], hist [total_N, d],
+    hist_offsets [B+1] int64 (device), weights: list of per-layer dicts with
+    w_qkv [3d, d], w_o [d, d], w_gate/w_up [d_ff, d], w_down [d, d_ff].
+    Returns (links_pers [B, ell, d], hist_out [total_N, d] or None)."""
+    _want(links_ctx, "links_ctx", dims=3)
+    dt = links_ctx.dtype
+    _want(hist, "hist", dt, 2)
+    _want(hist_offsets, "hist_offsets", torch.int64, 1)
+    B, ell, d = links_ctx.shape
+    if hist.shape[1] != d or hist_offsets.shape[0] != B + 1:
+        raise ValueError("shape mismatch between links_ctx, hist and hist_offsets")
+    total_N = hist.shape[0]
+    if max_N is None:
+        lens = hist_offsets.diff()
+        max_N = int(lens.max().item()) if B > 0 else 0
+    layers = len(weights)
+    d_ff = weights[0]["w_gate"].shape[0] if layers else d
+    arr = (LayerWeights * max(1, layers))()
+    for i, lw in enumerate(weights):
+        for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
+            _want(lw[k], f"weights[{i}].{k}", dt, 2)
+        arr[i] = LayerWeights(*(lw[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down")))
+    if scale is None:
+        scale = (d // heads) ** -0.5
+    if links_pers is None:
+        links_pers = torch.empty_like(links_ctx)
+    if want_hist and hist_out is None:
+        hist_out = torch.empty_like(hist)
+    need = xor_fwd_workspace_size(dt, B, ell, d, heads, d_ff, total_N, max_N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=links_ctx.device)
+    _check(lib.lime_xor_fwd(DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
+                            _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
+                            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel(),
+                            _stream(stream)), "lime_xor_fwd")
+    return links_pers, hist_out
+
+
+def qk_cache_build(items, link_keys, phi: str = "silu_mean", scale: float | None = None,
+                   cache=None, stream=None):
+    """QK cache [n_items, heads, ell] from items [n_items, d] and link_keys
+    [heads, ell, d]."""
+    _want(items, "items", dims=2)
+    _want(link_keys, "link_keys", items.dtype, 3)
+    n, d = items.shape
+    H, ell, d2 = link_keys.shape
+    if d2 != d:
+        raise ValueError("items and link_keys disagree on d")
+    if scale is None:
+        scale = (d // H) ** -0.5 if d % H == 0 else d ** -0.5
+    if cache is None:
+        cache = torch.empty((n, H, ell), dtype=items.dtype, device=items.device)
+    _check(lib.lime_qk_cache_build(_dtype(items), PHI[phi], scale, n, d, H, ell, _ptr(items),
+                                   _ptr(link_keys), _ptr(cache), _stream(stream)),
+           "lime_qk_cache_build")
+    return cache
+
+
+def cand_score(cache, links_pers, cand_ids, cand_offsets, out=None, bad_id_count=None,
+               stream=None):
+    """Scores [total_M, d] for candidates cand_ids [total_M] (int64) split by
+    cand_offsets [B+1] (int64) over users with links_pers [B, ell, d]."""
+    _want(cache, "cache", dims=3)
+    _want(links_pers, "links_pers", cache.dtype, 3)
+    _want(cand_ids, "cand_ids", torch.int64, 1)
+    _want(cand_offsets, "cand_offsets", torch.int64, 1)
+    n_items, H, ell = cache.shape
+    B, ell2, d = links_pers.shape
+    if ell2 != ell or cand_offsets.shape[0] != B + 1:
+        raise ValueError("shape mismatch between cache, links_pers and cand_offsets")
+    M = cand_ids.shape[0]
+    if out is None:
+        out = torch.empty((M, d), dtype=cache.dtype, device=cache.device)
+    if bad_id_count is not None:
+        _want(bad_id_count, "bad_id_count", torch.int32)
+    _check(lib.lime_cand_score(_dtype(cache), B, ell, d, H, _ptr(cache), n_items, _ptr(links_pers),
+                               _ptr(cand_ids), _ptr(cand_offsets), M, _ptr(out),
+                               _ptr(bad_id_count), _stream(stream)), "lime_cand_score")
+    return out

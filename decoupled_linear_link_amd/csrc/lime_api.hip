@@ -1,0 +1,303 @@
+// C ABI of the LIME hot path: argument validation, launch planning and the
+// kernel launches.  Every check that the host can make happens before the
+// first launch, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "lime.h"
+#include "common.h"
+#include "generic_kernels.h"
+#include "mfma_kernels.h"
+
+using namespace lime;
+
+namespace {
+
+thread_local std::string g_err;
+
+lime_status_t fail(lime_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+lime_status_t ok() {
+  g_err.clear();
+  return LIME_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+#define LIME_CHECK_LAUNCH(what)                                                          \
+  do {                                                                                   \
+    hipError_t e_ = hipGetLastError();                                                   \
+    if (e_ != hipSuccess)                                                                \
+      return fail(LIME_ERR_HIP, "%s: %s", what, hipGetErrorString(e_));                  \
+  } while (0)
+
+bool dh_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
+
+// ---------------------------------------------------------------------------
+// lime_xor_fwd planning
+// ---------------------------------------------------------------------------
+struct XorPlan {
+  int64_t nlr = 0, R = 0;  // link rows, all rows
+  int S = 1;               // history splits per user
+  int64_t chunk = 1;       // history rows per split
+  size_t o_x = 0, o_qkv = 0, o_y = 0, o_h = 0, o_part = 0, total = 0;
+};
+
+lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
+                          int32_t d_ff, int64_t total_N, int32_t max_N) {
+  if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+  if (B < 1) return fail(LIME_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  if (ell < 1) return fail(LIME_ERR_INVALID_ARG, "ell must be >= 1 (got %d)", ell);
+  if (d < 1 || heads < 1) return fail(LIME_ERR_INVALID_ARG, "d and heads must be >= 1");
+  if (d % heads != 0) return fail(LIME_ERR_INVALID_ARG, "d (%d) must be a multiple of heads (%d)", d, heads);
+  if (d_ff < 1) return fail(LIME_ERR_INVALID_ARG, "d_ff must be >= 1");
+  if (total_N < 0 || max_N < 0) return fail(LIME_ERR_INVALID_ARG, "total_N and max_N must be >= 0");
+  if (ell > 256) return fail(LIME_ERR_UNSUPPORTED, "ell > 256 unsupported (got %d)", ell);
+  if (d % 8 != 0 || d > 1024) return fail(LIME_ERR_UNSUPPORTED, "d must be a multiple of 8 and <= 1024 (got %d)", d);
+  if (d_ff % 8 != 0 || d_ff > 4096) return fail(LIME_ERR_UNSUPPORTED, "d_ff must be a multiple of 8 and <= 4096 (got %d)", d_ff);
+  if (!dh_supported(d / heads)) return fail(LIME_ERR_UNSUPPORTED, "d/heads must be 16, 32, 64 or 128 (got %d)", d / heads);
+  return LIME_OK;
+}
+
+XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
+                 int32_t d_ff, int64_t total_N, int32_t max_N) {
+  XorPlan p;
+  const size_t es = dtype == LIME_F32 ? 4 : 2;
+  p.nlr = static_cast<int64_t>(B) * ell;
+  p.R = p.nlr + total_N;
+  // enough splits that B*heads*S work items cover the chip, each split
+  // holding at least a few hundred history rows
+  int64_t S = (static_cast<int64_t>(max_N) + 511) / 512;
+  if (S < 1) S = 1;
+  if (S > 64) S = 64;
+  p.S = static_cast<int>(S);
+  p.chunk = (static_cast<int64_t>(max_N) + S - 1) / S;
+  if (p.chunk < 1) p.chunk = 1;
+  const int dh = d / heads;
+  size_t off = 0;
+  p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+  p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R) * 3 * d * es);
+  p.o_y = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+  p.o_h = off;    off = up256(off + static_cast<size_t>(p.R) * d_ff * es);
+  p.o_part = off; off = up256(off + static_cast<size_t>(B) * heads * p.S * ell * (dh + 2) * 4);
+  p.total = off;
+  return p;
+}
+
+template <typename T, int DH>
+lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int B, int ell,
+                              int d, int H, int layers, int d_ff, const void* links_ctx,
+                              const void* hist, const int64_t* off, int64_t total_N,
+                              const lime_layer_weights_t* w, void* links_pers, void* hist_out,
+                              char* ws, hipStream_t st) {
+  using namespace gen;
+  T* X = reinterpret_cast<T*>(ws + P.o_x);
+  T* QKV = reinterpret_cast<T*>(ws + P.o_qkv);
+  T* Y = reinterpret_cast<T*>(ws + P.o_y);
+  T* Hm = reinterpret_cast<T*>(ws + P.o_h);
+  float* part = reinterpret_cast<float*>(ws + P.o_part);
+  const int64_t nlr = P.nlr, R = P.R;
+  const Rows Xws{X, X + nlr * d, nlr, d};
+  const Rows QKVr{QKV, QKV + nlr * 3 * d, nlr, 3 * static_cast<int64_t>(d)};
+  const Rows Yr{Y, Y + nlr * d, nlr, d};
+  const Rows Hr{Hm, Hm + nlr * d_ff, nlr, d_ff};
+  const Rows none{nullptr, nullptr, 0, 0};
+  const dim3 blk(256);
+  auto gx = [](int64_t rows) { return static_cast<unsigned>((rows + GB_M - 1) / GB_M); };
+  auto gy = [](int cols) { return static_cast<unsigned>((cols + GB_N - 1) / GB_N); };
+
+  for (int l = 0; l < layers; ++l) {
+    const bool last = (l == layers - 1);
+    const bool full = !last || hist_out != nullptr;
+    const int64_t rows_post = full ? R : nlr;
+    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, d} : Xws;
+    const Rows Xfinal = last ? Rows{links_pers, hist_out, nlr, d} : Xws;
+    const T* Wqkv = static_cast<const T*>(w[l].w_qkv);
+
+    hipLaunchKernelGGL((gemm_rows<T, true, EPI_STORE>), dim3(gx(R), gy(3 * d)), blk, 0, st, Xin,
+                       int64_t(0), R, d, Wqkv, nullptr, 3 * d, none, QKVr);
+    LIME_CHECK_LAUNCH("qkv projection");
+    hipLaunchKernelGGL((xor_attn<T, DH>), dim3(B, H, P.S), blk, 0, st, QKV, Y, part, off, B, ell,
+                       d, H, P.S, P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0);
+    LIME_CHECK_LAUNCH("xor attention");
+    {
+      const int64_t n = static_cast<int64_t>(B) * H * ell * DH;
+      hipLaunchKernelGGL((xor_combine<T, DH>), dim3(static_cast<unsigned>((n + 255) / 256)), blk, 0,
+                         st, part, Y, B, ell, d, H, P.S);
+      LIME_CHECK_LAUNCH("xor combine");
+    }
+    hipLaunchKernelGGL((gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
+                       Yr, int64_t(0), rows_post, d, static_cast<const T*>(w[l].w_o), nullptr, d,
+                       Xin, Xws);
+    LIME_CHECK_LAUNCH("output projection");
+    hipLaunchKernelGGL((gemm_rows<T, true, EPI_SWIGLU>), dim3(gx(rows_post), gy(d_ff)), blk, 0,
+                       st, Xws, int64_t(0), rows_post, d, static_cast<const T*>(w[l].w_gate),
+                       static_cast<const T*>(w[l].w_up), d_ff, none, Hr);
+    LIME_CHECK_LAUNCH("gated mlp up");
+    hipLaunchKernelGGL((gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
+                       Hr, int64_t(0), rows_post, d_ff, static_cast<const T*>(w[l].w_down),
+                       nullptr, d, Xws, Xfinal);
+    LIME_CHECK_LAUNCH("gated mlp down");
+  }
+  return ok();
+}
+
+template <typename T>
+lime_status_t dispatch_xor_generic(int dh, const XorPlan& P, lime_phi_t phi, float scale, int B,
+                                   int ell, int d, int H, int layers, int d_ff,
+                                   const void* links_ctx, const void* hist, const int64_t* off,
+                                   int64_t total_N, const lime_layer_weights_t* w,
+                                   void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+  switch (dh) {
+    case 16: return run_xor_generic<T, 16>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+    case 32: return run_xor_generic<T, 32>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+    case 64: return run_xor_generic<T, 64>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+    case 128: return run_xor_generic<T, 128>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+  }
+  return fail(LIME_ERR_UNSUPPORTED, "d_h %d", dh);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lime_status_string(lime_status_t s) {
+  switch (s) {
+    case LIME_OK: return "LIME_OK";
+    case LIME_ERR_INVALID_ARG: return "LIME_ERR_INVALID_ARG";
+    case LIME_ERR_UNSUPPORTED: return "LIME_ERR_UNSUPPORTED";
+    case LIME_ERR_WORKSPACE: return "LIME_ERR_WORKSPACE";
+    case LIME_ERR_HIP: return "LIME_ERR_HIP";
+  }
+  return "LIME_ERR_UNKNOWN";
+}
+
+const char* lime_last_error(void) { return g_err.c_str(); }
+
+size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                   int32_t heads, int32_t d_ff, int64_t total_N, int32_t max_N) {
+  if (check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N) != LIME_OK) return 0;
+  return plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N).total;
+}
+
+lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                           int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
+                           const void* links_ctx, const void* hist, const int64_t* hist_offsets,
+                           int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                           void* links_pers, void* hist_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  lime_status_t st = check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  if (st != LIME_OK) return st;
+  if (phi != LIME_PHI_SOFTMAX && phi != LIME_PHI_SILU_MEAN) return fail(LIME_ERR_INVALID_ARG, "bad phi %d", (int)phi);
+  if (!std::isfinite(scale)) return fail(LIME_ERR_INVALID_ARG, "scale must be finite");
+  if (layers < 1) return fail(LIME_ERR_INVALID_ARG, "layers must be >= 1 (got %d)", layers);
+  if (!links_ctx || !hist_offsets || !w || !links_pers) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (total_N > 0 && !hist) return fail(LIME_ERR_INVALID_ARG, "hist is null but total_N > 0");
+  if (!aligned16(links_ctx) || !aligned16(hist) || !aligned16(hist_offsets) ||
+      !aligned16(links_pers) || !aligned16(hist_out))
+    return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  for (int l = 0; l < layers; ++l) {
+    const lime_layer_weights_t& lw = w[l];
+    if (!lw.w_qkv || !lw.w_o || !lw.w_gate || !lw.w_up || !lw.w_down)
+      return fail(LIME_ERR_INVALID_ARG, "null weight pointer in layer %d", l);
+    if (!aligned16(lw.w_qkv) || !aligned16(lw.w_o) || !aligned16(lw.w_gate) ||
+        !aligned16(lw.w_up) || !aligned16(lw.w_down))
+      return fail(LIME_ERR_INVALID_ARG, "weights of layer %d not 16-byte aligned", l);
+  }
+  const XorPlan P = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  if (!workspace) return fail(LIME_ERR_WORKSPACE, "workspace is null");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(LIME_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < P.total)
+    return fail(LIME_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, P.total);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int dh = d / heads;
+  if (dtype == LIME_F32)
+    return dispatch_xor_generic<float>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
+                                       hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
+  return dispatch_xor_generic<bf16_t>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
+                                      hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
+}
+
+lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                  int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                  const void* items, const void* link_keys, void* cache,
+                                  void* stream) {
+  if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+  if (phi != LIME_PHI_SOFTMAX && phi != LIME_PHI_SILU_MEAN) return fail(LIME_ERR_INVALID_ARG, "bad phi %d", (int)phi);
+  if (!std::isfinite(scale)) return fail(LIME_ERR_INVALID_ARG, "scale must be finite");
+  if (n_items < 0 || d < 1 || heads < 1 || ell < 1) return fail(LIME_ERR_INVALID_ARG, "sizes must be positive");
+  if (ell > 256) return fail(LIME_ERR_UNSUPPORTED, "ell > 256 unsupported (got %d)", ell);
+  if (d % 8 != 0 || d > 1024) return fail(LIME_ERR_UNSUPPORTED, "d must be a multiple of 8 and <= 1024 (got %d)", d);
+  if (heads > 65535) return fail(LIME_ERR_UNSUPPORTED, "too many heads");
+  if (!link_keys) return fail(LIME_ERR_INVALID_ARG, "link_keys is null");
+  if (n_items > 0 && (!items || !cache)) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(items) || !aligned16(link_keys) || !aligned16(cache))
+    return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (n_items == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>((n_items + 63) / 64), heads);
+  const size_t lds = 64 * static_cast<size_t>(ell) * 4;
+  if (dtype == LIME_F32)
+    hipLaunchKernelGGL(gen::qk_cache<float>, grid, dim3(64), lds, s, static_cast<const float*>(items),
+                       static_cast<const float*>(link_keys), static_cast<float*>(cache), n_items, d,
+                       heads, ell, scale, static_cast<int>(phi));
+  else
+    hipLaunchKernelGGL(gen::qk_cache<bf16_t>, grid, dim3(64), lds, s, static_cast<const bf16_t*>(items),
+                       static_cast<const bf16_t*>(link_keys), static_cast<bf16_t*>(cache), n_items,
+                       d, heads, ell, scale, static_cast<int>(phi));
+  LIME_CHECK_LAUNCH("qk cache build");
+  return ok();
+}
+
+lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                              int32_t heads, const void* cache, int64_t n_items,
+                              const void* links_pers, const int64_t* cand_ids,
+                              const int64_t* cand_offsets, int64_t total_M, void* out,
+                              int32_t* bad_id_count, void* stream) {
+  if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+  if (B < 1 || ell < 1 || d < 1 || heads < 1 || n_items < 0 || total_M < 0)
+    return fail(LIME_ERR_INVALID_ARG, "sizes must be positive");
+  if (d % heads != 0) return fail(LIME_ERR_INVALID_ARG, "d (%d) must be a multiple of heads (%d)", d, heads);
+  if (ell > 256) return fail(LIME_ERR_UNSUPPORTED, "ell > 256 unsupported (got %d)", ell);
+  if (!dh_supported(d / heads)) return fail(LIME_ERR_UNSUPPORTED, "d/heads must be 16, 32, 64 or 128 (got %d)", d / heads);
+  if (!links_pers || !cand_offsets) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (total_M > 0 && (!cand_ids || !out)) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (n_items > 0 && !cache) return fail(LIME_ERR_INVALID_ARG, "cache is null");
+  if (!aligned16(cache) || !aligned16(links_pers) || !aligned16(cand_ids) ||
+      !aligned16(cand_offsets) || !aligned16(out))
+    return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(bad_id_count) & 3u) != 0)
+    return fail(LIME_ERR_INVALID_ARG, "bad_id_count must be 4-byte aligned");
+  if (total_M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = total_M * d;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (dtype == LIME_F32)
+    hipLaunchKernelGGL(gen::cand_score<float>, grid, dim3(256), 0, s, static_cast<const float*>(cache),
+                       n_items, static_cast<const float*>(links_pers), cand_ids, cand_offsets, B, ell,
+                       d, heads, total_M, static_cast<float*>(out), bad_id_count);
+  else
+    hipLaunchKernelGGL(gen::cand_score<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(cache),
+                       n_items, static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B,
+                       ell, d, heads, total_M, static_cast<bf16_t*>(out), bad_id_count);
+  LIME_CHECK_LAUNCH("candidate scoring");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+/*
+ * lime.h — C ABI of the LIME inference hot path on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Three operations, following the LIME pages:
+ *
+ *   lime_xor_fwd        user side: stacked LIME-XOR layers over the context
+ *                       links L^C and the user history E, giving the
+ *                       personalised links L^P (LIME notes on papernotes.org,
+ *                       "Key design 2", XORA equation; framework flowchart,
+ *                       online user-side stage).
+ *   lime_qk_cache_build offline: the QK cache phi(scale * K_L[h] . T_m) over
+ *                       an item catalogue (LIME notes, "Key design 1" and the
+ *                       offline stage of the framework; LIME summary page,
+ *                       Table 12: per item, per head, ell weights).
+ *   lime_cand_score     online: O_i = phi(T_i L^T) L^P_b, a gather of cached
+ *                       weight rows by candidate id plus an ell-wide weighted
+ *                       sum per head (LIME notes, "complete example", step 3).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor argument is a DEVICE pointer to memory OWNED BY THE CALLER,
+ *   contiguous, row-major, 16-byte aligned.  Host pointers are named as such.
+ *   The library allocates no device memory; lime_xor_fwd takes a caller
+ *   workspace sized by lime_xor_fwd_workspace_size.  The library keeps no
+ *   state between calls except a per-thread error message.
+ * - Element type: LIME_F32 (float) or LIME_BF16 (bfloat16 bit patterns).
+ *   Arithmetic accumulates in float32; bf16 results are stored rounded to
+ *   nearest-even.  Candidate ids and offsets are int64.
+ * - Each call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *   default stream) and returns without waiting.  Outputs are valid once the
+ *   stream has reached that point.  Calls that share output or workspace
+ *   memory must be ordered by the caller.
+ * - Errors: problems visible on the host (null pointers, bad sizes, bad
+ *   enums, misalignment, too small a workspace, unsupported shapes) return
+ *   synchronously, BEFORE anything is enqueued, leaving outputs untouched.
+ *   A failed launch returns LIME_ERR_HIP.  lime_last_error() gives details.
+ *   Data errors only the device can see have defined results (see each call).
+ *
+ * Attention nonlinearity phi (LIME notes, "Key design 1"; training strategy:
+ * scaled softmax for single-layer attention, SiLU for deep stacks):
+ *   LIME_PHI_SOFTMAX   softmax over the keys a row may attend;
+ *   LIME_PHI_SILU_MEAN SiLU(s) / (number of keys the row may attend):
+ *                      ell for history rows and the cache, N_b for link rows.
+ * `scale` multiplies every logit (usually 1/sqrt(d_h)).
+ * A row with no keys to attend (a user with empty history) outputs 0.
+ */
+#ifndef LIME_H_
+#define LIME_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIME_OK = 0,
+  LIME_ERR_INVALID_ARG = 1,  /* null pointer, negative/inconsistent size, bad enum, misalignment */
+  LIME_ERR_UNSUPPORTED = 2,  /* valid but outside the supported shape limits */
+  LIME_ERR_WORKSPACE = 3,    /* workspace null or smaller than required */
+  LIME_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} lime_status_t;
+
+typedef enum { LIME_F32 = 0, LIME_BF16 = 1 } lime_dtype_t;
+
+typedef enum { LIME_PHI_SOFTMAX = 0, LIME_PHI_SILU_MEAN = 1 } lime_phi_t;
+
+/* Weights of one LIME-XOR layer, device pointers, all in [out, in] row-major
+ * layout (y = x . W^T), element type = the call's dtype:
+ *   w_qkv  [3d, d]   rows 0..d-1 give Q, d..2d-1 give K, 2d..3d-1 give V
+ *                    (one projection shared by both XOR branches, as in the
+ *                    XORA equation's single parameter set)
+ *   w_o    [d, d]    output projection, added to the residual stream
+ *   w_gate [d_ff, d], w_up [d_ff, d], w_down [d, d_ff]
+ *                    gated MLP: x += (SiLU(G w_gate^T) * (G w_up^T)) w_down^T
+ *                    with G = LayerNorm(x)  (LIME notes, "Key design 2":
+ *                    residual + GatedMLP)                                     */
+typedef struct {
+  const void* w_qkv;
+  const void* w_o;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} lime_layer_weights_t;
+
+/* Bytes of workspace lime_xor_fwd needs for these sizes (0 on invalid
+ * sizes).  The same arguments must be passed to lime_xor_fwd.               */
+size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                   int32_t heads, int32_t d_ff, int64_t total_N, int32_t max_N);
+
+/* User-side encoder: `layers` LIME-XOR layers over X_b = [L^C_b ; E_b].
+ *
+ * Per layer (LIME notes, "Key design 2" and training strategy; the layer
+ * internals beyond the XORA equation are this library's reading):
+ *   H = LayerNorm(X) (no affine, eps 1e-5);  [Q|K|V] = H w_qkv^T
+ *   history rows attend to their user's ell link rows only, link rows attend
+ *   to their user's N_b history rows only (no history<->history and no
+ *   link<->link terms), per head on column slices of width d/heads;
+ *   X += Y w_o^T;  X += SwiGLU-MLP(LayerNorm(X)).
+ *
+ *   links_ctx    [B, ell, d]          context links L^C (device)
+ *   hist         [total_N, d]         packed histories E (device)
+ *   hist_offsets [B+1] int64 (device) exclusive prefix sum of history
+ *                                     lengths: user b owns rows
+ *                                     [off[b], off[b+1]); off[0] = 0 and
+ *                                     off[B] = total_N are required (other
+ *                                     values give unspecified outputs but no
+ *                                     access outside the buffers).
+ *   total_N      host, rows of hist;  max_N host, the largest N_b (a
+ *                                     planning hint: a larger N_b is still
+ *                                     computed correctly, only slower).
+ *   w            HOST array of `layers` weight structs (device pointers).
+ *   links_pers   [B, ell, d] out: L^P, the link rows after the last layer.
+ *   hist_out     [total_N, d] out or NULL: the history rows after the last
+ *                layer.  With NULL the last layer's history-row work that
+ *                cannot reach L^P is skipped.
+ *   workspace    device, >= lime_xor_fwd_workspace_size(...) bytes, 256-byte
+ *                aligned; contents on entry are ignored.
+ * Limits: d % heads == 0, d_h = d/heads in {16, 32, 64, 128}, d % 8 == 0,
+ * d <= 1024, d_ff % 8 == 0, 1 <= ell <= 256, B >= 1, layers >= 1.           */
+lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                           int32_t B, int32_t ell, int32_t d, int32_t heads, int32_t layers,
+                           int32_t d_ff, const void* links_ctx, const void* hist,
+                           const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
+                           const lime_layer_weights_t* w, void* links_pers, void* hist_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Offline QK cache over items [n_items, d] and per-head link keys
+ * link_keys [heads, ell, d] (the global links with the candidate-side
+ * query/key projections folded in; heads = 1 and link_keys = L is the
+ * pages' literal formula):
+ *   cache[m, h, k] = phi_k( scale * sum_c items[m, c] * link_keys[h, k, c] )
+ * phi taken over the ell links of head h.  cache is [n_items, heads, ell],
+ * same dtype.  Items are independent, so a partial refresh of rows
+ * [r0, r1) is a call with items + r0*d, cache + r0*heads*ell and
+ * n_items = r1 - r0.  n_items = 0 is a no-op.
+ * Limits: 1 <= ell <= 256, d % 8 == 0, d <= 1024, heads >= 1.               */
+lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                  int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                  const void* items, const void* link_keys, void* cache,
+                                  void* stream);
+
+/* Candidate scoring: for candidate i of user b (cand_offsets[b] <= i <
+ * cand_offsets[b+1]) and head h,
+ *   out[i, h*d_h + c] = sum_k cache[cand_ids[i], h, k] * links_pers[b, k, h*d_h + c]
+ *   cache       [n_items, heads, ell]   (from lime_qk_cache_build)
+ *   links_pers  [B, ell, d]             (from lime_xor_fwd)
+ *   cand_ids    [total_M] int64, cand_offsets [B+1] int64 (device), the
+ *               exclusive prefix sum of per-user candidate counts with
+ *               cand_offsets[0] = 0, cand_offsets[B] = total_M.
+ *   out         [total_M, d]
+ *   bad_id_count device int32 or NULL: an id outside [0, n_items) gives a
+ *               zero output row and adds 1 here (the caller zeroes it).
+ * Each output row depends only on its own id and user.
+ * Limits: d % heads == 0, d_h in {16, 32, 64, 128}, 1 <= ell <= 256.        */
+lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                              int32_t heads, const void* cache, int64_t n_items,
+                              const void* links_pers, const int64_t* cand_ids,
+                              const int64_t* cand_offsets, int64_t total_M, void* out,
+                              int32_t* bad_id_count, void* stream);
+
+/* Static string naming a status code. */
+const char* lime_status_string(lime_status_t status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* lime_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIME_H_ */

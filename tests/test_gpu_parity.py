@@ -1,0 +1,247 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the
+same seeded inputs.  Small workloads are compared in full; the large ones on
+samples the oracle can compute one by one (users, items, candidates are
+independent of each other, so a sample is exact).  Bar: max|err| <= tol *
+max|ref| with tol 1e-4 (float32) and 2e-2 (bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.lime_oracle as O
+import workloads as W
+from parity_utils import (assert_close, cache_inputs, dev, dev_weights, host_f64, ids_for,
+                          synthetic_cache, user_inputs)
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny", "ctr", "long", "large_m", "lifelong"]
+SAMPLE = 65536
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import decoupled_linear_link_amd as lib
+    return lib
+
+
+def _sample(n, k=SAMPLE, seed=0):
+    if n <= k:
+        return np.arange(n)
+    return np.sort(np.random.default_rng(seed).choice(n, k, replace=False))
+
+
+def _oracle_scores(cache_st, lp_st, ids, coff, sel, n_items):
+    """Oracle scores of the sampled candidates `sel` (sorted) only."""
+    B = len(coff) - 1
+    users = np.searchsorted(coff, sel, side="right") - 1
+    sub_off = W.offsets_from_lengths(np.bincount(users, minlength=B))
+    sid = ids[sel]
+    ok = (sid >= 0) & (sid < n_items)
+    uniq, inv = np.unique(sid[ok], return_inverse=True)
+    remap = np.full(len(sid), -1, dtype=np.int64)
+    remap[ok] = inv
+    return O.cand_score(cache_st[uniq], lp_st, remap, sub_off, n_items=len(uniq))
+
+
+# ------------------------------------------------------------ candidate scoring
+
+@pytest.mark.parametrize("name", ALL)
+def test_cand_score(L, name):
+    w = W.workload(name)
+    cache = synthetic_cache(name)
+    lp = W.links_pers(w, stress=True)
+    ids, coff = ids_for(name), W.candidate_offsets(w)
+    print(f"cand_score {name}: total_M={len(ids)} n_items={w.n_items}", flush=True)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = L.cand_score(dev(cache), dev(lp), dev(ids), dev(coff), bad_id_count=bad)
+    torch.cuda.synchronize()
+    sel = _sample(len(ids))
+    ref, nbad = _oracle_scores(cache, lp, ids, coff, sel, w.n_items)
+    assert nbad == 0 and int(bad.item()) == 0
+    assert_close(host_f64(out[torch.from_numpy(sel).cuda()]), ref, w.dtype, f"cand_score[{name}]")
+
+
+def test_cand_score_bad_ids_and_ragged_users(L):
+    w = W.workload("ctr")
+    cache = synthetic_cache("ctr")
+    lp = W.links_pers(w, stress=True)
+    rng = np.random.default_rng(5)
+    counts = rng.integers(0, 70, size=w.B)
+    counts[[0, 7]] = 0
+    coff = W.offsets_from_lengths(counts)
+    ids = rng.integers(0, w.n_items, size=int(coff[-1]))
+    ids[::97] = -5
+    ids[13::101] = w.n_items
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = L.cand_score(dev(cache), dev(lp), dev(ids), dev(coff), bad_id_count=bad)
+    torch.cuda.synchronize()
+    ref, nbad = _oracle_scores(cache, lp, ids, coff, np.arange(len(ids)), w.n_items)
+    assert int(bad.item()) == nbad > 0
+    got = host_f64(out)
+    assert np.all(got[(ids < 0) | (ids >= w.n_items)] == 0)
+    assert_close(got, ref, "bf16", "cand_score ragged/bad ids")
+
+
+def test_cand_score_f32_small_odd_shapes(L):
+    rng = np.random.default_rng(6)
+    for B, ell, d, H, n in ((3, 5, 32, 2, 40), (2, 1, 64, 4, 7), (4, 33, 48, 3, 100)):
+        cache = rng.random((n, H, ell)).astype(np.float32)
+        lp = rng.standard_normal((B, ell, d)).astype(np.float32)
+        coff = W.offsets_from_lengths(rng.integers(0, 9, size=B))
+        ids = rng.integers(0, n, size=int(coff[-1]))
+        out = L.cand_score(dev(cache), dev(lp), dev(ids), dev(coff))
+        torch.cuda.synchronize()
+        ref, _ = O.cand_score(cache, lp, ids, coff)
+        if len(ids):
+            assert_close(host_f64(out), ref, "f32", f"cand_score f32 {B,ell,d,H}")
+
+
+# ------------------------------------------------------------ QK cache
+
+@pytest.mark.parametrize("stress", [False, True])
+@pytest.mark.parametrize("name", ALL)
+def test_qk_cache_build(L, name, stress):
+    w = W.workload(name)
+    ci = cache_inputs(name, stress)
+    scale = W.scale_for(w)
+    print(f"qk_cache_build {name} stress={stress}: n_items={w.n_items}", flush=True)
+    cache = L.qk_cache_build(dev(ci["items"]), dev(ci["link_keys"]), phi=w.phi, scale=scale)
+    torch.cuda.synchronize()
+    sel = _sample(w.n_items)
+    ref = O.qk_cache_build(ci["items"][sel], ci["link_keys"], scale, w.phi)
+    got = host_f64(cache[torch.from_numpy(sel).cuda()])
+    assert_close(got, ref, w.dtype, f"qk_cache[{name}]")
+
+
+@pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
+def test_qk_cache_build_odd_shapes(L, phi):
+    rng = np.random.default_rng(7)
+    for dt in ("f32", "bf16"):
+        for n, d, H, ell in ((1, 8, 1, 1), (77, 40, 3, 5), (300, 64, 2, 33), (129, 256, 8, 64)):
+            items = W.as_storage(rng.standard_normal((n, d)).astype(np.float32), dt)
+            keys = W.as_storage(rng.standard_normal((H, ell, d)).astype(np.float32), dt)
+            cache = L.qk_cache_build(dev(items), dev(keys), phi=phi, scale=0.3)
+            torch.cuda.synchronize()
+            ref = O.qk_cache_build(items, keys, 0.3, phi)
+            assert_close(host_f64(cache), ref, dt, f"qk_cache {dt} {n,d,H,ell}")
+
+
+# ------------------------------------------------------------ user side
+
+def _users_for(w, off):
+    if w.B <= 256 and int(off[-1]) <= 20000:
+        return list(range(w.B))
+    lens = np.diff(off)
+    longest = int(np.argmax(lens))
+    other = int(np.random.default_rng(1).integers(0, w.B))
+    return sorted({longest, other})
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_xor_fwd(L, name):
+    w = W.workload(name)
+    ui = user_inputs(name)
+    off = ui["hist_offsets"]
+    print(f"xor_fwd {name}: B={w.B} total_N={int(off[-1])} layers={w.layers}", flush=True)
+    lp, _ = L.xor_fwd(dev(ui["links_ctx"]), dev(ui["hist"]), dev(off), dev_weights(ui["weights"]),
+                      heads=w.heads, phi=w.phi, scale=W.scale_for(w), max_N=int(np.diff(off).max()))
+    torch.cuda.synchronize()
+    users = _users_for(w, off)
+    ref, _ = O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, W.scale_for(w),
+                       w.phi, users=users)
+    assert_close(host_f64(lp)[users], ref, w.dtype, f"L^P[{name}]")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ctr"])
+@pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
+def test_xor_fwd_both_phis_with_history_out(L, name, phi):
+    w = W.workload(name)
+    ui = user_inputs(name, stress=True)
+    off = ui["hist_offsets"]
+    lp, ho = L.xor_fwd(dev(ui["links_ctx"]), dev(ui["hist"]), dev(off), dev_weights(ui["weights"]),
+                       heads=w.heads, phi=phi, scale=W.scale_for(w), want_hist=True)
+    torch.cuda.synchronize()
+    ref, href = O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, W.scale_for(w), phi)
+    assert_close(host_f64(lp), ref, w.dtype, f"L^P[{name},{phi}]")
+    assert_close(host_f64(ho), np.concatenate(href), w.dtype, f"hist_out[{name},{phi}]")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
+def test_xor_fwd_ragged_empty_and_odd_shapes(L, dt, phi):
+    """Ragged lengths including empty and single-row histories, ell not a
+    multiple of 8, several splits per user, d_ff != d."""
+    rng = np.random.default_rng(8)
+    for B, ell, d, H, layers, dff, lens in (
+            (5, 3, 32, 1, 2, 64, [0, 1, 700, 2, 1500]),
+            (3, 32, 64, 2, 1, 32, [1100, 0, 5]),
+            (2, 64, 256, 8, 1, 256, [130, 2049])):
+        off = W.offsets_from_lengths(lens)
+        lc = W.as_storage(rng.standard_normal((B, ell, d)).astype(np.float32), dt)
+        hs = W.as_storage((rng.standard_normal((int(off[-1]), d)) * 0.5).astype(np.float32), dt)
+        ws = []
+        for _ in range(layers):
+            ws.append({k: W.as_storage((rng.standard_normal(s) * s[1] ** -0.5).astype(np.float32), dt)
+                       for k, s in (("w_qkv", (3 * d, d)), ("w_o", (d, d)), ("w_gate", (dff, d)),
+                                    ("w_up", (dff, d)), ("w_down", (d, dff)))})
+        scale = (d // H) ** -0.5
+        lp, ho = L.xor_fwd(dev(lc), dev(hs), dev(off), dev_weights(ws), heads=H, phi=phi, scale=scale,
+                           max_N=int(max(lens)), want_hist=True)
+        torch.cuda.synchronize()
+        ref, href = O.xor_fwd(lc, hs, off, ws, H, scale, phi)
+        assert_close(host_f64(lp), ref, dt, f"L^P odd {B,ell,d,H} {dt} {phi}")
+        assert_close(host_f64(ho), np.concatenate(href), dt, f"hist_out odd {B,ell,d,H} {dt} {phi}")
+
+
+def test_xor_fwd_max_n_hint_too_small_is_still_correct(L):
+    w = W.workload("ctr")
+    ui = user_inputs("ctr")
+    off = ui["hist_offsets"]
+    lp, _ = L.xor_fwd(dev(ui["links_ctx"]), dev(ui["hist"]), dev(off), dev_weights(ui["weights"]),
+                      heads=w.heads, phi=w.phi, max_N=1)
+    torch.cuda.synchronize()
+    ref, _ = O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, W.scale_for(w), w.phi,
+                       users=[0, 100, 255])
+    assert_close(host_f64(lp)[[0, 100, 255]], ref, "bf16", "L^P small max_N hint")
+
+
+# ------------------------------------------------------------ whole path
+
+@pytest.mark.parametrize("name", ["tiny", "ctr"])
+def test_end_to_end(L, name):
+    """user encoder -> QK cache -> candidate scores, all on the GPU, against
+    the oracle's own pipeline on the same inputs."""
+    w = W.workload(name)
+    ui, ci = user_inputs(name), cache_inputs(name)
+    ids, coff = ids_for(name), W.candidate_offsets(w)
+    sc = W.scale_for(w)
+    lp, _ = L.xor_fwd(dev(ui["links_ctx"]), dev(ui["hist"]), dev(ui["hist_offsets"]),
+                      dev_weights(ui["weights"]), heads=w.heads, phi=w.phi, scale=sc)
+    cache = L.qk_cache_build(dev(ci["items"]), dev(ci["link_keys"]), phi=w.phi, scale=sc)
+    out = L.cand_score(cache, lp, dev(ids), dev(coff))
+    torch.cuda.synchronize()
+    lp_ref, _ = O.xor_fwd(ui["links_ctx"], ui["hist"], ui["hist_offsets"], ui["weights"], w.heads, sc, w.phi)
+    uniq, inv = np.unique(ids, return_inverse=True)
+    c_ref = O.qk_cache_build(ci["items"][uniq], ci["link_keys"], sc, w.phi)
+    ref, _ = O.cand_score(c_ref, lp_ref, inv, coff)
+    assert_close(host_f64(out), ref, w.dtype, f"end-to-end[{name}]")
+
+
+def test_repeat_runs_are_bitwise_identical(L):
+    w = W.workload("ctr")
+    ui, ci = user_inputs("ctr"), cache_inputs("ctr")
+    args = (dev(ui["links_ctx"]), dev(ui["hist"]), dev(ui["hist_offsets"]), dev_weights(ui["weights"]))
+    a, _ = L.xor_fwd(*args, heads=w.heads, phi=w.phi)
+    b, _ = L.xor_fwd(*args, heads=w.heads, phi=w.phi)
+    items, keys = dev(ci["items"]), dev(ci["link_keys"])
+    c1 = L.qk_cache_build(items, keys, phi=w.phi)
+    c2 = L.qk_cache_build(items, keys, phi=w.phi)
+    ids, coff = dev(ids_for("ctr")), dev(W.candidate_offsets(w))
+    o1 = L.cand_score(c1, a, ids, coff)
+    o2 = L.cand_score(c1, a, ids, coff)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
