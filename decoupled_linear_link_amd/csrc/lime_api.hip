@@ -46,14 +46,97 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool dh_supported(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <typename K>
+int blocks_per_cu(K kernel, int threads) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
+// ---------------------------------------------------------------------------
+// QK cache: matrix-core kernel for the shapes it is instantiated for
+// ---------------------------------------------------------------------------
+template <int ELL, int D, int H>
+lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, int64_t n_items,
+                             float scale, int phi, hipStream_t st) {
+  using C = mfma::QkCfg<ELL, D, H>;
+  auto k = mfma::qk_cache<ELL, D, H>;
+  static const int per_cu = blocks_per_cu(k, C::NT);
+  const int64_t ntiles = (n_items + C::TI - 1) / C::TI;
+  int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+  if (grid > ntiles) grid = ntiles;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, st,
+                     static_cast<const bf16_t*>(items), static_cast<const bf16_t*>(keys),
+                     static_cast<bf16_t*>(cache), n_items, scale, phi, ntiles);
+  LIME_CHECK_LAUNCH("qk cache build (mfma)");
+  return ok();
+}
+
+// returns LIME_ERR_UNSUPPORTED (without launching) if no instantiation fits
+lime_status_t try_qk_mfma(int ell, int d, int H, const void* items, const void* keys, void* cache,
+                          int64_t n_items, float scale, int phi, hipStream_t st) {
+#define LIME_QK(E, DD, HH) \
+  if (ell == E && d == DD && H == HH) return launch_qk_mfma<E, DD, HH>(items, keys, cache, n_items, scale, phi, st);
+  LIME_QK(32, 64, 2)
+  LIME_QK(32, 128, 4)
+  LIME_QK(64, 128, 4)
+  LIME_QK(32, 256, 8)
+  LIME_QK(64, 256, 8)
+#undef LIME_QK
+  return LIME_ERR_UNSUPPORTED;
+}
+
+// ---------------------------------------------------------------------------
+// candidate scoring: matrix-core kernel for d_h = 32, ell in {32, 64}
+// ---------------------------------------------------------------------------
+template <int ELL, int H>
+lime_status_t launch_cs_mfma(const void* cache, int64_t n_items, const void* lp,
+                             const int64_t* ids, const int64_t* off, int B, int64_t total_M,
+                             void* out, int* bad, hipStream_t st) {
+  const int64_t ntiles = (total_M + 15) / 16;
+  const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16;
+  int64_t tpw = (ntiles + target_waves - 1) / target_waves;
+  if (tpw < 1) tpw = 1;
+  const int64_t waves = (ntiles + tpw - 1) / tpw;
+  const int64_t grid = (waves + 3) / 4;
+  hipLaunchKernelGGL((mfma::cand_score<ELL, H>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     static_cast<const bf16_t*>(cache), n_items, static_cast<const bf16_t*>(lp), ids,
+                     off, B, total_M, static_cast<bf16_t*>(out), bad, tpw);
+  LIME_CHECK_LAUNCH("candidate scoring (mfma)");
+  return ok();
+}
+
+lime_status_t try_cs_mfma(int ell, int d, int H, const void* cache, int64_t n_items, const void* lp,
+                          const int64_t* ids, const int64_t* off, int B, int64_t total_M, void* out,
+                          int* bad, hipStream_t st) {
+  if (d != 32 * H) return LIME_ERR_UNSUPPORTED;
+#define LIME_CS(E, HH) \
+  if (ell == E && H == HH) return launch_cs_mfma<E, HH>(cache, n_items, lp, ids, off, B, total_M, out, bad, st);
+  LIME_CS(32, 1) LIME_CS(32, 2) LIME_CS(32, 4) LIME_CS(32, 8)
+  LIME_CS(64, 1) LIME_CS(64, 2) LIME_CS(64, 4) LIME_CS(64, 8)
+#undef LIME_CS
+  return LIME_ERR_UNSUPPORTED;
+}
+
 // ---------------------------------------------------------------------------
 // lime_xor_fwd planning
 // ---------------------------------------------------------------------------
 struct XorPlan {
+  bool mfma = false;       // matrix-core path
   int64_t nlr = 0, R = 0;  // link rows, all rows
+  int64_t R_pad = 0;       // rows of the QK / packed-V buffers (matrix-core path)
   int S = 1;               // history splits per user
   int64_t chunk = 1;       // history rows per split
-  size_t o_x = 0, o_qkv = 0, o_y = 0, o_h = 0, o_part = 0, total = 0;
+  size_t o_x = 0, o_qkv = 0, o_v = 0, o_y = 0, o_h = 0, o_part = 0, total = 0;
 };
 
 lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
@@ -72,29 +155,111 @@ lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
   return LIME_OK;
 }
 
+// shapes served by the matrix-core user-side kernels
+bool xor_mfma_ok(lime_dtype_t dtype, int ell, int d, int heads, int d_ff) {
+  return dtype == LIME_BF16 && d == 32 * heads && (ell == 32 || ell == 64) &&
+         (d == 64 || d == 128 || d == 256) && d_ff == d;
+}
+
 XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
                  int32_t d_ff, int64_t total_N, int32_t max_N) {
   XorPlan p;
   const size_t es = dtype == LIME_F32 ? 4 : 2;
+  p.mfma = xor_mfma_ok(dtype, ell, d, heads, d_ff);
   p.nlr = static_cast<int64_t>(B) * ell;
   p.R = p.nlr + total_N;
-  // enough splits that B*heads*S work items cover the chip, each split
-  // holding at least a few hundred history rows
-  int64_t S = (static_cast<int64_t>(max_N) + 511) / 512;
+  const int dh = d / heads;
+  int64_t S;
+  if (p.mfma) {
+    // about 2048 (user, head, split) waves, splits of at least 64 rows
+    S = (2048 + static_cast<int64_t>(B) * heads - 1) / (static_cast<int64_t>(B) * heads);
+    const int64_t smax = (static_cast<int64_t>(max_N) + 63) / 64;
+    if (S > smax) S = smax;
+  } else {
+    S = (static_cast<int64_t>(max_N) + 511) / 512;
+  }
   if (S < 1) S = 1;
   if (S > 64) S = 64;
   p.S = static_cast<int>(S);
   p.chunk = (static_cast<int64_t>(max_N) + S - 1) / S;
+  if (p.mfma) p.chunk = (p.chunk + 31) / 32 * 32;
   if (p.chunk < 1) p.chunk = 1;
-  const int dh = d / heads;
   size_t off = 0;
-  p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
-  p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R) * 3 * d * es);
-  p.o_y = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
-  p.o_h = off;    off = up256(off + static_cast<size_t>(p.R) * d_ff * es);
-  p.o_part = off; off = up256(off + static_cast<size_t>(B) * heads * p.S * ell * (dh + 2) * 4);
+  if (p.mfma) {
+    p.R_pad = (p.R + 32 + 31) / 32 * 32;
+    p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+    p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R_pad) * 2 * d * es);
+    p.o_v = off;    off = up256(off + static_cast<size_t>(p.R_pad) * d * es);
+    p.o_y = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+    p.o_part = off; off = up256(off + static_cast<size_t>(B) * heads * p.S * ell * (dh + 2) * 4);
+  } else {
+    p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+    p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R) * 3 * d * es);
+    p.o_y = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
+    p.o_h = off;    off = up256(off + static_cast<size_t>(p.R) * d_ff * es);
+    p.o_part = off; off = up256(off + static_cast<size_t>(B) * heads * p.S * ell * (dh + 2) * 4);
+  }
   p.total = off;
   return p;
+}
+
+// matrix-core user side: per layer QKV projection, XOR attention, split
+// combine, fused post-attention block
+template <int ELL, int D>
+lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B, int layers,
+                           const void* links_ctx, const void* hist, const int64_t* off,
+                           int64_t total_N, const lime_layer_weights_t* w, void* links_pers,
+                           void* hist_out, char* ws, hipStream_t st) {
+  constexpr int H = D / 32;
+  constexpr int RPW = D >= 256 ? 16 : 32;
+  bf16_t* X = reinterpret_cast<bf16_t*>(ws + P.o_x);
+  bf16_t* QK = reinterpret_cast<bf16_t*>(ws + P.o_qkv);
+  bf16_t* Vp = reinterpret_cast<bf16_t*>(ws + P.o_v);
+  bf16_t* Y = reinterpret_cast<bf16_t*>(ws + P.o_y);
+  float* part = reinterpret_cast<float*>(ws + P.o_part);
+  const int64_t nlr = P.nlr, R = P.R;
+  const Rows Xws{X, X + nlr * D, nlr, D};
+  const Rows Yr{Y, Y + nlr * D, nlr, D};
+  for (int l = 0; l < layers; ++l) {
+    const bool last = (l == layers - 1);
+    const bool full = !last || hist_out != nullptr;
+    const int64_t rows_post = full ? R : nlr;
+    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, D} : Xws;
+    const Rows Xout = last ? Rows{links_pers, hist_out, nlr, D} : Xws;
+    hipLaunchKernelGGL((mfma::qkv_proj<D>), dim3(static_cast<unsigned>(P.R_pad / 128 + (P.R_pad % 128 ? 1 : 0))),
+                       dim3(256), 0, st, Xin, R, P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+    LIME_CHECK_LAUNCH("qkv projection (mfma)");
+    const int64_t waves = static_cast<int64_t>(B) * H * P.S;
+    hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
+                       QK, Vp, Y, part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi),
+                       full ? 1 : 0);
+    LIME_CHECK_LAUNCH("xor attention (mfma)");
+    {
+      const int64_t n = static_cast<int64_t>(B) * H * ELL * 32;
+      hipLaunchKernelGGL((gen::xor_combine<bf16_t, 32>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                         0, st, part, Y, B, ELL, D, H, P.S);
+      LIME_CHECK_LAUNCH("xor combine");
+    }
+    const int64_t pw = (rows_post + RPW - 1) / RPW;
+    hipLaunchKernelGGL((mfma::post_block<D, D, RPW>), dim3(static_cast<unsigned>((pw + 3) / 4)), dim3(256), 0, st,
+                       Yr, Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
+                       static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
+                       static_cast<const bf16_t*>(w[l].w_down));
+    LIME_CHECK_LAUNCH("post-attention block (mfma)");
+  }
+  return ok();
+}
+
+lime_status_t dispatch_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B, int ell, int d,
+                                int layers, const void* links_ctx, const void* hist,
+                                const int64_t* off, int64_t total_N, const lime_layer_weights_t* w,
+                                void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+#define LIME_XM(E, DD) \
+  if (ell == E && d == DD) return run_xor_mfma<E, DD>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+  LIME_XM(32, 64) LIME_XM(32, 128) LIME_XM(32, 256)
+  LIME_XM(64, 64) LIME_XM(64, 128) LIME_XM(64, 256)
+#undef LIME_XM
+  return fail(LIME_ERR_UNSUPPORTED, "no matrix-core user-side kernel for ell=%d d=%d", ell, d);
 }
 
 template <typename T, int DH>
@@ -227,6 +392,9 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const int dh = d / heads;
+  if (P.mfma)
+    return dispatch_xor_mfma(P, phi, scale, B, ell, d, layers, links_ctx, hist, hist_offsets, total_N,
+                             w, links_pers, hist_out, ws, s);
   if (dtype == LIME_F32)
     return dispatch_xor_generic<float>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
                                        hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
@@ -251,6 +419,11 @@ lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scal
     return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (n_items == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LIME_BF16) {
+    const lime_status_t r = try_qk_mfma(ell, d, heads, items, link_keys, cache, n_items, scale,
+                                        static_cast<int>(phi), s);
+    if (r != LIME_ERR_UNSUPPORTED) return r;
+  }
   const dim3 grid(static_cast<unsigned>((n_items + 63) / 64), heads);
   const size_t lds = 64 * static_cast<size_t>(ell) * 4;
   if (dtype == LIME_F32)
@@ -286,6 +459,11 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
     return fail(LIME_ERR_INVALID_ARG, "bad_id_count must be 4-byte aligned");
   if (total_M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LIME_BF16) {
+    const lime_status_t r = try_cs_mfma(ell, d, heads, cache, n_items, links_pers, cand_ids,
+                                        cand_offsets, B, total_M, out, bad_id_count, s);
+    if (r != LIME_ERR_UNSUPPORTED) return r;
+  }
   const int64_t n = total_M * d;
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
   if (dtype == LIME_F32)

@@ -84,6 +84,27 @@ def test_cand_score_bad_ids_and_ragged_users(L):
     assert_close(got, ref, "bf16", "cand_score ragged/bad ids")
 
 
+@pytest.mark.parametrize("ell,H", [(32, 1), (32, 4), (64, 2), (64, 8)])
+def test_cand_score_bf16_ragged_users(L, ell, H):
+    """Users whose candidate ranges start and end inside 16-candidate tiles,
+    single-candidate and empty users, a partial last tile."""
+    rng = np.random.default_rng(9 + ell + H)
+    B, d, n = 37, 32 * H, 500
+    counts = rng.integers(0, 40, size=B)
+    counts[[3, 4, 5]] = [1, 0, 1]
+    coff = W.offsets_from_lengths(counts)
+    cache = W.as_storage(rng.random((n, H, ell)).astype(np.float32) / ell, "bf16")
+    lp = W.as_storage(rng.standard_normal((B, ell, d)).astype(np.float32), "bf16")
+    ids = rng.integers(0, n, size=int(coff[-1]))
+    ids[::53] = n + 7
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = L.cand_score(dev(cache), dev(lp), dev(ids), dev(coff), bad_id_count=bad)
+    torch.cuda.synchronize()
+    ref, nbad = O.cand_score(cache, lp, ids, coff)
+    assert int(bad.item()) == nbad
+    assert_close(host_f64(out), ref, "bf16", f"cand_score bf16 ragged ell={ell} H={H}")
+
+
 def test_cand_score_f32_small_odd_shapes(L):
     rng = np.random.default_rng(6)
     for B, ell, d, H, n in ((3, 5, 32, 2, 40), (2, 1, 64, 4, 7), (4, 33, 48, 3, 100)):
@@ -119,7 +140,8 @@ def test_qk_cache_build(L, name, stress):
 def test_qk_cache_build_odd_shapes(L, phi):
     rng = np.random.default_rng(7)
     for dt in ("f32", "bf16"):
-        for n, d, H, ell in ((1, 8, 1, 1), (77, 40, 3, 5), (300, 64, 2, 33), (129, 256, 8, 64)):
+        for n, d, H, ell in ((1, 8, 1, 1), (77, 40, 3, 5), (300, 64, 2, 33), (129, 256, 8, 64),
+                                (77, 128, 4, 32), (1000, 64, 2, 32), (65, 256, 8, 32), (200, 128, 4, 64)):
             items = W.as_storage(rng.standard_normal((n, d)).astype(np.float32), dt)
             keys = W.as_storage(rng.standard_normal((H, ell, d)).astype(np.float32), dt)
             cache = L.qk_cache_build(dev(items), dev(keys), phi=phi, scale=0.3)
@@ -177,7 +199,9 @@ def test_xor_fwd_ragged_empty_and_odd_shapes(L, dt, phi):
     for B, ell, d, H, layers, dff, lens in (
             (5, 3, 32, 1, 2, 64, [0, 1, 700, 2, 1500]),
             (3, 32, 64, 2, 1, 32, [1100, 0, 5]),
-            (2, 64, 256, 8, 1, 256, [130, 2049])):
+            (2, 64, 256, 8, 1, 256, [130, 2049]),
+            (6, 32, 64, 2, 2, 64, [0, 1, 77, 2, 1500, 33]),
+            (4, 64, 128, 4, 2, 128, [17, 0, 640, 5])):
         off = W.offsets_from_lengths(lens)
         lc = W.as_storage(rng.standard_normal((B, ell, d)).astype(np.float32), dt)
         hs = W.as_storage((rng.standard_normal((int(off[-1]), d)) * 0.5).astype(np.float32), dt)
