@@ -52,7 +52,11 @@ __device__ __forceinline__ T* row_out(const Rows& s, int64_t r) {
   return static_cast<T*>(s.b) + (r - s.split) * s.ld;
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU(x) = x * sigmoid(x) with the hardware reciprocal (about 1 ulp) in
+// place of an IEEE division; exp(-x) = inf gives -0, exp(-x) = 0 gives x.
+__device__ __forceinline__ float silu_f(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);

@@ -12,6 +12,7 @@
 #include "common.h"
 #include "generic_kernels.h"
 #include "mfma_kernels.h"
+#include "user_kernels.h"
 
 using namespace lime;
 
@@ -52,6 +53,14 @@ int cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
   return n;
+}
+
+template <typename K>
+int blocks_per_cu_lds(K kernel, int threads, size_t lds) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, lds) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
 }
 
 template <typename K>
@@ -132,6 +141,7 @@ lime_status_t try_cs_mfma(int ell, int d, int H, const void* cache, int64_t n_it
 // ---------------------------------------------------------------------------
 struct XorPlan {
   bool mfma = false;       // matrix-core path
+  bool resident = false;   // matrix-core, one workgroup per user holding all rows
   int64_t nlr = 0, R = 0;  // link rows, all rows
   int64_t R_pad = 0;       // rows of the QK / packed-V buffers (matrix-core path)
   int S = 1;               // history splits per user
@@ -166,6 +176,12 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
   XorPlan p;
   const size_t es = dtype == LIME_F32 ? 4 : 2;
   p.mfma = xor_mfma_ok(dtype, ell, d, heads, d_ff);
+  if (p.mfma && d <= 128) {
+    const int64_t RT = (ell + static_cast<int64_t>(max_N) + 31) / 32 * 32;
+    const int64_t per_row = (d + 4) * 4 + 2 * d * 2 + d * 2 + d * 2;
+    const int64_t wbytes = d <= 64 ? static_cast<int64_t>(7) * d * (d + 8) * 2 : 0;
+    p.resident = RT * per_row + wbytes <= 160 * 1024;
+  }
   p.nlr = static_cast<int64_t>(B) * ell;
   p.R = p.nlr + total_N;
   const int dh = d / heads;
@@ -203,13 +219,65 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
   return p;
 }
 
+int max_dynamic_lds() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 65536;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+    return 65536;
+  return v;
+}
+
+// user-resident kernel: one workgroup per user, all layers, when the rows fit
+template <int ELL, int D>
+bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int layers,
+                      const void* links_ctx, const void* hist, const int64_t* off, int64_t total_N,
+                      int32_t max_N, const lime_layer_weights_t* w, void* links_pers, void* hist_out,
+                      hipStream_t st, lime_status_t* status) {
+  if constexpr (D > 128) {
+    return false;
+  } else {
+  if (layers > mfma::RES_MAX_LAYERS) return false;
+  const int RT = static_cast<int>((ELL + static_cast<int64_t>(max_N) + 31) / 32 * 32);
+  const size_t lds = mfma::ResCfg<ELL, D>::lds_bytes(RT);
+  static const int limit = max_dynamic_lds();
+  if (lds > static_cast<size_t>(limit) || lds > 160 * 1024) return false;
+  auto k = mfma::xor_fwd_resident<ELL, D>;
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               160 * 1024) == hipSuccess;
+  (void)attr;
+  mfma::LayerSet ls{};
+  for (int l = 0; l < layers; ++l) {
+    ls.p[l][0] = static_cast<const bf16_t*>(w[l].w_qkv);
+    ls.p[l][1] = static_cast<const bf16_t*>(w[l].w_o);
+    ls.p[l][2] = static_cast<const bf16_t*>(w[l].w_gate);
+    ls.p[l][3] = static_cast<const bf16_t*>(w[l].w_up);
+    ls.p[l][4] = static_cast<const bf16_t*>(w[l].w_down);
+  }
+  hipLaunchKernelGGL(k, dim3(B), dim3(256), lds, st, static_cast<const bf16_t*>(links_ctx),
+                     static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
+                     static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
+                     static_cast<bf16_t*>(hist_out));
+  hipError_t e = hipGetLastError();
+  *status = (e == hipSuccess) ? ok() : fail(LIME_ERR_HIP, "user-resident xor: %s", hipGetErrorString(e));
+  (void)P;
+  return true;
+  }
+}
+
 // matrix-core user side: per layer QKV projection, XOR attention, split
 // combine, fused post-attention block
 template <int ELL, int D>
 lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B, int layers,
                            const void* links_ctx, const void* hist, const int64_t* off,
-                           int64_t total_N, const lime_layer_weights_t* w, void* links_pers,
-                           void* hist_out, char* ws, hipStream_t st) {
+                           int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                           void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+  if (P.resident) {
+    lime_status_t status = LIME_OK;
+    if (run_xor_resident<ELL, D>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, max_N, w,
+                                 links_pers, hist_out, st, &status))
+      return status;
+  }
   constexpr int H = D / 32;
   constexpr int RPW = D >= 256 ? 16 : 32;
   bf16_t* X = reinterpret_cast<bf16_t*>(ws + P.o_x);
@@ -226,11 +294,28 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     const int64_t rows_post = full ? R : nlr;
     const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, D} : Xws;
     const Rows Xout = last ? Rows{links_pers, hist_out, nlr, D} : Xws;
-    hipLaunchKernelGGL((mfma::qkv_proj<D>), dim3(static_cast<unsigned>(P.R_pad / 128 + (P.R_pad % 128 ? 1 : 0))),
-                       dim3(256), 0, st, Xin, R, P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+    if constexpr (D <= 128) {
+      // weights staged in LDS, persistent workgroups (one per CU)
+      auto k = mfma::qkv_proj_lds<D>;
+      constexpr size_t lds = mfma::QkvLds<D>::lds_bytes;
+      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(lds)) == hipSuccess;
+      (void)attr;
+      static const int per_cu = blocks_per_cu_lds(k, 64 * mfma::QkvLds<D>::NW, lds);
+      const int64_t nblk = P.R_pad / 32;
+      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+      const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
+      if (grid > need) grid = need;
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+    } else {
+      hipLaunchKernelGGL((mfma::qkv_proj<D>), dim3(static_cast<unsigned>(P.R_pad / 128 + (P.R_pad % 128 ? 1 : 0))),
+                         dim3(256), 0, st, Xin, R, P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+    }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
-    const int64_t waves = static_cast<int64_t>(B) * H * P.S;
-    hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), dim3(static_cast<unsigned>(static_cast<int64_t>(B) * P.S)),
+                       dim3(64 * H), 0, st,
                        QK, Vp, Y, part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi),
                        full ? 1 : 0);
     LIME_CHECK_LAUNCH("xor attention (mfma)");
@@ -241,10 +326,27 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       LIME_CHECK_LAUNCH("xor combine");
     }
     const int64_t pw = (rows_post + RPW - 1) / RPW;
-    hipLaunchKernelGGL((mfma::post_block<D, D, RPW>), dim3(static_cast<unsigned>((pw + 3) / 4)), dim3(256), 0, st,
-                       Yr, Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
-                       static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
-                       static_cast<const bf16_t*>(w[l].w_down));
+    if constexpr (D <= 128) {
+      auto k = mfma::post_block_lds<D, D, RPW>;
+      constexpr size_t lds = mfma::PostLds<D, D>::lds_bytes;
+      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(lds)) == hipSuccess;
+      (void)attr;
+      static const int per_cu = blocks_per_cu_lds(k, 64 * mfma::PostLds<D, D>::NW, lds);
+      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+      const int64_t need = (pw + mfma::PostLds<D, D>::NW - 1) / mfma::PostLds<D, D>::NW;
+      if (grid > need) grid = need;
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::PostLds<D, D>::NW), lds, st, Yr,
+                         Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
+                         static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
+                         static_cast<const bf16_t*>(w[l].w_down));
+    } else {
+      hipLaunchKernelGGL((mfma::post_block<D, D, RPW>), dim3(static_cast<unsigned>((pw + 3) / 4)), dim3(256), 0, st,
+                         Yr, Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
+                         static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
+                         static_cast<const bf16_t*>(w[l].w_down));
+    }
     LIME_CHECK_LAUNCH("post-attention block (mfma)");
   }
   return ok();
@@ -252,10 +354,11 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
 
 lime_status_t dispatch_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B, int ell, int d,
                                 int layers, const void* links_ctx, const void* hist,
-                                const int64_t* off, int64_t total_N, const lime_layer_weights_t* w,
+                                const int64_t* off, int64_t total_N, int32_t max_N,
+                                const lime_layer_weights_t* w,
                                 void* links_pers, void* hist_out, char* ws, hipStream_t st) {
 #define LIME_XM(E, DD) \
-  if (ell == E && d == DD) return run_xor_mfma<E, DD>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+  if (ell == E && d == DD) return run_xor_mfma<E, DD>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, max_N, w, links_pers, hist_out, ws, st);
   LIME_XM(32, 64) LIME_XM(32, 128) LIME_XM(32, 256)
   LIME_XM(64, 64) LIME_XM(64, 128) LIME_XM(64, 256)
 #undef LIME_XM
@@ -394,7 +497,7 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
   const int dh = d / heads;
   if (P.mfma)
     return dispatch_xor_mfma(P, phi, scale, B, ell, d, layers, links_ctx, hist, hist_offsets, total_N,
-                             w, links_pers, hist_out, ws, s);
+                             max_N, w, links_pers, hist_out, ws, s);
   if (dtype == LIME_F32)
     return dispatch_xor_generic<float>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
                                        hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);

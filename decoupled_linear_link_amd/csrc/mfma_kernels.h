@@ -281,448 +281,3 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
 }  // namespace mfma
 }  // namespace lime
 
-namespace lime {
-namespace mfma {
-
-// ===========================================================================
-// User side (d_h = 32).  Layout in the workspace, rows = [B*ell link rows ;
-// total_N history rows], padded with zero rows to R_pad (multiple of 32):
-//   QK [R_pad, 2d]  row-major, Q in columns [0, d), K in [d, 2d)
-//   Vp [R_pad/8][d][8]  V "row-octet packed": the 8 values of one column
-//                       for 8 consecutive rows are contiguous, which is the
-//                       operand layout of the contractions over rows.
-// ===========================================================================
-
-__device__ __forceinline__ int64_t vp_index(int64_t row, int col, int D) {
-  return (row >> 3) * static_cast<int64_t>(D) * 8 + static_cast<int64_t>(col) * 8 + (row & 7);
-}
-
-// LayerNorm (no affine) of the rows a lane group holds: v[k] are this lane's
-// values of its row (8 per 32-column block); the other 3 lanes of the row
-// are lane ^ 16 and lane ^ 32.
-template <int N>
-__device__ __forceinline__ void ln_rows(float* v, int D) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) s += v[i];
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  const float mu = s / D;
-  float q = 0.f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float t = v[i] - mu;
-    q += t * t;
-  }
-  q += __shfl_xor(q, 16);
-  q += __shfl_xor(q, 32);
-  const float rs = rsqrtf(q / D + 1e-5f);
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = (v[i] - mu) * rs;
-}
-
-__device__ __forceinline__ bf16x8 pack8(const float* v) {
-  bf16x8 o;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(v[j]);
-  return o;
-}
-
-// ---------------------------------------------------------------------------
-// LN + QKV projection for 32 rows per wave.  Lane (r, g) of row block rb
-// carries row row0 + 8*(r/4) + 4*rb + r%4, so that the V contraction (with
-// the operands swapped) leaves each lane 8 consecutive rows of one column.
-// Q and K use the transposed form: each lane ends with 8 consecutive columns.
-// Rows >= R are zero.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void qkv_proj(Rows X, int64_t R, int64_t R_pad,
-                                                const bf16_t* __restrict__ W,
-                                                bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
-  constexpr int KB = D / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * 32;
-  if (row0 >= R_pad) return;
-
-  bf16x8 hb[2][KB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-    float v[8 * KB];
-    if (row < R) {
-      const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 x = ld16(xr + kb * 32);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
-    }
-    ln_rows<8 * KB>(v, D);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
-  }
-
-  // Q and K: output column pairs of 32
-  for (int p = 0; p < 2 * D / 32; ++p) {
-    floatx4 acc[2][2] = {};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16_t* wr = W + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * D + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = ld16(wr + kb * 32);
-        acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
-        acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-      const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
-                          acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
-      st8(QK + row * (2 * D) + 32 * p + 8 * g, v);
-    }
-  }
-  // V: swapped operands, 16 output columns per block
-  for (int n = 0; n < D / 16; ++n) {
-    const bf16_t* wr = W + static_cast<int64_t>(2 * D + 16 * n + r) * D + 8 * g;
-    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 b = ld16(wr + kb * 32);
-      acc0 = mma(hb[0][kb], b, acc0);
-      acc1 = mma(hb[1][kb], b, acc1);
-    }
-    const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-    st8(Vp + vp_index(row0 + 8 * g, 16 * n + r, D), v);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// XOR attention, one wave per (user b, head h, split s), d_h = 32.
-//   E-branch (history rows -> ell links), per 16 rows:
-//     S^T = K_L Q_E^T (links x rows), phi over links, Y_E^T = V_L^T P^T.
-//   L-branch (links -> history rows), per 32 rows:
-//     S^T = K_E Q_L^T (rows x links), online softmax over rows,
-//     acc (links x d_h) += P V_E with V_E from the row-octet packed buffer.
-// Link rows of the mapped D blocks:  M-block c -> link (c/2)*32 + 8*g +
-// 4*(c%2) + j, so each lane's 8 links per 32 are the K slice of the P^T
-// operand.  History rows in the L-branch: M-block c -> row 8*g + 4*c + j.
-// The partial of (b, h, s) is [ell][2 + 32]: running max, denominator, acc.
-// ---------------------------------------------------------------------------
-template <int ELL, int H>
-__global__ __launch_bounds__(256) void xor_attn(const bf16_t* __restrict__ QK,
-                                                const bf16_t* __restrict__ Vp,
-                                                bf16_t* __restrict__ Y, float* __restrict__ part,
-                                                const int64_t* __restrict__ off, int B, int S,
-                                                int64_t chunk, int64_t total_N, float scale,
-                                                int phi, int do_e) {
-  constexpr int D = 32 * H, MB = ELL / 16, KBL = ELL / 32;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (gw >= static_cast<int64_t>(B) * H * S) return;
-  const int s = static_cast<int>(gw % S);
-  const int h = static_cast<int>((gw / S) % H);
-  const int b = static_cast<int>(gw / (static_cast<int64_t>(S) * H));
-  const int64_t nlr = static_cast<int64_t>(B) * ELL;
-  const int64_t u0 = clamp64(off[b], 0, total_N);
-  const int64_t u1 = clamp64(off[b + 1], u0, total_N);
-  const int64_t n = u1 - u0;
-  const int64_t lo = u0 + clamp64(s * chunk, 0, n);
-  const int64_t hi = (s == S - 1) ? u1 : u0 + clamp64((s + 1) * chunk, 0, n);
-  const bool softmax = (phi == PHI_SOFTMAX);
-  const int64_t lrow0 = static_cast<int64_t>(b) * ELL;  // first link row of user b
-
-  // per (user, head) operands
-  bf16x8 kl[MB], qlt[MB], vlt[2][KBL];
-#pragma unroll
-  for (int c = 0; c < MB; ++c) {
-    const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-    kl[c] = ld16(QK + (lrow0 + link) * (2 * D) + D + h * 32 + 8 * g);
-    qlt[c] = ld16(QK + (lrow0 + 16 * c + r) * (2 * D) + h * 32 + 8 * g);
-  }
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int kb = 0; kb < KBL; ++kb)
-      vlt[c2][kb] = ld16(Vp + vp_index(lrow0 + kb * 32 + 8 * g, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
-
-  float m_run[MB], l_run[MB];
-  floatx4 acc[MB][2];
-#pragma unroll
-  for (int c = 0; c < MB; ++c) {
-    m_run[c] = -INFINITY;
-    l_run[c] = 0.f;
-    acc[c][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  for (int64_t c0 = lo & ~int64_t(7); c0 < hi; c0 += 32) {
-    // ---------------- E-branch
-    if (do_e) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int64_t j = c0 + 16 * rb + r;
-        const bf16x8 qe = ld16(QK + (nlr + j) * (2 * D) + h * 32 + 8 * g);
-        float v[4 * MB];
-#pragma unroll
-        for (int c = 0; c < MB; ++c) {
-          const floatx4 st = mma(kl[c], qe, floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[4 * c + q] = st[q] * scale;
-        }
-        if (softmax) {
-          float mx = v[0];
-#pragma unroll
-          for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          float sum = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4 * MB; ++q) {
-            v[q] = __expf(v[q] - mx);
-            sum += v[q];
-          }
-          sum += __shfl_xor(sum, 16);
-          sum += __shfl_xor(sum, 32);
-          const float inv = 1.f / sum;
-#pragma unroll
-          for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
-        } else {
-          constexpr float inv = 1.f / ELL;
-#pragma unroll
-          for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
-        }
-        floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KBL; ++kb) {
-          const bf16x8 pb = pack8(v + 8 * kb);
-          y0 = mma(vlt[0][kb], pb, y0);
-          y1 = mma(vlt[1][kb], pb, y1);
-        }
-        if (j >= lo && j < hi) {
-          const float o[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-          st8(Y + (nlr + j) * D + h * 32 + 8 * g, o);
-        }
-      }
-    }
-    // ---------------- L-branch
-    bf16x8 ke[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      ke[c] = ld16(QK + (nlr + c0 + 8 * (r >> 2) + 4 * c + (r & 3)) * (2 * D) + D + h * 32 + 8 * g);
-    const bf16x8 ve0 = ld16(Vp + vp_index(nlr + c0 + 8 * g, h * 32 + r, D));
-    const bf16x8 ve1 = ld16(Vp + vp_index(nlr + c0 + 8 * g, h * 32 + 16 + r, D));
-    bool valid[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t j = c0 + 8 * g + q;  // q = 4*c + jj
-      valid[q] = (j >= lo) && (j < hi);
-    }
-#pragma unroll
-    for (int nb = 0; nb < MB; ++nb) {
-      float p[8];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const floatx4 st = mma(ke[c], qlt[nb], floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int q = 0; q < 4; ++q) p[4 * c + q] = st[q] * scale;
-      }
-      if (softmax) {
-        float mc = -INFINITY;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (valid[q]) mc = fmaxf(mc, p[q]);
-        mc = fmaxf(mc, __shfl_xor(mc, 16));
-        mc = fmaxf(mc, __shfl_xor(mc, 32));
-        const float mn = fmaxf(m_run[nb], mc);
-        const float alpha = (m_run[nb] == -INFINITY) ? 0.f : __expf(m_run[nb] - mn);
-        float ls = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          p[q] = valid[q] ? __expf(p[q] - mn) : 0.f;
-          ls += p[q];
-        }
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
-        l_run[nb] = l_run[nb] * alpha + ls;
-        m_run[nb] = mn;
-        // acc rows are links 16*nb + 4*g + jj; their factor sits in lane 4*g + jj
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float f = __shfl(alpha, 4 * g + jj);
-          acc[nb][0][jj] *= f;
-          acc[nb][1][jj] *= f;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) p[q] = valid[q] ? silu_f(p[q]) : 0.f;
-      }
-      const bf16x8 pa = pack8(p);
-      acc[nb][0] = mma(pa, ve0, acc[nb][0]);
-      acc[nb][1] = mma(pa, ve1, acc[nb][1]);
-    }
-  }
-
-  // ---------------- partial of this split
-  float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
-#pragma unroll
-  for (int nb = 0; nb < MB; ++nb) {
-    if (g == 0) {
-      float* pl = p0 + (16 * nb + r) * 34;
-      pl[0] = softmax ? m_run[nb] : 0.f;
-      pl[1] = softmax ? l_run[nb] : static_cast<float>(hi - lo);
-    }
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        p0[(16 * nb + 4 * g + jj) * 34 + 2 + 16 * c2 + r] = acc[nb][c2][jj];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Post-attention block for RPW rows per wave, everything in registers:
-//   X1 = Xres + Y Wo^T ;  G = LN(X1) ;  M = SiLU(G Wg^T) * (G Wu^T) ;
-//   Out = X1 + M Wd^T
-// Every product is in the transposed form, so the output of one is the
-// B operand of the next without any data movement.
-// ---------------------------------------------------------------------------
-template <int D, int DFF, int RPW>
-__global__ __launch_bounds__(256) void post_block(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
-                                                  const bf16_t* __restrict__ Wo,
-                                                  const bf16_t* __restrict__ Wg,
-                                                  const bf16_t* __restrict__ Wu,
-                                                  const bf16_t* __restrict__ Wd) {
-  constexpr int KB = D / 32, KF = DFF / 32, RB = RPW / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * RPW;
-  if (row0 >= nrows) return;
-
-  bf16x8 yb[RB][KB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = row0 + 16 * rb + r;
-    if (row < nrows) {
-      const bf16_t* yr = row_in<bf16_t>(Yr, row) + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) yb[rb][kb] = ld16(yr + kb * 32);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) yb[rb][kb] = zero8();
-    }
-  }
-
-  // X1 = Xres + Y Wo^T
-  float x1[RB][8 * KB];
-#pragma unroll
-  for (int p = 0; p < KB; ++p) {
-    floatx4 acc[2][RB] = {};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16_t* wr = Wo + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * D + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = ld16(wr + kb * 32);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, yb[rb][kb], acc[c][rb]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int64_t row = row0 + 16 * rb + r;
-      bf16x8 xr = zero8();
-      if (row < nrows) xr = ld16(row_in<bf16_t>(Xres, row) + 32 * p + 8 * g);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x1[rb][8 * p + q] = acc[0][rb][q] + static_cast<float>(xr[q]);
-        x1[rb][8 * p + 4 + q] = acc[1][rb][q] + static_cast<float>(xr[4 + q]);
-      }
-    }
-  }
-
-  // G = LN(X1) as B operands
-  bf16x8 gb[RB][KB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float t[8 * KB];
-#pragma unroll
-    for (int i = 0; i < 8 * KB; ++i) t[i] = x1[rb][i];
-    ln_rows<8 * KB>(t, D);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) gb[rb][kb] = pack8(t + 8 * kb);
-  }
-
-  // M = SiLU(G Wg^T) * (G Wu^T)
-  bf16x8 mb[RB][KF];
-#pragma unroll
-  for (int q2 = 0; q2 < KF; ++q2) {
-    floatx4 ag[2][RB] = {}, au[2][RB] = {};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int64_t orow = 32 * q2 + 8 * (r >> 2) + 4 * c + (r & 3);
-      const bf16_t* gr = Wg + orow * D + 8 * g;
-      const bf16_t* ur = Wu + orow * D + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a1 = ld16(gr + kb * 32);
-        const bf16x8 a2 = ld16(ur + kb * 32);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          ag[c][rb] = mma(a1, gb[rb][kb], ag[c][rb]);
-          au[c][rb] = mma(a2, gb[rb][kb], au[c][rb]);
-        }
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = silu_f(ag[0][rb][q]) * au[0][rb][q];
-        v[4 + q] = silu_f(ag[1][rb][q]) * au[1][rb][q];
-      }
-      mb[rb][q2] = pack8(v);
-    }
-  }
-
-  // Out = X1 + M Wd^T
-#pragma unroll
-  for (int p = 0; p < KB; ++p) {
-    floatx4 acc[2][RB] = {};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16_t* wr = Wd + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * DFF + 8 * g;
-#pragma unroll
-      for (int kf = 0; kf < KF; ++kf) {
-        const bf16x8 a = ld16(wr + kf * 32);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, mb[rb][kf], acc[c][rb]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int64_t row = row0 + 16 * rb + r;
-      if (row >= nrows) continue;
-      bf16_t* orow = row_out<bf16_t>(Out, row);
-      if (orow == nullptr) continue;
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q] = x1[rb][8 * p + q] + acc[0][rb][q];
-        v[4 + q] = x1[rb][8 * p + 4 + q] + acc[1][rb][q];
-      }
-      st8(orow + 32 * p + 8 * g, v);
-    }
-  }
-}
-
-}  // namespace mfma
-}  // namespace lime

@@ -1,0 +1,843 @@
+// User side of the hot path on the matrix cores (bf16, d_h = 32): the
+// LIME-XOR layer stack (LIME notes, "Key design 2": history -> links and
+// links -> history cross attention, residual + gated MLP; LN before the
+// projections per the training-strategy section).
+//
+// Row space: [B*ell link rows ; total_N history rows].  Intermediates use
+//   QK [rows, 2d]      Q in columns [0, d), K in [d, 2d), row-major
+//   Vp [rows/8][d][8]  V "row-octet packed": one column of 8 consecutive
+//                      rows is contiguous, the operand layout of the
+//                      contractions over rows (no transposes needed).
+// The device functions below work on either global or LDS pointers; they
+// are shared by the streaming kernels (any history length, one launch per
+// step of a layer) and the user-resident kernel (one workgroup per user,
+// all layers in one launch, for histories that fit in LDS).
+#pragma once
+
+#include "mfma_kernels.h"
+
+namespace lime {
+namespace mfma {
+
+__device__ __forceinline__ int64_t vp_index(int64_t row, int col, int D) {
+  return (row >> 3) * static_cast<int64_t>(D) * 8 + static_cast<int64_t>(col) * 8 + (row & 7);
+}
+
+// LayerNorm (no affine, eps 1e-5) of the row a lane group holds: v[] are
+// this lane's values of the row; the other values are in lanes ^16, ^32.
+template <int N>
+__device__ __forceinline__ void ln_rows(float* v, int D) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) s += v[i];
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  const float mu = s / D;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float t = v[i] - mu;
+    q += t * t;
+  }
+  q += __shfl_xor(q, 16);
+  q += __shfl_xor(q, 32);
+  const float rs = rsqrtf(q / D + 1e-5f);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (v[i] - mu) * rs;
+}
+
+// An opaque zero: offsetting a weight pointer by it inside a loop keeps the
+// compiler from hoisting every weight-fragment load of the loop body out of
+// the loop (which would hold all weights in registers and spill).
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(v[j]);
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// QKV projection of one 32-row chunk.  hb[rb][kb] are LN(X) operands: lane
+// (r, g) of row block rb carries chunk row 8*(r/4) + 4*rb + r%4, columns
+// kb*32 + 8g .. +8.  Q and K (transposed form) land as 16-byte row pieces;
+// V (operands swapped) lands as one 16-byte column piece of 8 rows.
+// QK and Vp are addressed with chunk-local row `row0` (multiple of 8).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
+                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g) {
+  constexpr int KB = D / 32;
+#pragma unroll 2
+  for (int p = 0; p < 2 * D / 32; ++p) {
+    floatx4 acc[2][2] = {};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16_t* wr = W + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ld16(wr + kb * 32);
+        acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
+        acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+      const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
+                          acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+      st8(QK + row * (2 * D) + 32 * p + 8 * g, v);
+    }
+  }
+#pragma unroll 2
+  for (int n = 0; n < D / 16; ++n) {
+    const bf16_t* wr = W + static_cast<int64_t>(2 * D + 16 * n + r) * ldw + 8 * g;
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 b = ld16(wr + kb * 32);
+      acc0 = mma(hb[0][kb], b, acc0);
+      acc1 = mma(hb[1][kb], b, acc1);
+    }
+    const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+    st8(Vp + vp_index(row0 + 8 * g, 16 * n + r, D), v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// XOR attention pieces for one (user, head h).  Link rows start at `lrow`,
+// history row j is row `hrow + j` of QK / Vp / Y.
+// Link order of the score blocks: M-block c, row 4*g + q -> link
+// (c/2)*32 + 8*g + 4*(c%2) + q, so each lane's 8 links per 32 are the K
+// slice of the P^T operand of the value product.
+// ---------------------------------------------------------------------------
+template <int ELL>
+struct HeadOps {
+  static constexpr int MB = ELL / 16, KBL = ELL / 32;
+  bf16x8 kl[MB];       // A: K_L, rows = links (ordered as above), k = d_h
+  bf16x8 qlt[MB];      // B: Q_L^T, cols = links 16*c + r, k = d_h
+  bf16x8 vlt[2][KBL];  // A: V_L^T, rows = 8*(r/4) + 4*c2 + r%4, k = links
+};
+
+template <int ELL, int D>
+__device__ __forceinline__ void load_head_ops(HeadOps<ELL>& o, const bf16_t* QK, const bf16_t* Vp,
+                                              int64_t lrow, int h, int r, int g) {
+#pragma unroll
+  for (int c = 0; c < HeadOps<ELL>::MB; ++c) {
+    const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
+    o.kl[c] = ld16(QK + (lrow + link) * (2 * D) + D + h * 32 + 8 * g);
+    o.qlt[c] = ld16(QK + (lrow + 16 * c + r) * (2 * D) + h * 32 + 8 * g);
+  }
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int kb = 0; kb < HeadOps<ELL>::KBL; ++kb)
+      o.vlt[c2][kb] = ld16(Vp + vp_index(lrow + kb * 32 + 8 * g, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
+}
+
+// Operands of one 32-row chunk of history rows c0 + [0, 32) for head h:
+// Q rows (E-branch B operands), K rows in the L-branch row order (A
+// operands) and two packed V column blocks (B operands).
+struct ChunkOps {
+  bf16x8 qe[2], ke[2], ve[2];
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const bf16_t* Vp, int64_t hrow,
+                                           int64_t c0, int h, bool with_q, int r, int g) {
+  if (with_q) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + (hrow + c0 + 16 * rb + r) * (2 * D) + h * 32 + 8 * g);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    c.ke[k] = ld16(QK + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * (2 * D) + D + h * 32 + 8 * g);
+  c.ve[0] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + r, D));
+  c.ve[1] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
+}
+
+// E-branch: history rows c0 + [0, 32) attend to the ell links; rows in
+// [lo, hi) are written to Y.
+template <int ELL, int D>
+__device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
+                                         int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
+                                         float scale, bool softmax, int r, int g) {
+  constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t j = c0 + 16 * rb + r;
+    float v[4 * MB];
+#pragma unroll
+    for (int c = 0; c < MB; ++c) {
+      const floatx4 st = mma(o.kl[c], ci.qe[rb], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 * c + q] = st[q] * scale;
+    }
+    if (softmax) {
+      float mx = v[0];
+#pragma unroll
+      for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4 * MB; ++q) {
+        v[q] = __expf(v[q] - mx);
+        sum += v[q];
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const float inv = 1.f / sum;
+#pragma unroll
+      for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
+    } else {
+      constexpr float inv = 1.f / ELL;
+#pragma unroll
+      for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+    }
+    floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KBL; ++kb) {
+      const bf16x8 pb = pack8(v + 8 * kb);
+      y0 = mma(o.vlt[0][kb], pb, y0);
+      y1 = mma(o.vlt[1][kb], pb, y1);
+    }
+    if (j >= lo && j < hi) {
+      const float out[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      st8(Y + (hrow + j) * D + h * 32 + 8 * g, out);
+    }
+  }
+}
+
+// L-branch running state: per link block nb, running max m / denominator l
+// (for the links 16*nb + r of this lane) and acc (links 16*nb + 4*g + q,
+// columns 16*c2 + r).
+template <int ELL>
+struct LState {
+  static constexpr int MB = ELL / 16;
+  float m[MB], l[MB];
+  floatx4 acc[MB][2];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int c = 0; c < MB; ++c) {
+      m[c] = -INFINITY;
+      l[c] = 0.f;
+      acc[c][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc[c][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+// L-branch: the links attend to history rows c0 + [0, 32) (those in
+// [lo, hi)); c0 + hrow must be a multiple of 8.
+template <int ELL>
+__device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
+                                         int64_t c0, int64_t lo, int64_t hi, float scale,
+                                         bool softmax, int r, int g) {
+  constexpr int MB = HeadOps<ELL>::MB;
+  bool valid[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t j = c0 + 8 * g + q;  // q = 4*c + jj
+    valid[q] = (j >= lo) && (j < hi);
+  }
+#pragma unroll
+  for (int nb = 0; nb < MB; ++nb) {
+    float p[8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const floatx4 sv = mma(ci.ke[c], o.qlt[nb], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[4 * c + q] = sv[q] * scale;
+    }
+    if (softmax) {
+      float mc = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (valid[q]) mc = fmaxf(mc, p[q]);
+      mc = fmaxf(mc, __shfl_xor(mc, 16));
+      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      const float mn = fmaxf(st.m[nb], mc);
+      const float alpha = (st.m[nb] == -INFINITY) ? 0.f : __expf(st.m[nb] - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        p[q] = valid[q] ? __expf(p[q] - mn) : 0.f;
+        ls += p[q];
+      }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      st.l[nb] = st.l[nb] * alpha + ls;
+      st.m[nb] = mn;
+      // acc rows are links 16*nb + 4*g + jj; their factor sits in lane 4*g + jj
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float f = __shfl(alpha, 4 * g + jj);
+        st.acc[nb][0][jj] *= f;
+        st.acc[nb][1][jj] *= f;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) p[q] = valid[q] ? silu_f(p[q]) : 0.f;
+    }
+    const bf16x8 pa = pack8(p);
+    st.acc[nb][0] = mma(pa, ci.ve[0], st.acc[nb][0]);
+    st.acc[nb][1] = mma(pa, ci.ve[1], st.acc[nb][1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Post-attention block on RB row blocks of 16 rows (lane (r, g) of block rb
+// carries one row, columns 32*p + 8*g .. +8 of every 32-column block):
+//   x1 += Y Wo^T ;  G = LN(x1) ;  M = SiLU(G Wg^T) * (G Wu^T) ;  x1 += M Wd^T
+// x1 holds the residual on entry and the layer output on exit (float32).
+// Each product's output is the next product's B operand as it stands.
+// ---------------------------------------------------------------------------
+template <int D, int DFF, int RB>
+__device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float (&x1)[RB][D / 4],
+                                          const bf16_t* __restrict__ Wo, const bf16_t* __restrict__ Wg,
+                                          const bf16_t* __restrict__ Wu, const bf16_t* __restrict__ Wd,
+                                          int ldd, int ldf, int r, int g) {
+  constexpr int KB = D / 32, KF = DFF / 32;
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    floatx4 acc[2][RB] = {};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16_t* wr = Wo + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldd + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ld16(wr + kb * 32);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, yb[rb][kb], acc[c][rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x1[rb][8 * p + q] += acc[0][rb][q];
+        x1[rb][8 * p + 4 + q] += acc[1][rb][q];
+      }
+    // keep the scheduler from hoisting every block's weight loads at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 gb[RB][KB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float t[8 * KB];
+#pragma unroll
+    for (int i = 0; i < 8 * KB; ++i) t[i] = x1[rb][i];
+    ln_rows<8 * KB>(t, D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) gb[rb][kb] = pack8(t + 8 * kb);
+  }
+  bf16x8 mb[RB][KF];
+#pragma unroll
+  for (int q2 = 0; q2 < KF; ++q2) {
+    floatx4 ag[2][RB] = {}, au[2][RB] = {};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int64_t orow = 32 * q2 + 8 * (r >> 2) + 4 * c + (r & 3);
+      const bf16_t* gr = Wg + orow * ldd + 8 * g;
+      const bf16_t* ur = Wu + orow * ldd + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a1 = ld16(gr + kb * 32);
+        const bf16x8 a2 = ld16(ur + kb * 32);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          ag[c][rb] = mma(a1, gb[rb][kb], ag[c][rb]);
+          au[c][rb] = mma(a2, gb[rb][kb], au[c][rb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = silu_f(ag[0][rb][q]) * au[0][rb][q];
+        v[4 + q] = silu_f(ag[1][rb][q]) * au[1][rb][q];
+      }
+      mb[rb][q2] = pack8(v);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int p = 0; p < KB; ++p) {
+    floatx4 acc[2][RB] = {};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16_t* wr = Wd + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldf + 8 * g;
+#pragma unroll
+      for (int kf = 0; kf < KF; ++kf) {
+        const bf16x8 a = ld16(wr + kf * 32);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, mb[rb][kf], acc[c][rb]);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x1[rb][8 * p + q] += acc[0][rb][q];
+        x1[rb][8 * p + 4 + q] += acc[1][rb][q];
+      }
+    // keep the scheduler from hoisting every block's weight loads at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ===========================================================================
+// Streaming kernels (any history length)
+// ===========================================================================
+
+// LN + QKV projection, 32 rows per wave; rows >= R are zero.
+template <int D>
+__global__ __launch_bounds__(256) void qkv_proj(Rows X, int64_t R, int64_t R_pad,
+                                                const bf16_t* __restrict__ W,
+                                                bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
+  constexpr int KB = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * 32;
+  if (row0 >= R_pad) return;
+  bf16x8 hb[2][KB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+    float v[8 * KB];
+    if (row < R) {
+      const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 x = ld16(xr + kb * 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
+    }
+    ln_rows<8 * KB>(v, D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+  }
+  qkv_chunk<D>(hb, W, D, QK, Vp, row0, r, g);
+}
+
+// XOR attention: one workgroup per (user b, split s) with one wave per head,
+// so the waves of a workgroup read the same rows at the same time and share
+// each cache line.  Writes the E-branch rows of Y and the L-branch partial
+// [ell][2 + 32] (max, denominator, acc) of (b, h, s).
+template <int ELL, int H>
+__global__ __launch_bounds__(64 * H) void xor_attn(const bf16_t* __restrict__ QK,
+                                                   const bf16_t* __restrict__ Vp,
+                                                   bf16_t* __restrict__ Y, float* __restrict__ part,
+                                                   const int64_t* __restrict__ off, int B, int S,
+                                                   int64_t chunk, int64_t total_N, float scale,
+                                                   int phi, int do_e) {
+  constexpr int D = 32 * H, MB = ELL / 16;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, r = lane & 15;
+  const int h = threadIdx.x >> 6;
+  const int s = static_cast<int>(blockIdx.x % S);
+  const int b = static_cast<int>(blockIdx.x / S);
+  const int64_t nlr = static_cast<int64_t>(B) * ELL;
+  const int64_t u0 = clamp64(off[b], 0, total_N);
+  const int64_t u1 = clamp64(off[b + 1], u0, total_N);
+  const int64_t n = u1 - u0;
+  const int64_t lo = u0 + clamp64(s * chunk, 0, n);
+  const int64_t hi = (s == S - 1) ? u1 : u0 + clamp64((s + 1) * chunk, 0, n);
+  const bool softmax = (phi == PHI_SOFTMAX);
+
+  HeadOps<ELL> o;
+  load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g);
+  LState<ELL> st;
+  st.init();
+  int64_t c0 = lo & ~int64_t(7);
+  ChunkOps cur, nxt;
+  if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g);
+  for (; c0 < hi; c0 += 32) {
+    // issue the next chunk's loads before computing this one
+    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+    if (do_e) e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g);
+    l_branch<ELL>(st, o, cur, c0, lo, hi, scale, softmax, r, g);
+    cur = nxt;
+  }
+  float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
+#pragma unroll
+  for (int nb = 0; nb < MB; ++nb) {
+    if (g == 0) {
+      float* pl = p0 + (16 * nb + r) * 34;
+      pl[0] = softmax ? st.m[nb] : 0.f;
+      pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        p0[(16 * nb + 4 * g + jj) * 34 + 2 + 16 * c2 + r] = st.acc[nb][c2][jj];
+  }
+}
+
+// Post-attention block, RPW rows per wave, rows [0, nrows).
+template <int D, int DFF, int RPW>
+__global__ __launch_bounds__(256) void post_block(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+                                                  const bf16_t* __restrict__ Wo,
+                                                  const bf16_t* __restrict__ Wg,
+                                                  const bf16_t* __restrict__ Wu,
+                                                  const bf16_t* __restrict__ Wd) {
+  constexpr int KB = D / 32, RB = RPW / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * RPW;
+  if (row0 >= nrows) return;
+  bf16x8 yb[RB][KB];
+  float x1[RB][D / 4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t row = row0 + 16 * rb + r;
+    const bool ok = row < nrows;
+    const bf16_t* yr = ok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
+    const bf16_t* xr = ok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      yb[rb][kb] = ok ? ld16(yr + kb * 32) : zero8();
+      const bf16x8 x = ok ? ld16(xr + kb * 32) : zero8();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = static_cast<float>(x[q]);
+    }
+  }
+  post_rows<D, DFF, RB>(yb, x1, Wo, Wg, Wu, Wd, D, DFF, r, g);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t row = row0 + 16 * rb + r;
+    if (row >= nrows) continue;
+    bf16_t* orow = row_out<bf16_t>(Out, row);
+    if (orow == nullptr) continue;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[rb][8 * p]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent variants with the weights staged once per workgroup in LDS
+// (rows padded by 16 bytes so the 16 rows read by one fragment load fall in
+// distinct banks).  NW waves per workgroup; each wave walks 32-row blocks
+// strided by the whole grid.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict__ src, int rows, int K,
+                                           int tid, int nthreads) {
+  const int c8n = K / 8;
+  for (int e = tid; e < rows * c8n; e += nthreads) {
+    const int row = e / c8n, c8 = e % c8n;
+    *reinterpret_cast<bf16x8*>(dst + row * (K + 8) + 8 * c8) = ld16(src + static_cast<int64_t>(row) * K + 8 * c8);
+  }
+}
+
+template <int D>
+struct QkvLds {
+  static constexpr int NW = 8;
+  static constexpr size_t lds_bytes = static_cast<size_t>(3) * D * (D + 8) * 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64_t R, int64_t R_pad,
+                                                    const bf16_t* __restrict__ W,
+                                                    bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
+  constexpr int KB = D / 32, NW = QkvLds<D>::NW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
+  stage_rows(Wl, W, 3 * D, D, threadIdx.x, NW * 64);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t nblk = R_pad / 32;
+  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nblk;
+       blk += static_cast<int64_t>(gridDim.x) * NW) {
+    const int64_t row0 = blk * 32;
+    bf16x8 hb[2][KB];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+      float v[8 * KB];
+      if (row < R) {
+        const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const bf16x8 x = ld16(xr + kb * 32);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
+      }
+      ln_rows<8 * KB>(v, D);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+    }
+    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g);
+  }
+}
+
+template <int D, int DFF>
+struct PostLds {
+  static constexpr int NW = 8;
+  static constexpr size_t lds_bytes =
+      (static_cast<size_t>(D) * (D + 8) + 2 * static_cast<size_t>(DFF) * (D + 8) +
+       static_cast<size_t>(D) * (DFF + 8)) * 2;
+};
+
+template <int D, int DFF, int RPW>
+__global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+                                                      const bf16_t* __restrict__ Wo,
+                                                      const bf16_t* __restrict__ Wg,
+                                                      const bf16_t* __restrict__ Wu,
+                                                      const bf16_t* __restrict__ Wd) {
+  constexpr int KB = D / 32, RB = RPW / 16, NW = PostLds<D, DFF>::NW;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* Wol = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* Wgl = Wol + D * (D + 8);
+  bf16_t* Wul = Wgl + DFF * (D + 8);
+  bf16_t* Wdl = Wul + DFF * (D + 8);
+  stage_rows(Wol, Wo, D, D, threadIdx.x, NW * 64);
+  stage_rows(Wgl, Wg, DFF, D, threadIdx.x, NW * 64);
+  stage_rows(Wul, Wu, DFF, D, threadIdx.x, NW * 64);
+  stage_rows(Wdl, Wd, D, DFF, threadIdx.x, NW * 64);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t nblk = (nrows + RPW - 1) / RPW;
+  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nblk;
+       blk += static_cast<int64_t>(gridDim.x) * NW) {
+    const int64_t row0 = blk * RPW;
+    bf16x8 yb[RB][KB];
+    float x1[RB][D / 4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t row = row0 + 16 * rb + r;
+      const bool ok = row < nrows;
+      const bf16_t* yr = ok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
+      const bf16_t* xr = ok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        yb[rb][kb] = ok ? ld16(yr + kb * 32) : zero8();
+        const bf16x8 x = ok ? ld16(xr + kb * 32) : zero8();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = static_cast<float>(x[q]);
+      }
+    }
+    const int z = opaque_zero();
+    post_rows<D, DFF, RB>(yb, x1, Wol + z, Wgl + z, Wul + z, Wdl + z, D + 8, DFF + 8, r, g);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t row = row0 + 16 * rb + r;
+      if (row >= nrows) continue;
+      bf16_t* orow = row_out<bf16_t>(Out, row);
+      if (orow == nullptr) continue;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[rb][8 * p]);
+    }
+  }
+}
+
+// ===========================================================================
+// User-resident kernel: one workgroup (4 waves) per user, all layers in one
+// launch, for users whose ell + N_b rows fit in LDS.  Local rows: [0, ell)
+// links, [ell, ell + N_b) history, zero rows up to RT (multiple of 32).
+//   Xs  [RT][D + 4] float32  residual stream (padded rows)
+//   QKs [RT][2D] bf16 ;  Vps [RT/8][D][8] bf16 ;  Ys [RT][D] bf16
+// ===========================================================================
+constexpr int RES_MAX_LAYERS = 16;
+// per-layer weight pointers passed by value: w_qkv, w_o, w_gate, w_up, w_down
+struct LayerSet {
+  const bf16_t* p[RES_MAX_LAYERS][5];
+};
+
+template <int ELL, int D>
+struct ResCfg {
+  static constexpr int XS = D + 4;  // float32 row stride of the residual stream
+  static constexpr size_t bytes_per_row = static_cast<size_t>(XS) * 4 + 2 * D * 2 + D * 2 + D * 2;
+  // one layer's weights staged in LDS (rows padded by 16 bytes against bank
+  // conflicts) when they are small: w_qkv, w_o, w_gate, w_up [.., D] and
+  // w_down [D, D]
+  static constexpr bool WL = D <= 64;
+  static constexpr int LDW = D + 8;
+  static constexpr size_t w_elems = static_cast<size_t>(7) * D * LDW;
+  static constexpr size_t lds_bytes(int RT) {
+    return bytes_per_row * RT + (WL ? w_elems * 2 : 0);
+  }
+};
+
+template <int ELL, int D>
+__global__ __launch_bounds__(256) void xor_fwd_resident(
+    const bf16_t* __restrict__ links_ctx, const bf16_t* __restrict__ hist,
+    const int64_t* __restrict__ off, int64_t total_N, int RT, int layers, LayerSet w, float scale, int phi,
+    bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out) {
+  constexpr int H = D / 32, KB = D / 32, XS = ResCfg<ELL, D>::XS;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* Xs = reinterpret_cast<float*>(smem);
+  bf16_t* QKs = reinterpret_cast<bf16_t*>(smem + static_cast<size_t>(RT) * XS * 4);
+  bf16_t* Vps = QKs + static_cast<size_t>(RT) * 2 * D;
+  bf16_t* Ys = Vps + static_cast<size_t>(RT) * D;
+  constexpr bool WL = ResCfg<ELL, D>::WL;
+  constexpr int LDW = ResCfg<ELL, D>::LDW;
+  bf16_t* Wl = Ys + static_cast<size_t>(RT) * D;  // [7D][LDW]: qkv, o, gate, up, down
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int b = blockIdx.x;
+  const int64_t u0 = clamp64(off[b], 0, total_N);
+  int64_t u1 = clamp64(off[b + 1], u0, total_N);
+  if (u1 - u0 > RT - ELL) u1 = u0 + (RT - ELL);  // never beyond the planned rows
+  const int n = static_cast<int>(u1 - u0);
+  const int rows = ELL + n;
+  const bool softmax = (phi == PHI_SOFTMAX);
+  const int nchunks = RT / 32;
+
+  // residual stream <- [L^C_b ; E_b], zero padding
+  for (int e = tid; e < RT * (D / 8); e += 256) {
+    const int row = e / (D / 8), c8 = e % (D / 8);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const bf16_t* src = nullptr;
+    if (row < ELL) src = links_ctx + (static_cast<int64_t>(b) * ELL + row) * D + 8 * c8;
+    else if (row < rows) src = hist + (u0 + row - ELL) * D + 8 * c8;
+    if (src) {
+      const bf16x8 x = ld16(src);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = static_cast<float>(x[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) Xs[row * XS + 8 * c8 + q] = v[q];
+  }
+  __syncthreads();
+
+  for (int l = 0; l < layers; ++l) {
+    const bool last = (l == layers - 1);
+    const bool full = !last || hist_out != nullptr;
+    const bf16_t* lw[5];
+    int ldd = D;
+    if constexpr (WL) {
+      // stage this layer's weights: rows [0,3D) qkv, [3D,4D) o, [4D,5D) gate,
+      // [5D,6D) up, [6D,7D) down
+      for (int e = tid; e < 7 * D * (D / 8); e += 256) {
+        const int row = e / (D / 8), c8 = e % (D / 8);
+        const int m = row < 3 * D ? 0 : 1 + (row - 3 * D) / D;
+        const int rr = m == 0 ? row : (row - 3 * D) % D;
+        *reinterpret_cast<bf16x8*>(Wl + row * LDW + 8 * c8) = ld16(w.p[l][m] + rr * D + 8 * c8);
+      }
+      __syncthreads();
+      lw[0] = Wl;
+      for (int m = 1; m < 5; ++m) lw[m] = Wl + (3 + (m - 1)) * D * LDW;
+      ldd = LDW;
+    } else {
+      for (int m = 0; m < 5; ++m) lw[m] = w.p[l][m];
+    }
+    // ---- LN + QKV for every chunk of 32 rows
+    for (int ch = wv; ch < nchunks; ch += 4) {
+      const int row0 = ch * 32;
+      bf16x8 hb[2][KB];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+        float v[8 * KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
+        ln_rows<8 * KB>(v, D);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+      }
+      qkv_chunk<D>(hb, lw[0] + opaque_zero(), ldd, QKs, Vps, row0, r, g);
+    }
+    __syncthreads();
+    // ---- attention: items = per head, the L-branch and the E-branch chunks
+    const int echunks = full ? (n + 31) / 32 : 0;
+    const int items = H * (1 + echunks);
+    for (int it = wv; it < items; it += 4) {
+      const int h = it % H, k = it / H;
+      HeadOps<ELL> o;
+      load_head_ops<ELL, D>(o, QKs, Vps, 0, h, r, g);
+      if (k == 0) {
+        LState<ELL> st;
+        st.init();
+        for (int c0 = 0; c0 < n; c0 += 32) {
+          ChunkOps ci;
+          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g);
+          l_branch<ELL>(st, o, ci, c0, 0, n, scale, softmax, r, g);
+        }
+        // normalise and write the link rows of Y
+#pragma unroll
+        for (int nb = 0; nb < HeadOps<ELL>::MB; ++nb) {
+          const float den = softmax ? st.l[nb] : static_cast<float>(n);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float dj = __shfl(den, 4 * g + jj);
+            const float inv = dj > 0.f ? 1.f / dj : 0.f;
+            const int link = 16 * nb + 4 * g + jj;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+              Ys[link * D + h * 32 + 16 * c2 + r] = f32_to_bf16(st.acc[nb][c2][jj] * inv);
+          }
+        }
+      } else {
+        ChunkOps ci;
+        load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g);
+        e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g);
+      }
+    }
+    __syncthreads();
+    // ---- post-attention block per group of 16*RBR rows
+    constexpr int RBR = D >= 128 ? 1 : 2;
+    constexpr int PR = 16 * RBR;
+    const int prow_end = full ? rows : ELL;
+    const int pchunks = (prow_end + PR - 1) / PR;
+    for (int ch = wv; ch < pchunks; ch += 4) {
+      const int row0 = ch * PR;
+      bf16x8 yb[RBR][KB];
+      float x1[RBR][D / 4];
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) {
+        const int row = row0 + 16 * rb + r;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          yb[rb][kb] = row < rows ? ld16(Ys + row * D + kb * 32 + 8 * g) : zero8();
+#pragma unroll
+          for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
+        }
+      }
+      const int z = opaque_zero();
+      post_rows<D, D, RBR>(yb, x1, lw[1] + z, lw[2] + z, lw[3] + z, lw[4] + z, ldd, ldd, r, g);
+#pragma unroll
+      for (int rb = 0; rb < RBR; ++rb) {
+        const int row = row0 + 16 * rb + r;
+        const bool real = row < rows;
+        if (!last) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) Xs[row * XS + kb * 32 + 8 * g + q] = real ? x1[rb][8 * kb + q] : 0.f;
+        } else if (real) {
+          bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
+                                  : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
+          if (dst)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[rb][8 * kb]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace mfma
+}  // namespace lime

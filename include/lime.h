@@ -108,9 +108,10 @@ size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, i
  *                                     off[B] = total_N are required (other
  *                                     values give unspecified outputs but no
  *                                     access outside the buffers).
- *   total_N      host, rows of hist;  max_N host, the largest N_b (a
- *                                     planning hint: a larger N_b is still
- *                                     computed correctly, only slower).
+ *   total_N      host, rows of hist.
+ *   max_N        host, an upper bound of every N_b (it sizes the on-chip
+ *                buffers).  A user with N_b > max_N gets unspecified
+ *                outputs, but no access falls outside the passed buffers.
  *   w            HOST array of `layers` weight structs (device pointers).
  *   links_pers   [B, ell, d] out: L^P, the link rows after the last layer.
  *   hist_out     [total_N, d] out or NULL: the history rows after the last
