@@ -9,11 +9,13 @@ Inputs are resident in HBM before the timed region starts.
     python bench.py [--steps K] [--warmup W] [--workload ctr] [--no-cpu-baseline]
 
 Prints ONE JSON line.  `value` = candidates scored per second of whole-step
-time; users encoded/s and items cached/s are reported alongside.  The
-`roofline` object is for the kernel with the largest share of step time,
-measured with HIP events on the launch stream over a second pass of the
-same K steps; `cpu_baseline` is the CPU oracle timed on a bounded sample of
-the same workload.
+time; users encoded/s and items cached/s are reported alongside.  The K
+timed steps are captured in one HIP graph and replayed once (every kernel
+of every step is a graph node; --no-graph launches them eagerly instead).  The `roofline` object is
+for the kernel with the largest share of step time, its duration measured
+with HIP events on the launch stream around a graph of K back-to-back calls;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -41,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the timed steps eagerly instead of replaying a HIP graph of one step")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -84,64 +90,113 @@ def main():
     out = torch.empty((len(ids), w.d), dtype=dt, device="cuda")
     ws_bytes = L.xor_fwd_workspace_size(dt, w.B, w.ell, w.d, w.heads, w.dff, total_N, max_N)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
 
-    def user():
+    def user(stream=None):
         L.xor_fwd(lc, hs, hoff, wts, heads=w.heads, phi=w.phi, scale=scale, max_N=max_N,
                   links_pers=lp, workspace=ws, stream=stream)
 
-    def build():
+    def build(stream=None):
         L.qk_cache_build(items, keys, phi=w.phi, scale=scale, cache=cache, stream=stream)
 
-    def score():
+    def score(stream=None):
         L.cand_score(cache, lp, ids_d, coff_d, out=out, stream=stream)
 
-    def step():
-        user()
-        build()
-        score()
+    def step(stream=None):
+        user(stream)
+        build(stream)
+        score(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    def capture(fn, reps):
+        """A HIP graph of `reps` back-to-back calls of fn (kernels only, no
+        allocation or memset inside)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    # one HIP graph holding exactly the K timed steps (every kernel of every
+    # step is a node), so host launch costs do not pace the GPU
+    graph = None if args.no_graph else capture(step, args.steps)
+    if graph is not None:
+        graph.replay()  # warm replay, outside the timed region
+        torch.cuda.synchronize()
+
     # ---- timed region: exactly K steps
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
 
-    # ---- per-call breakdown with HIP events on the launch stream
+    # ---- per-call average duration: HIP events on the launch stream around
+    # a graph of K back-to-back calls (no host gaps between the kernels)
     calls = {"lime_xor_fwd": user, "lime_qk_cache_build": build, "lime_cand_score": score}
-    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k in calls}
-    for i in range(args.steps):
-        for k, fn in calls.items():
-            ev[k][i][0].record(stream)
-            fn()
-            ev[k][i][1].record(stream)
-    torch.cuda.synchronize()
-    call_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) for k in calls}
+    call_ms = {}
+    for k, fn in calls.items():
+        g = capture(fn, args.steps)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        call_ms[k] = e0.elapsed_time(e1) / args.steps
+        del g
 
-    # algorithmic bytes / flops per launch of the single-kernel calls
+    # roofline of the kernel with the largest share of step time among the
+    # calls that are one kernel launch (lime_xor_fwd is one launch on the
+    # user-resident path)
     n_cand = len(ids)
+    launches, plan = L.xor_fwd_plan(dt, w.B, w.ell, w.d, w.heads, w.layers, w.dff, total_N, max_N)
     algo = {
-        "lime_qk_cache_build": dict(kernel="qk_cache_build", bytes=w.n_items * (w.d + w.heads * w.ell) * es,
+        "lime_qk_cache_build": dict(kernel="qk_cache", bound="hbm",
+                                    bytes=w.n_items * (w.d + w.heads * w.ell) * es,
                                     flops=2.0 * w.n_items * w.d * w.heads * w.ell),
-        "lime_cand_score": dict(kernel="cand_score", bytes=n_cand * (w.heads * w.ell * es + w.d * es + 8),
+        "lime_cand_score": dict(kernel="cand_score", bound="hbm",
+                                bytes=n_cand * (w.heads * w.ell * es + w.d * es + 8),
                                 flops=2.0 * n_cand * w.ell * w.d),
     }
+    if launches == 1:
+        algo["lime_xor_fwd"] = dict(kernel="xor_fwd_resident", bound="mfma",
+                                    bytes=(w.B * w.ell * 2 + total_N) * w.d * es,
+                                    flops=xor_fwd_flops(w, np.diff(off)))
     single = {k: v for k, v in call_ms.items() if k in algo}
     dom = max(single, key=single.get)
     a = algo[dom]
     t = single[dom] * 1e-3
-    achieved = a["bytes"] / t / 1e9
-    roofline = {"kernel": a["kernel"], "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_launch_us": round(single[dom] * 1e3, 2),
-                "algorithmic_bytes_per_launch": int(a["bytes"])}
+    if a["bound"] == "hbm":
+        achieved, peak, unit = a["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = a["flops"] / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    roofline = {"kernel": a["kernel"], "bound": a["bound"], "achieved": round(achieved, 2),
+                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic_from_profiles(w.name, a["kernel"]),
+                "avg_launch_us": round(single[dom] * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(a["bytes"]),
+                "algorithmic_flops_per_launch": float(a["flops"])}
+    per_call = {}
+    for k, v in algo.items():
+        tk = call_ms[k] * 1e-3
+        per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "GB/s": round(v["bytes"] / tk / 1e9, 1),
+                       "TFLOP/s": round(v["flops"] / tk / 1e12, 2)}
+
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     res = {
         "metric": "candidates scored/sec + user histories encoded/sec; % HBM/MFMA roofline",
@@ -164,12 +219,56 @@ def main():
         "users_per_s": w.B / (ms_step * 1e-3),
         "items_per_s": w.n_items / (ms_step * 1e-3),
         "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
+        "per_call": per_call,
+        "xor_fwd_plan": plan,
+        "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
         "roofline": roofline,
     }
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, ui, ci, ids, coff, scale, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def xor_fwd_flops(w, lens):
+    """Algorithmic flops of one lime_xor_fwd call without hist_out: every
+    layer projects all rows (QKV 6d^2, W_o 2d^2, gated MLP 6 d d_ff per row)
+    and runs both XOR branches (8 ell N d per user); the last layer needs
+    only the K,V projection of history rows (4d^2) and the link-side branch
+    (4 ell N d)."""
+    d, f, ell, L = w.d, w.dff, w.ell, w.layers
+    N = float(np.sum(lens))
+    rows_link = w.B * ell
+    full = (rows_link + N) * (8 * d * d + 6 * d * f) + 8 * ell * N * d
+    last = rows_link * (8 * d * d + 6 * d * f) + N * 4 * d * d + 4 * ell * N * d
+    return (L - 1) * full + last
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE in
+    KiB per dispatch, scaled by the copy-kernel factors recorded there), or
+    None if there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        csrc = os.path.join(ROOT, "decoupled_linear_link_amd", "csrc")
+        for f in sorted(os.listdir(csrc)):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+        if kv.get("sources_sha256") != h.hexdigest():
+            return None
+        return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])
+                   + float(kv["write_kib"]) * 1024 * float(kv["write_factor"]))
+    except (KeyError, ValueError, OSError):
+        return None
 
 
 def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):

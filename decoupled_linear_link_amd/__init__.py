@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = [
-    "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "qk_cache_build",
+    "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "xor_fwd_plan", "qk_cache_build",
     "cand_score", "PHI", "DTYPE", "EXPORTED",
 ]
 
@@ -30,7 +30,7 @@ lib_path = os.path.join(_HERE, "_lib", "liblime.so")
 if not os.path.exists(lib_path):
     raise ImportError(
         f"{lib_path} is missing: build it first with "
-        "`python -m decoupled_linear_link_amd.build` (hipcc, gfx950)")
+        "`python decoupled_linear_link_amd/build.py` (hipcc, gfx950)")
 
 lib = ctypes.CDLL(lib_path)
 
@@ -40,8 +40,8 @@ STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
           3: "LIME_ERR_WORKSPACE", 4: "LIME_ERR_HIP"}
 
 # every symbol include/lime.h declares
-EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_workspace_size", "lime_qk_cache_build",
-            "lime_cand_score", "lime_status_string", "lime_last_error")
+EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_workspace_size", "lime_xor_fwd_plan",
+            "lime_qk_cache_build", "lime_cand_score", "lime_status_string", "lime_last_error")
 
 
 class LayerWeights(ctypes.Structure):
@@ -57,6 +57,9 @@ lib.lime_last_error.restype = ctypes.c_char_p
 lib.lime_last_error.argtypes = []
 lib.lime_xor_fwd_workspace_size.restype = ctypes.c_size_t
 lib.lime_xor_fwd_workspace_size.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i64, _i32]
+lib.lime_xor_fwd_plan.restype = ctypes.c_int32
+lib.lime_xor_fwd_plan.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32,
+                                  ctypes.c_char_p, ctypes.c_size_t]
 lib.lime_xor_fwd.restype = ctypes.c_int
 lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _vp, _vp, _vp, _i64, _i32, ctypes.POINTER(LayerWeights), _vp, _vp,
@@ -113,6 +116,14 @@ def _want(t, name, dtype=None, dims=None):
 
 def xor_fwd_workspace_size(dtype, B, ell, d, heads, d_ff, total_N, max_N) -> int:
     return int(lib.lime_xor_fwd_workspace_size(DTYPE[dtype], B, ell, d, heads, d_ff, total_N, max_N))
+
+
+def xor_fwd_plan(dtype, B, ell, d, heads, layers, d_ff, total_N, max_N, with_hist=False):
+    """(number of kernel launches, description) of the plan lime_xor_fwd uses."""
+    buf = ctypes.create_string_buffer(256)
+    n = lib.lime_xor_fwd_plan(DTYPE[dtype], B, ell, d, heads, layers, d_ff, total_N, max_N,
+                              int(bool(with_hist)), buf, 256)
+    return int(n), buf.value.decode()
 
 
 def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",

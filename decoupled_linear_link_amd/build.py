@@ -1,6 +1,9 @@
 """Build the HIP library liblime.so for gfx950, in-tree.
 
-    python -m decoupled_linear_link_amd.build
+    python decoupled_linear_link_amd/build.py     (or __graft_entry__.build())
+
+Run it by path: importing the package first would load the library being
+rebuilt.
 
 hipcc cross-compiles without a GPU.  The library links the HIP runtime that
 PyTorch ships (with an rpath to it), so a process that also uses torch holds

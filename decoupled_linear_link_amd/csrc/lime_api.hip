@@ -178,7 +178,7 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
   p.mfma = xor_mfma_ok(dtype, ell, d, heads, d_ff);
   if (p.mfma && d <= 128) {
     const int64_t RT = (ell + static_cast<int64_t>(max_N) + 31) / 32 * 32;
-    const int64_t per_row = (d + 4) * 4 + 2 * d * 2 + d * 2 + d * 2;
+    const int64_t per_row = (d + 4) * 4 + (2 * d + 8) * 2 + d * 2 + (d + 8) * 2;
     const int64_t wbytes = d <= 64 ? static_cast<int64_t>(7) * d * (d + 8) * 2 : 0;
     p.resident = RT * per_row + wbytes <= 160 * 1024;
   }
@@ -254,7 +254,7 @@ bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int 
     ls.p[l][3] = static_cast<const bf16_t*>(w[l].w_up);
     ls.p[l][4] = static_cast<const bf16_t*>(w[l].w_down);
   }
-  hipLaunchKernelGGL(k, dim3(B), dim3(256), lds, st, static_cast<const bf16_t*>(links_ctx),
+  hipLaunchKernelGGL(k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
                      static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
                      static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
                      static_cast<bf16_t*>(hist_out));
@@ -459,6 +459,33 @@ size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, i
                                    int32_t heads, int32_t d_ff, int64_t total_N, int32_t max_N) {
   if (check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N) != LIME_OK) return 0;
   return plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N).total;
+}
+
+int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
+                          int32_t layers, int32_t d_ff, int64_t total_N, int32_t max_N,
+                          int32_t with_hist, char* buf, size_t buf_len) {
+  if (check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N) != LIME_OK || layers < 1) return 0;
+  const XorPlan P = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  const bool resident = P.mfma && P.resident && d <= 128 && layers <= mfma::RES_MAX_LAYERS;
+  int32_t launches;
+  char line[256];
+  if (resident) {
+    launches = 1;
+    snprintf(line, sizeof(line), "user-resident: 1 launch for %d layers, one workgroup per user", layers);
+  } else if (P.mfma) {
+    launches = 4 * layers;
+    snprintf(line, sizeof(line),
+             "streaming matrix-core: 4 launches per layer (qkv, xor_attn, combine, post), "
+             "%d splits per user of %lld rows", P.S, static_cast<long long>(P.chunk));
+  } else {
+    launches = 6 * layers;
+    snprintf(line, sizeof(line),
+             "generic: 6 launches per layer, %d splits per user of %lld rows", P.S,
+             static_cast<long long>(P.chunk));
+  }
+  (void)with_hist;
+  if (buf && buf_len > 0) snprintf(buf, buf_len, "%s", line);
+  return launches;
 }
 
 lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,

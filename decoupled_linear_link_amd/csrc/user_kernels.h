@@ -70,8 +70,8 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 // QK and Vp are addressed with chunk-local row `row0` (multiple of 8).
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
-                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g) {
+__device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
+                                        int ldw, bf16_t* QK, int64_t row0, int r, int g, int ldqk = 2 * D) {
   constexpr int KB = D / 32;
 #pragma unroll 2
   for (int p = 0; p < 2 * D / 32; ++p) {
@@ -91,9 +91,15 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
       const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
       const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
                           acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
-      st8(QK + row * (2 * D) + 32 * p + 8 * g, v);
+      st8(QK + row * ldqk + 32 * p + 8 * g, v);
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void v_part(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
+                                       int ldw, bf16_t* Vp, int64_t row0, int r, int g) {
+  constexpr int KB = D / 32;
 #pragma unroll 2
   for (int n = 0; n < D / 16; ++n) {
     const bf16_t* wr = W + static_cast<int64_t>(2 * D + 16 * n + r) * ldw + 8 * g;
@@ -107,6 +113,13 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
     const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
     st8(Vp + vp_index(row0 + 8 * g, 16 * n + r, D), v);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
+                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g) {
+  qk_part<D>(hb, W, ldw, QK, row0, r, g);
+  v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -126,12 +139,12 @@ struct HeadOps {
 
 template <int ELL, int D>
 __device__ __forceinline__ void load_head_ops(HeadOps<ELL>& o, const bf16_t* QK, const bf16_t* Vp,
-                                              int64_t lrow, int h, int r, int g) {
+                                              int64_t lrow, int h, int r, int g, int ldqk = 2 * D) {
 #pragma unroll
   for (int c = 0; c < HeadOps<ELL>::MB; ++c) {
     const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-    o.kl[c] = ld16(QK + (lrow + link) * (2 * D) + D + h * 32 + 8 * g);
-    o.qlt[c] = ld16(QK + (lrow + 16 * c + r) * (2 * D) + h * 32 + 8 * g);
+    o.kl[c] = ld16(QK + (lrow + link) * ldqk + D + h * 32 + 8 * g);
+    o.qlt[c] = ld16(QK + (lrow + 16 * c + r) * ldqk + h * 32 + 8 * g);
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
@@ -149,14 +162,14 @@ struct ChunkOps {
 
 template <int D>
 __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const bf16_t* Vp, int64_t hrow,
-                                           int64_t c0, int h, bool with_q, int r, int g) {
+                                           int64_t c0, int h, bool with_q, int r, int g, int ldqk = 2 * D) {
   if (with_q) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + (hrow + c0 + 16 * rb + r) * (2 * D) + h * 32 + 8 * g);
+    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + (hrow + c0 + 16 * rb + r) * ldqk + h * 32 + 8 * g);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    c.ke[k] = ld16(QK + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * (2 * D) + D + h * 32 + 8 * g);
+    c.ke[k] = ld16(QK + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * ldqk + D + h * 32 + 8 * g);
   c.ve[0] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + r, D));
   c.ve[1] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
 }
@@ -166,7 +179,7 @@ __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const 
 template <int ELL, int D>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
-                                         float scale, bool softmax, int r, int g) {
+                                         float scale, bool softmax, int r, int g, int ldy = D) {
   constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -209,7 +222,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
     }
     if (j >= lo && j < hi) {
       const float out[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-      st8(Y + (hrow + j) * D + h * 32 + 8 * g, out);
+      st8(Y + (hrow + j) * ldy + h * 32 + 8 * g, out);
     }
   }
 }
@@ -650,11 +663,18 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Row
 }
 
 // ===========================================================================
-// User-resident kernel: one workgroup (4 waves) per user, all layers in one
+// User-resident kernel: one workgroup (8 waves) per user, all layers in one
 // launch, for users whose ell + N_b rows fit in LDS.  Local rows: [0, ell)
 // links, [ell, ell + N_b) history, zero rows up to RT (multiple of 32).
 //   Xs  [RT][D + 4] float32  residual stream (padded rows)
 //   QKs [RT][2D] bf16 ;  Vps [RT/8][D][8] bf16 ;  Ys [RT][D] bf16
+//   (D <= 64) one layer's weights, rows padded by 16 bytes:
+//   Wq [3D][D+8] (w_qkv) ; Wp [4D][D+8] (w_o, w_gate, w_up, w_down)
+// Phases per layer, separated by barriers: LN+QKV (items: 32-row chunk x
+// {Q|K, V}), attention (items: per head the L-branch and each 32-row
+// E-branch chunk), post-attention block (items: 16-row blocks).  The next
+// layer's weights are loaded into registers while the current layer runs
+// and written to LDS once their region is free.
 // ===========================================================================
 constexpr int RES_MAX_LAYERS = 16;
 // per-layer weight pointers passed by value: w_qkv, w_o, w_gate, w_up, w_down
@@ -664,33 +684,52 @@ struct LayerSet {
 
 template <int ELL, int D>
 struct ResCfg {
+  static constexpr int NW = 8;
+  static constexpr int NT = 64 * NW;
   static constexpr int XS = D + 4;  // float32 row stride of the residual stream
-  static constexpr size_t bytes_per_row = static_cast<size_t>(XS) * 4 + 2 * D * 2 + D * 2 + D * 2;
-  // one layer's weights staged in LDS (rows padded by 16 bytes against bank
-  // conflicts) when they are small: w_qkv, w_o, w_gate, w_up [.., D] and
-  // w_down [D, D]
-  static constexpr bool WL = D <= 64;
+  // bf16 row strides of QK and Y padded by 16 bytes: the 16 rows one
+  // fragment access touches then start in distinct banks
+  static constexpr int LQK = 2 * D + 8, LY = D + 8;
+  static constexpr size_t bytes_per_row = static_cast<size_t>(XS) * 4 + LQK * 2 + D * 2 + LY * 2;
+  static constexpr bool WL = D <= 64;  // weights staged in LDS
   static constexpr int LDW = D + 8;
+  static constexpr int QCH = 3 * D * (D / 8);  // 16-byte chunks of w_qkv
+  static constexpr int PCH = 4 * D * (D / 8);  // 16-byte chunks of the post weights
+  static constexpr int QPT = (QCH + NT - 1) / NT, PPT = (PCH + NT - 1) / NT;
   static constexpr size_t w_elems = static_cast<size_t>(7) * D * LDW;
   static constexpr size_t lds_bytes(int RT) {
     return bytes_per_row * RT + (WL ? w_elems * 2 : 0);
   }
 };
 
+// chunk e of a weight set -> (source pointer, LDS row) ; set 0 = w_qkv,
+// set 1 = w_o, w_gate, w_up, w_down stacked
+template <int D>
+__device__ __forceinline__ const bf16_t* wsrc(const LayerSet& w, int l, int set, int e, int* row_out) {
+  const int row = e / (D / 8), c8 = e % (D / 8);
+  *row_out = row;
+  if (set == 0) return w.p[l][0] + static_cast<int64_t>(row) * D + 8 * c8;
+  const int m = 1 + row / D;
+  return w.p[l][m] + static_cast<int64_t>(row % D) * D + 8 * c8;
+}
+
 template <int ELL, int D>
-__global__ __launch_bounds__(256) void xor_fwd_resident(
+__global__ __launch_bounds__(512) void xor_fwd_resident(
     const bf16_t* __restrict__ links_ctx, const bf16_t* __restrict__ hist,
     const int64_t* __restrict__ off, int64_t total_N, int RT, int layers, LayerSet w, float scale, int phi,
     bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out) {
-  constexpr int H = D / 32, KB = D / 32, XS = ResCfg<ELL, D>::XS;
+  using C = ResCfg<ELL, D>;
+  constexpr int H = D / 32, KB = D / 32, XS = C::XS, NW = C::NW, NT = C::NT;
+  constexpr bool WL = C::WL;
+  constexpr int LDW = C::LDW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* Xs = reinterpret_cast<float*>(smem);
+  constexpr int LQK = C::LQK, LY = C::LY;
   bf16_t* QKs = reinterpret_cast<bf16_t*>(smem + static_cast<size_t>(RT) * XS * 4);
-  bf16_t* Vps = QKs + static_cast<size_t>(RT) * 2 * D;
+  bf16_t* Vps = QKs + static_cast<size_t>(RT) * LQK;
   bf16_t* Ys = Vps + static_cast<size_t>(RT) * D;
-  constexpr bool WL = ResCfg<ELL, D>::WL;
-  constexpr int LDW = ResCfg<ELL, D>::LDW;
-  bf16_t* Wl = Ys + static_cast<size_t>(RT) * D;  // [7D][LDW]: qkv, o, gate, up, down
+  bf16_t* Wq = Ys + static_cast<size_t>(RT) * LY;  // [3D][LDW]
+  bf16_t* Wp = Wq + 3 * D * LDW;                  // [4D][LDW]
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
@@ -703,8 +742,41 @@ __global__ __launch_bounds__(256) void xor_fwd_resident(
   const bool softmax = (phi == PHI_SOFTMAX);
   const int nchunks = RT / 32;
 
+  // weight prefetch registers: set 0 (w_qkv) and set 1 (post weights)
+  bf16x8 pq[C::QPT], pp[C::PPT];
+  auto load_set = [&](int l, int set) {
+    if constexpr (WL) {
+      const int cnt = set == 0 ? C::QCH : C::PCH;
+#pragma unroll
+      for (int i = 0; i < (set == 0 ? C::QPT : C::PPT); ++i) {
+        const int e = tid + i * NT;
+        int row;
+        if (e < cnt) {
+          const bf16x8 v = ld16(wsrc<D>(w, l, set, e, &row));
+          if (set == 0) pq[i] = v; else pp[i] = v;
+        }
+      }
+    }
+  };
+  auto store_set = [&](int set) {
+    if constexpr (WL) {
+      const int cnt = set == 0 ? C::QCH : C::PCH;
+      bf16_t* dst = set == 0 ? Wq : Wp;
+#pragma unroll
+      for (int i = 0; i < (set == 0 ? C::QPT : C::PPT); ++i) {
+        const int e = tid + i * NT;
+        if (e < cnt) {
+          const int row = e / (D / 8), c8 = e % (D / 8);
+          *reinterpret_cast<bf16x8*>(dst + row * LDW + 8 * c8) = set == 0 ? pq[i] : pp[i];
+        }
+      }
+    }
+  };
+
+  load_set(0, 0);
+  load_set(0, 1);
   // residual stream <- [L^C_b ; E_b], zero padding
-  for (int e = tid; e < RT * (D / 8); e += 256) {
+  for (int e = tid; e < RT * (D / 8); e += NT) {
     const int row = e / (D / 8), c8 = e % (D / 8);
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const bf16_t* src = nullptr;
@@ -718,32 +790,19 @@ __global__ __launch_bounds__(256) void xor_fwd_resident(
 #pragma unroll
     for (int q = 0; q < 8; ++q) Xs[row * XS + 8 * c8 + q] = v[q];
   }
+  store_set(0);
+  store_set(1);
   __syncthreads();
 
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
     const bool full = !last || hist_out != nullptr;
-    const bf16_t* lw[5];
-    int ldd = D;
-    if constexpr (WL) {
-      // stage this layer's weights: rows [0,3D) qkv, [3D,4D) o, [4D,5D) gate,
-      // [5D,6D) up, [6D,7D) down
-      for (int e = tid; e < 7 * D * (D / 8); e += 256) {
-        const int row = e / (D / 8), c8 = e % (D / 8);
-        const int m = row < 3 * D ? 0 : 1 + (row - 3 * D) / D;
-        const int rr = m == 0 ? row : (row - 3 * D) % D;
-        *reinterpret_cast<bf16x8*>(Wl + row * LDW + 8 * c8) = ld16(w.p[l][m] + rr * D + 8 * c8);
-      }
-      __syncthreads();
-      lw[0] = Wl;
-      for (int m = 1; m < 5; ++m) lw[m] = Wl + (3 + (m - 1)) * D * LDW;
-      ldd = LDW;
-    } else {
-      for (int m = 0; m < 5; ++m) lw[m] = w.p[l][m];
-    }
-    // ---- LN + QKV for every chunk of 32 rows
-    for (int ch = wv; ch < nchunks; ch += 4) {
-      const int row0 = ch * 32;
+    const bf16_t* lq = WL ? Wq : w.p[l][0];
+    const int ldd = WL ? LDW : D;
+    // ---- LN + QKV: items (chunk, part)
+    if (!last) load_set(l + 1, 0);
+    for (int it = wv; it < 2 * nchunks; it += NW) {
+      const int row0 = (it >> 1) * 32;
       bf16x8 hb[2][KB];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -757,22 +816,24 @@ __global__ __launch_bounds__(256) void xor_fwd_resident(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
       }
-      qkv_chunk<D>(hb, lw[0] + opaque_zero(), ldd, QKs, Vps, row0, r, g);
+      if (it & 1) v_part<D>(hb, lq + opaque_zero(), ldd, Vps, row0, r, g);
+      else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, LQK);
     }
     __syncthreads();
     // ---- attention: items = per head, the L-branch and the E-branch chunks
+    if (!last) store_set(0);  // w_qkv region is free: next layer's projection
     const int echunks = full ? (n + 31) / 32 : 0;
     const int items = H * (1 + echunks);
-    for (int it = wv; it < items; it += 4) {
+    for (int it = wv; it < items; it += NW) {
       const int h = it % H, k = it / H;
       HeadOps<ELL> o;
-      load_head_ops<ELL, D>(o, QKs, Vps, 0, h, r, g);
+      load_head_ops<ELL, D>(o, QKs, Vps, 0, h, r, g, LQK);
       if (k == 0) {
         LState<ELL> st;
         st.init();
         for (int c0 = 0; c0 < n; c0 += 32) {
           ChunkOps ci;
-          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g);
+          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, LQK);
           l_branch<ELL>(st, o, ci, c0, 0, n, scale, softmax, r, g);
         }
         // normalise and write the link rows of Y
@@ -786,56 +847,55 @@ __global__ __launch_bounds__(256) void xor_fwd_resident(
             const int link = 16 * nb + 4 * g + jj;
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2)
-              Ys[link * D + h * 32 + 16 * c2 + r] = f32_to_bf16(st.acc[nb][c2][jj] * inv);
+              Ys[link * LY + h * 32 + 16 * c2 + r] = f32_to_bf16(st.acc[nb][c2][jj] * inv);
           }
         }
       } else {
         ChunkOps ci;
-        load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g);
-        e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g);
+        load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g, LQK);
+        e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY);
       }
     }
     __syncthreads();
-    // ---- post-attention block per group of 16*RBR rows
-    constexpr int RBR = D >= 128 ? 1 : 2;
-    constexpr int PR = 16 * RBR;
+    // ---- post-attention block per 16-row block
+    if (!last) load_set(l + 1, 1);
+    const bf16_t* lo_w = WL ? Wp : w.p[l][1];
+    const bf16_t* lg_w = WL ? Wp + D * LDW : w.p[l][2];
+    const bf16_t* lu_w = WL ? Wp + 2 * D * LDW : w.p[l][3];
+    const bf16_t* ld_w = WL ? Wp + 3 * D * LDW : w.p[l][4];
     const int prow_end = full ? rows : ELL;
-    const int pchunks = (prow_end + PR - 1) / PR;
-    for (int ch = wv; ch < pchunks; ch += 4) {
-      const int row0 = ch * PR;
-      bf16x8 yb[RBR][KB];
-      float x1[RBR][D / 4];
+    const int pblocks = (prow_end + 15) / 16;
+    for (int it = wv; it < pblocks; it += NW) {
+      const int row = it * 16 + r;
+      bf16x8 yb[1][KB];
+      float x1[1][D / 4];
 #pragma unroll
-      for (int rb = 0; rb < RBR; ++rb) {
-        const int row = row0 + 16 * rb + r;
+      for (int kb = 0; kb < KB; ++kb) {
+        yb[0][kb] = row < rows ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          yb[rb][kb] = row < rows ? ld16(Ys + row * D + kb * 32 + 8 * g) : zero8();
-#pragma unroll
-          for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
-        }
+        for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
       }
       const int z = opaque_zero();
-      post_rows<D, D, RBR>(yb, x1, lw[1] + z, lw[2] + z, lw[3] + z, lw[4] + z, ldd, ldd, r, g);
+      post_rows<D, D, 1>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
+      const bool real = row < rows;
+      if (!last) {
 #pragma unroll
-      for (int rb = 0; rb < RBR; ++rb) {
-        const int row = row0 + 16 * rb + r;
-        const bool real = row < rows;
-        if (!last) {
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
+          for (int q = 0; q < 8; ++q) Xs[row * XS + kb * 32 + 8 * g + q] = real ? x1[0][8 * kb + q] : 0.f;
+      } else if (real) {
+        bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
+                                : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
+        if (dst)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) Xs[row * XS + kb * 32 + 8 * g + q] = real ? x1[rb][8 * kb + q] : 0.f;
-        } else if (real) {
-          bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
-                                  : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
-          if (dst)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[rb][8 * kb]);
-        }
+          for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[0][8 * kb]);
       }
     }
     __syncthreads();
+    if (!last) {
+      store_set(1);  // post-weight region is free: next layer's post weights
+      // visible before the next post phase: two barriers follow
+    }
   }
 }
 

@@ -128,6 +128,16 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale,
                            const lime_layer_weights_t* w, void* links_pers, void* hist_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Launch plan lime_xor_fwd would use for these sizes (host only, no GPU
+ * work): returns the number of kernel launches of one call (0 on invalid
+ * sizes) and, if buf is not NULL, writes a one-line description (path name,
+ * splits, rows per split) of at most buf_len bytes including the NUL.
+ * with_hist says whether hist_out will be passed.  An introspection aid for
+ * profiling and tuning; lime_xor_fwd does not need it.                     */
+int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
+                          int32_t layers, int32_t d_ff, int64_t total_N, int32_t max_N,
+                          int32_t with_hist, char* buf, size_t buf_len);
+
 /* Offline QK cache over items [n_items, d] and per-head link keys
  * link_keys [heads, ell, d] (the global links with the candidate-side
  * query/key projections folded in; heads = 1 and link_keys = L is the
