@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "xor_fwd_plan", "qk_cache_build",
-    "cand_score", "PHI", "DTYPE", "EXPORTED",
+    "qk_cache_build_i8", "cand_score", "cand_score_i8", "cand_score_uncached", "PHI", "DTYPE", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,8 @@ STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
 
 # every symbol include/lime.h declares
 EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_workspace_size", "lime_xor_fwd_plan",
-            "lime_qk_cache_build", "lime_cand_score", "lime_status_string", "lime_last_error")
+            "lime_qk_cache_build", "lime_qk_cache_build_i8", "lime_cand_score", "lime_cand_score_i8",
+            "lime_cand_score_uncached", "lime_status_string", "lime_last_error")
 
 
 class LayerWeights(ctypes.Structure):
@@ -67,6 +68,15 @@ lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32,
 lib.lime_qk_cache_build.restype = ctypes.c_int
 lib.lime_qk_cache_build.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i64, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]
+lib.lime_qk_cache_build_i8.restype = ctypes.c_int
+lib.lime_qk_cache_build_i8.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i64, _i32, _i32, _i32,
+                                       _vp, _vp, _vp, _vp, _vp]
+lib.lime_cand_score_i8.restype = ctypes.c_int
+lib.lime_cand_score_i8.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _vp, _vp,
+                                   _i64, _vp, _vp, _vp]
+lib.lime_cand_score_uncached.restype = ctypes.c_int
+lib.lime_cand_score_uncached.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32, _i32, _vp, _i64,
+                                         _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]
 lib.lime_cand_score.restype = ctypes.c_int
 lib.lime_cand_score.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp,
                                 _i64, _vp, _vp, _vp]
@@ -207,4 +217,76 @@ def cand_score(cache, links_pers, cand_ids, cand_offsets, out=None, bad_id_count
     _check(lib.lime_cand_score(_dtype(cache), B, ell, d, H, _ptr(cache), n_items, _ptr(links_pers),
                                _ptr(cand_ids), _ptr(cand_offsets), M, _ptr(out),
                                _ptr(bad_id_count), _stream(stream)), "lime_cand_score")
+    return out
+
+
+def qk_cache_build_i8(items, link_keys, phi: str = "silu_mean", scale: float | None = None,
+                      codes=None, qscale=None, stream=None):
+    """Int8 QK cache: (codes [n_items, heads, ell] int8, qscale [n_items,
+    heads] float32)."""
+    _want(items, "items", dims=2)
+    _want(link_keys, "link_keys", items.dtype, 3)
+    n, d = items.shape
+    H, ell, d2 = link_keys.shape
+    if d2 != d:
+        raise ValueError("items and link_keys disagree on d")
+    if scale is None:
+        scale = (d // H) ** -0.5 if d % H == 0 else d ** -0.5
+    if codes is None:
+        codes = torch.empty((n, H, ell), dtype=torch.int8, device=items.device)
+    if qscale is None:
+        qscale = torch.empty((n, H), dtype=torch.float32, device=items.device)
+    _check(lib.lime_qk_cache_build_i8(_dtype(items), PHI[phi], scale, n, d, H, ell, _ptr(items),
+                                      _ptr(link_keys), _ptr(codes), _ptr(qscale), _stream(stream)),
+           "lime_qk_cache_build_i8")
+    return codes, qscale
+
+
+def cand_score_i8(codes, qscale, links_pers, cand_ids, cand_offsets, out=None, bad_id_count=None,
+                  stream=None):
+    """Scores [total_M, d] from the int8 cache."""
+    _want(codes, "codes", torch.int8, 3)
+    _want(qscale, "qscale", torch.float32, 2)
+    _want(links_pers, "links_pers", dims=3)
+    _want(cand_ids, "cand_ids", torch.int64, 1)
+    _want(cand_offsets, "cand_offsets", torch.int64, 1)
+    n_items, H, ell = codes.shape
+    B, ell2, d = links_pers.shape
+    if ell2 != ell or cand_offsets.shape[0] != B + 1 or tuple(qscale.shape) != (n_items, H):
+        raise ValueError("shape mismatch between codes, qscale, links_pers and cand_offsets")
+    M = cand_ids.shape[0]
+    if out is None:
+        out = torch.empty((M, d), dtype=links_pers.dtype, device=links_pers.device)
+    if bad_id_count is not None:
+        _want(bad_id_count, "bad_id_count", torch.int32)
+    _check(lib.lime_cand_score_i8(_dtype(links_pers), B, ell, d, H, _ptr(codes), _ptr(qscale), n_items,
+                                  _ptr(links_pers), _ptr(cand_ids), _ptr(cand_offsets), M, _ptr(out),
+                                  _ptr(bad_id_count), _stream(stream)), "lime_cand_score_i8")
+    return out
+
+
+def cand_score_uncached(items, link_keys, links_pers, cand_ids, cand_offsets, phi: str = "silu_mean",
+                        scale: float | None = None, out=None, bad_id_count=None, stream=None):
+    """Scores [total_M, d] computed from the item rows without a cache."""
+    _want(items, "items", dims=2)
+    _want(link_keys, "link_keys", items.dtype, 3)
+    _want(links_pers, "links_pers", items.dtype, 3)
+    _want(cand_ids, "cand_ids", torch.int64, 1)
+    _want(cand_offsets, "cand_offsets", torch.int64, 1)
+    n_items, d = items.shape
+    H, ell, d2 = link_keys.shape
+    B, ell2, d3 = links_pers.shape
+    if d2 != d or d3 != d or ell2 != ell or cand_offsets.shape[0] != B + 1:
+        raise ValueError("shape mismatch between items, link_keys, links_pers and cand_offsets")
+    if scale is None:
+        scale = (d // H) ** -0.5
+    M = cand_ids.shape[0]
+    if out is None:
+        out = torch.empty((M, d), dtype=items.dtype, device=items.device)
+    if bad_id_count is not None:
+        _want(bad_id_count, "bad_id_count", torch.int32)
+    _check(lib.lime_cand_score_uncached(_dtype(items), PHI[phi], scale, B, ell, d, H, _ptr(items), n_items,
+                                        _ptr(link_keys), _ptr(links_pers), _ptr(cand_ids), _ptr(cand_offsets),
+                                        M, _ptr(out), _ptr(bad_id_count), _stream(stream)),
+           "lime_cand_score_uncached")
     return out

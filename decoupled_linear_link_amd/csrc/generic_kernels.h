@@ -276,13 +276,14 @@ __global__ void xor_combine(const float* __restrict__ part, T* __restrict__ Y, i
 }
 
 // ---------------------------------------------------------------------------
-// QK cache: one thread per (item, head); logits staged in LDS.
+// QK cache: one thread per (item, head); logits staged in LDS.  With I8 the
+// row is stored as symmetric int8 codes plus a float32 scale.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool I8 = false>
 __global__ __launch_bounds__(64) void qk_cache(const T* __restrict__ items,
-                                               const T* __restrict__ keys, T* __restrict__ cache,
-                                               int64_t n_items, int d, int H, int ell,
-                                               float scale, int phi) {
+                                               const T* __restrict__ keys, void* __restrict__ cache_out,
+                                               float* __restrict__ qscale, int64_t n_items, int d,
+                                               int H, int ell, float scale, int phi) {
   extern __shared__ float sbuf[];  // [64][ell]
   const int h = blockIdx.y;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
@@ -298,7 +299,6 @@ __global__ __launch_bounds__(64) void qk_cache(const T* __restrict__ items,
     s[k] = a;
     mx = fmaxf(mx, a);
   }
-  T* out = cache + (m * H + h) * ell;
   if (phi == PHI_SOFTMAX) {
     float z = 0.f;
     for (int k = 0; k < ell; ++k) {
@@ -306,18 +306,31 @@ __global__ __launch_bounds__(64) void qk_cache(const T* __restrict__ items,
       z += s[k];
     }
     const float inv = 1.f / z;
-    for (int k = 0; k < ell; ++k) Elt<T>::st(out + k, s[k] * inv);
+    for (int k = 0; k < ell; ++k) s[k] *= inv;
   } else {
     const float inv = 1.f / ell;
-    for (int k = 0; k < ell; ++k) Elt<T>::st(out + k, silu_f(s[k]) * inv);
+    for (int k = 0; k < ell; ++k) s[k] = silu_f(s[k]) * inv;
+  }
+  if constexpr (I8) {
+    float am = 0.f;
+    for (int k = 0; k < ell; ++k) am = fmaxf(am, fabsf(s[k]));
+    const float inv = am > 0.f ? 127.f / am : 0.f;
+    int8_t* out = static_cast<int8_t*>(cache_out) + (m * H + h) * ell;
+    for (int k = 0; k < ell; ++k)
+      out[k] = static_cast<int8_t>(fminf(fmaxf(__builtin_rintf(s[k] * inv), -127.f), 127.f));
+    qscale[m * H + h] = am / 127.f;
+  } else {
+    T* out = static_cast<T*>(cache_out) + (m * H + h) * ell;
+    for (int k = 0; k < ell; ++k) Elt<T>::st(out + k, s[k]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Candidate scoring: one thread per output element (candidate i, column c).
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void cand_score(const T* __restrict__ cache, int64_t n_items,
+template <typename T, bool I8 = false>
+__global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache_in,
+                                                  const float* __restrict__ qscale, int64_t n_items,
                                                   const T* __restrict__ lp,
                                                   const int64_t* __restrict__ ids,
                                                   const int64_t* __restrict__ off, int B,
@@ -335,11 +348,67 @@ __global__ __launch_bounds__(256) void cand_score(const T* __restrict__ cache, i
   if (id < 0 || id >= n_items) {
     if (c == 0 && bad != nullptr) atomicAdd(bad, 1);
   } else {
-    const T* w = cache + (id * H + h) * ell;
     const T* l = lp + static_cast<int64_t>(b) * ell * d + c;
-    for (int k = 0; k < ell; ++k) v += Elt<T>::ld(w + k) * Elt<T>::ld(l + static_cast<int64_t>(k) * d);
+    if constexpr (I8) {
+      const int8_t* w = static_cast<const int8_t*>(cache_in) + (id * H + h) * ell;
+      for (int k = 0; k < ell; ++k) v += static_cast<float>(w[k]) * Elt<T>::ld(l + static_cast<int64_t>(k) * d);
+      v *= qscale[id * H + h];
+    } else {
+      const T* w = static_cast<const T*>(cache_in) + (id * H + h) * ell;
+      for (int k = 0; k < ell; ++k) v += Elt<T>::ld(w + k) * Elt<T>::ld(l + static_cast<int64_t>(k) * d);
+    }
   }
   Elt<T>::st(out + gid, v);
+}
+
+// ---------------------------------------------------------------------------
+// Uncached scoring: one thread per (candidate, head); the candidate's
+// weights for the head are computed into LDS, then the weighted sum.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void cand_score_uncached(
+    const T* __restrict__ items, int64_t n_items, const T* __restrict__ keys, const T* __restrict__ lp,
+    const int64_t* __restrict__ ids, const int64_t* __restrict__ off, int B, int ell, int d, int H,
+    int64_t total_M, T* __restrict__ out, int* bad, float scale, int phi) {
+  extern __shared__ float sbuf[];  // [64][ell]
+  const int h = blockIdx.y;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x;
+  if (i >= total_M) return;
+  float* s = sbuf + threadIdx.x * ell;
+  const int dh = d / H;
+  const int64_t id = ids[i];
+  T* o = out + i * d + h * dh;
+  if (id < 0 || id >= n_items) {
+    if (h == 0 && bad != nullptr) atomicAdd(bad, 1);
+    for (int c = 0; c < dh; ++c) Elt<T>::st(o + c, 0.f);
+    return;
+  }
+  const int b = find_owner(off, B, i);
+  const T* t = items + id * d;
+  const T* kh = keys + static_cast<int64_t>(h) * ell * d;
+  float mx = -INFINITY;
+  for (int k = 0; k < ell; ++k) {
+    float a = 0.f;
+    for (int c = 0; c < d; ++c) a += Elt<T>::ld(t + c) * Elt<T>::ld(kh + static_cast<int64_t>(k) * d + c);
+    s[k] = a * scale;
+    mx = fmaxf(mx, s[k]);
+  }
+  if (phi == PHI_SOFTMAX) {
+    float z = 0.f;
+    for (int k = 0; k < ell; ++k) {
+      s[k] = __expf(s[k] - mx);
+      z += s[k];
+    }
+    for (int k = 0; k < ell; ++k) s[k] /= z;
+  } else {
+    for (int k = 0; k < ell; ++k) s[k] = silu_f(s[k]) / ell;
+  }
+  const T* l = lp + static_cast<int64_t>(b) * ell * d + h * dh;
+  for (int c = 0; c < dh; ++c) {
+    float v = 0.f;
+    for (int k = 0; k < ell; ++k) v += s[k] * Elt<T>::ld(l + static_cast<int64_t>(k) * d + c);
+    Elt<T>::st(o + c, v);
+  }
 }
 
 }  // namespace gen

@@ -74,27 +74,28 @@ int blocks_per_cu(K kernel, int threads) {
 // ---------------------------------------------------------------------------
 // QK cache: matrix-core kernel for the shapes it is instantiated for
 // ---------------------------------------------------------------------------
-template <int ELL, int D, int H>
-lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, int64_t n_items,
-                             float scale, int phi, hipStream_t st) {
+template <int ELL, int D, int H, bool I8>
+lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, float* qscale,
+                             int64_t n_items, float scale, int phi, hipStream_t st) {
   using C = mfma::QkCfg<ELL, D, H>;
-  auto k = mfma::qk_cache<ELL, D, H>;
+  auto k = mfma::qk_cache<ELL, D, H, I8>;
   static const int per_cu = blocks_per_cu(k, C::NT);
   const int64_t ntiles = (n_items + C::TI - 1) / C::TI;
   int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
   if (grid > ntiles) grid = ntiles;
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, st,
-                     static_cast<const bf16_t*>(items), static_cast<const bf16_t*>(keys),
-                     static_cast<bf16_t*>(cache), n_items, scale, phi, ntiles);
+                     static_cast<const bf16_t*>(items), static_cast<const bf16_t*>(keys), cache, qscale,
+                     n_items, scale, phi, ntiles);
   LIME_CHECK_LAUNCH("qk cache build (mfma)");
   return ok();
 }
 
 // returns LIME_ERR_UNSUPPORTED (without launching) if no instantiation fits
+template <bool I8>
 lime_status_t try_qk_mfma(int ell, int d, int H, const void* items, const void* keys, void* cache,
-                          int64_t n_items, float scale, int phi, hipStream_t st) {
+                          float* qscale, int64_t n_items, float scale, int phi, hipStream_t st) {
 #define LIME_QK(E, DD, HH) \
-  if (ell == E && d == DD && H == HH) return launch_qk_mfma<E, DD, HH>(items, keys, cache, n_items, scale, phi, st);
+  if (ell == E && d == DD && H == HH) return launch_qk_mfma<E, DD, HH, I8>(items, keys, cache, qscale, n_items, scale, phi, st);
   LIME_QK(32, 64, 2)
   LIME_QK(32, 128, 4)
   LIME_QK(64, 128, 4)
@@ -107,29 +108,31 @@ lime_status_t try_qk_mfma(int ell, int d, int H, const void* items, const void* 
 // ---------------------------------------------------------------------------
 // candidate scoring: matrix-core kernel for d_h = 32, ell in {32, 64}
 // ---------------------------------------------------------------------------
-template <int ELL, int H>
-lime_status_t launch_cs_mfma(const void* cache, int64_t n_items, const void* lp,
+template <int ELL, int H, bool I8>
+lime_status_t launch_cs_mfma(const void* cache, const float* qscale, int64_t n_items, const void* lp,
                              const int64_t* ids, const int64_t* off, int B, int64_t total_M,
                              void* out, int* bad, hipStream_t st) {
+  constexpr int NG = H < 4 ? 1 : H / 4;  // head groups per candidate tile (one wave each)
   const int64_t ntiles = (total_M + 15) / 16;
-  const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16;
+  const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16 / NG;
   int64_t tpw = (ntiles + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
-  const int64_t waves = (ntiles + tpw - 1) / tpw;
+  const int64_t waves = (ntiles + tpw - 1) / tpw * NG;
   const int64_t grid = (waves + 3) / 4;
-  hipLaunchKernelGGL((mfma::cand_score<ELL, H>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(cache), n_items, static_cast<const bf16_t*>(lp), ids,
-                     off, B, total_M, static_cast<bf16_t*>(out), bad, tpw);
+  hipLaunchKernelGGL((mfma::cand_score<ELL, H, I8>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     cache, qscale, n_items, static_cast<const bf16_t*>(lp), ids, off, B, total_M,
+                     static_cast<bf16_t*>(out), bad, tpw);
   LIME_CHECK_LAUNCH("candidate scoring (mfma)");
   return ok();
 }
 
-lime_status_t try_cs_mfma(int ell, int d, int H, const void* cache, int64_t n_items, const void* lp,
-                          const int64_t* ids, const int64_t* off, int B, int64_t total_M, void* out,
-                          int* bad, hipStream_t st) {
+template <bool I8>
+lime_status_t try_cs_mfma(int ell, int d, int H, const void* cache, const float* qscale, int64_t n_items,
+                          const void* lp, const int64_t* ids, const int64_t* off, int B, int64_t total_M,
+                          void* out, int* bad, hipStream_t st) {
   if (d != 32 * H) return LIME_ERR_UNSUPPORTED;
 #define LIME_CS(E, HH) \
-  if (ell == E && H == HH) return launch_cs_mfma<E, HH>(cache, n_items, lp, ids, off, B, total_M, out, bad, st);
+  if (ell == E && H == HH) return launch_cs_mfma<E, HH, I8>(cache, qscale, n_items, lp, ids, off, B, total_M, out, bad, st);
   LIME_CS(32, 1) LIME_CS(32, 2) LIME_CS(32, 4) LIME_CS(32, 8)
   LIME_CS(64, 1) LIME_CS(64, 2) LIME_CS(64, 4) LIME_CS(64, 8)
 #undef LIME_CS
@@ -532,10 +535,10 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
                                       hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
 }
 
-lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scale,
-                                  int64_t n_items, int32_t d, int32_t heads, int32_t ell,
-                                  const void* items, const void* link_keys, void* cache,
-                                  void* stream) {
+static lime_status_t qk_cache_impl(bool i8, lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                   int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                   const void* items, const void* link_keys, void* cache,
+                                   float* qscale, void* stream) {
   if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
   if (phi != LIME_PHI_SOFTMAX && phi != LIME_PHI_SILU_MEAN) return fail(LIME_ERR_INVALID_ARG, "bad phi %d", (int)phi);
   if (!std::isfinite(scale)) return fail(LIME_ERR_INVALID_ARG, "scale must be finite");
@@ -545,34 +548,41 @@ lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scal
   if (heads > 65535) return fail(LIME_ERR_UNSUPPORTED, "too many heads");
   if (!link_keys) return fail(LIME_ERR_INVALID_ARG, "link_keys is null");
   if (n_items > 0 && (!items || !cache)) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (i8 && n_items > 0 && !qscale) return fail(LIME_ERR_INVALID_ARG, "qscale is null");
   if (!aligned16(items) || !aligned16(link_keys) || !aligned16(cache))
     return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (i8 && (reinterpret_cast<uintptr_t>(qscale) & 3u) != 0)
+    return fail(LIME_ERR_INVALID_ARG, "qscale must be 4-byte aligned");
   if (n_items == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == LIME_BF16) {
-    const lime_status_t r = try_qk_mfma(ell, d, heads, items, link_keys, cache, n_items, scale,
-                                        static_cast<int>(phi), s);
+    const lime_status_t r = i8 ? try_qk_mfma<true>(ell, d, heads, items, link_keys, cache, qscale, n_items, scale,
+                                                   static_cast<int>(phi), s)
+                               : try_qk_mfma<false>(ell, d, heads, items, link_keys, cache, qscale, n_items, scale,
+                                                    static_cast<int>(phi), s);
     if (r != LIME_ERR_UNSUPPORTED) return r;
   }
   const dim3 grid(static_cast<unsigned>((n_items + 63) / 64), heads);
   const size_t lds = 64 * static_cast<size_t>(ell) * 4;
-  if (dtype == LIME_F32)
-    hipLaunchKernelGGL(gen::qk_cache<float>, grid, dim3(64), lds, s, static_cast<const float*>(items),
-                       static_cast<const float*>(link_keys), static_cast<float*>(cache), n_items, d,
-                       heads, ell, scale, static_cast<int>(phi));
-  else
-    hipLaunchKernelGGL(gen::qk_cache<bf16_t>, grid, dim3(64), lds, s, static_cast<const bf16_t*>(items),
-                       static_cast<const bf16_t*>(link_keys), static_cast<bf16_t*>(cache), n_items,
-                       d, heads, ell, scale, static_cast<int>(phi));
+#define LIME_QKG(T, I) \
+  hipLaunchKernelGGL((gen::qk_cache<T, I>), grid, dim3(64), lds, s, static_cast<const T*>(items), \
+                     static_cast<const T*>(link_keys), cache, qscale, n_items, d, heads, ell, scale, \
+                     static_cast<int>(phi))
+  if (dtype == LIME_F32) {
+    if (i8) LIME_QKG(float, true); else LIME_QKG(float, false);
+  } else {
+    if (i8) LIME_QKG(bf16_t, true); else LIME_QKG(bf16_t, false);
+  }
+#undef LIME_QKG
   LIME_CHECK_LAUNCH("qk cache build");
   return ok();
 }
 
-lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
-                              int32_t heads, const void* cache, int64_t n_items,
-                              const void* links_pers, const int64_t* cand_ids,
-                              const int64_t* cand_offsets, int64_t total_M, void* out,
-                              int32_t* bad_id_count, void* stream) {
+static lime_status_t cand_score_impl(bool i8, lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                     int32_t heads, const void* cache, const float* qscale,
+                                     int64_t n_items, const void* links_pers, const int64_t* cand_ids,
+                                     const int64_t* cand_offsets, int64_t total_M, void* out,
+                                     int32_t* bad_id_count, void* stream) {
   if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
   if (B < 1 || ell < 1 || d < 1 || heads < 1 || n_items < 0 || total_M < 0)
     return fail(LIME_ERR_INVALID_ARG, "sizes must be positive");
@@ -582,29 +592,129 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
   if (!links_pers || !cand_offsets) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
   if (total_M > 0 && (!cand_ids || !out)) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
   if (n_items > 0 && !cache) return fail(LIME_ERR_INVALID_ARG, "cache is null");
+  if (i8 && n_items > 0 && !qscale) return fail(LIME_ERR_INVALID_ARG, "qscale is null");
   if (!aligned16(cache) || !aligned16(links_pers) || !aligned16(cand_ids) ||
+      !aligned16(cand_offsets) || !aligned16(out))
+    return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(bad_id_count) & 3u) != 0 || (reinterpret_cast<uintptr_t>(qscale) & 3u) != 0)
+    return fail(LIME_ERR_INVALID_ARG, "bad_id_count and qscale must be 4-byte aligned");
+  if (total_M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == LIME_BF16) {
+    const lime_status_t r =
+        i8 ? try_cs_mfma<true>(ell, d, heads, cache, qscale, n_items, links_pers, cand_ids, cand_offsets, B,
+                               total_M, out, bad_id_count, s)
+           : try_cs_mfma<false>(ell, d, heads, cache, qscale, n_items, links_pers, cand_ids, cand_offsets, B,
+                                total_M, out, bad_id_count, s);
+    if (r != LIME_ERR_UNSUPPORTED) return r;
+  }
+  const int64_t n = total_M * d;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+#define LIME_CSG(T, I) \
+  hipLaunchKernelGGL((gen::cand_score<T, I>), grid, dim3(256), 0, s, cache, qscale, n_items, \
+                     static_cast<const T*>(links_pers), cand_ids, cand_offsets, B, ell, d, heads, total_M, \
+                     static_cast<T*>(out), bad_id_count)
+  if (dtype == LIME_F32) {
+    if (i8) LIME_CSG(float, true); else LIME_CSG(float, false);
+  } else {
+    if (i8) LIME_CSG(bf16_t, true); else LIME_CSG(bf16_t, false);
+  }
+#undef LIME_CSG
+  LIME_CHECK_LAUNCH("candidate scoring");
+  return ok();
+}
+
+lime_status_t lime_qk_cache_build(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                  int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                  const void* items, const void* link_keys, void* cache,
+                                  void* stream) {
+  return qk_cache_impl(false, dtype, phi, scale, n_items, d, heads, ell, items, link_keys, cache, nullptr,
+                       stream);
+}
+
+lime_status_t lime_qk_cache_build_i8(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                     int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                     const void* items, const void* link_keys, int8_t* codes,
+                                     float* qscale, void* stream) {
+  return qk_cache_impl(true, dtype, phi, scale, n_items, d, heads, ell, items, link_keys, codes, qscale,
+                       stream);
+}
+
+lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                              int32_t heads, const void* cache, int64_t n_items,
+                              const void* links_pers, const int64_t* cand_ids,
+                              const int64_t* cand_offsets, int64_t total_M, void* out,
+                              int32_t* bad_id_count, void* stream) {
+  return cand_score_impl(false, dtype, B, ell, d, heads, cache, nullptr, n_items, links_pers, cand_ids,
+                         cand_offsets, total_M, out, bad_id_count, stream);
+}
+
+lime_status_t lime_cand_score_i8(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                 int32_t heads, const int8_t* codes, const float* qscale,
+                                 int64_t n_items, const void* links_pers, const int64_t* cand_ids,
+                                 const int64_t* cand_offsets, int64_t total_M, void* out,
+                                 int32_t* bad_id_count, void* stream) {
+  return cand_score_impl(true, dtype, B, ell, d, heads, codes, qscale, n_items, links_pers, cand_ids,
+                         cand_offsets, total_M, out, bad_id_count, stream);
+}
+
+lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                       int32_t ell, int32_t d, int32_t heads, const void* items,
+                                       int64_t n_items, const void* link_keys, const void* links_pers,
+                                       const int64_t* cand_ids, const int64_t* cand_offsets,
+                                       int64_t total_M, void* out, int32_t* bad_id_count, void* stream) {
+  if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
+  if (phi != LIME_PHI_SOFTMAX && phi != LIME_PHI_SILU_MEAN) return fail(LIME_ERR_INVALID_ARG, "bad phi %d", (int)phi);
+  if (!std::isfinite(scale)) return fail(LIME_ERR_INVALID_ARG, "scale must be finite");
+  if (B < 1 || ell < 1 || d < 1 || heads < 1 || n_items < 0 || total_M < 0)
+    return fail(LIME_ERR_INVALID_ARG, "sizes must be positive");
+  if (d % heads != 0) return fail(LIME_ERR_INVALID_ARG, "d (%d) must be a multiple of heads (%d)", d, heads);
+  if (ell > 256) return fail(LIME_ERR_UNSUPPORTED, "ell > 256 unsupported (got %d)", ell);
+  if (d % 8 != 0 || d > 1024) return fail(LIME_ERR_UNSUPPORTED, "d must be a multiple of 8 and <= 1024 (got %d)", d);
+  if (heads > 65535) return fail(LIME_ERR_UNSUPPORTED, "too many heads");
+  if (!link_keys || !links_pers || !cand_offsets) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (total_M > 0 && (!cand_ids || !out)) return fail(LIME_ERR_INVALID_ARG, "null pointer argument");
+  if (n_items > 0 && !items) return fail(LIME_ERR_INVALID_ARG, "items is null");
+  if (!aligned16(items) || !aligned16(link_keys) || !aligned16(links_pers) || !aligned16(cand_ids) ||
       !aligned16(cand_offsets) || !aligned16(out))
     return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(bad_id_count) & 3u) != 0)
     return fail(LIME_ERR_INVALID_ARG, "bad_id_count must be 4-byte aligned");
   if (total_M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == LIME_BF16) {
-    const lime_status_t r = try_cs_mfma(ell, d, heads, cache, n_items, links_pers, cand_ids,
-                                        cand_offsets, B, total_M, out, bad_id_count, s);
-    if (r != LIME_ERR_UNSUPPORTED) return r;
+  if (dtype == LIME_BF16 && d == 32 * heads) {
+    const int64_t ntiles = (total_M + 15) / 16;
+    const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16;
+    int64_t tpw = (ntiles + target_waves - 1) / target_waves;
+    if (tpw < 1) tpw = 1;
+    const int64_t waves = (ntiles + tpw - 1) / tpw;
+    const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
+#define LIME_UC(E, DD, HH)                                                                             \
+    if (ell == E && d == DD && heads == HH) {                                                          \
+      constexpr size_t lds = mfma::UcCfg<E, DD, HH>::lds_bytes;                                        \
+      hipLaunchKernelGGL((mfma::cand_score_uncached<E, DD, HH>), dim3(grid), dim3(256), lds, s,        \
+                         static_cast<const bf16_t*>(items), n_items, static_cast<const bf16_t*>(link_keys), \
+                         static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B, total_M,   \
+                         static_cast<bf16_t*>(out), bad_id_count, scale, static_cast<int>(phi), tpw);  \
+      LIME_CHECK_LAUNCH("uncached scoring (mfma)");                                                    \
+      return ok();                                                                                     \
+    }
+    LIME_UC(32, 64, 2) LIME_UC(32, 128, 4) LIME_UC(64, 128, 4) LIME_UC(32, 256, 8)
+#undef LIME_UC
   }
-  const int64_t n = total_M * d;
-  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  const dim3 grid(static_cast<unsigned>((total_M + 63) / 64), heads);
+  const size_t lds = 64 * static_cast<size_t>(ell) * 4;
   if (dtype == LIME_F32)
-    hipLaunchKernelGGL(gen::cand_score<float>, grid, dim3(256), 0, s, static_cast<const float*>(cache),
-                       n_items, static_cast<const float*>(links_pers), cand_ids, cand_offsets, B, ell,
-                       d, heads, total_M, static_cast<float*>(out), bad_id_count);
+    hipLaunchKernelGGL(gen::cand_score_uncached<float>, grid, dim3(64), lds, s, static_cast<const float*>(items),
+                       n_items, static_cast<const float*>(link_keys), static_cast<const float*>(links_pers),
+                       cand_ids, cand_offsets, B, ell, d, heads, total_M, static_cast<float*>(out), bad_id_count,
+                       scale, static_cast<int>(phi));
   else
-    hipLaunchKernelGGL(gen::cand_score<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(cache),
-                       n_items, static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B,
-                       ell, d, heads, total_M, static_cast<bf16_t*>(out), bad_id_count);
-  LIME_CHECK_LAUNCH("candidate scoring");
+    hipLaunchKernelGGL(gen::cand_score_uncached<bf16_t>, grid, dim3(64), lds, s, static_cast<const bf16_t*>(items),
+                       n_items, static_cast<const bf16_t*>(link_keys), static_cast<const bf16_t*>(links_pers),
+                       cand_ids, cand_offsets, B, ell, d, heads, total_M, static_cast<bf16_t*>(out), bad_id_count,
+                       scale, static_cast<int>(phi));
+  LIME_CHECK_LAUNCH("uncached scoring");
   return ok();
 }
 

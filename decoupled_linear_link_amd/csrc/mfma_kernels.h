@@ -19,6 +19,15 @@ namespace mfma {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// An opaque zero: offsetting an LDS operand pointer by it inside a loop keeps
+// the compiler from hoisting every loop-invariant fragment load out of the
+// loop (which would hold whole weight matrices in registers and spill).
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return z;
+}
+
 __device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -74,10 +83,29 @@ struct QkCfg {
   static_assert((TI * CPR) % NT == 0, "tile load split");
 };
 
-template <int ELL, int D, int H>
+// Symmetric int8 codes of the values a lane holds for one (item, head): the
+// other values of the row are in lanes ^16, ^32.  scale = max|v| / 127,
+// code = round-half-even(v * 127 / max|v|); an all-zero row gets scale 0.
+template <int N>
+__device__ __forceinline__ float quantize_i8(const float* v, int8_t* q) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float inv = m > 0.f ? 127.f / m : 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float c = __builtin_rintf(v[i] * inv);
+    q[i] = static_cast<int8_t>(fminf(fmaxf(c, -127.f), 127.f));
+  }
+  return m / 127.f;
+}
+
+template <int ELL, int D, int H, bool I8 = false>
 __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
-    const bf16_t* __restrict__ items, const bf16_t* __restrict__ keys, bf16_t* __restrict__ cache,
-    int64_t n_items, float scale, int phi, int64_t ntiles) {
+    const bf16_t* __restrict__ items, const bf16_t* __restrict__ keys, void* __restrict__ cache_out,
+    float* __restrict__ qscale, int64_t n_items, float scale, int phi, int64_t ntiles) {
   using C = QkCfg<ELL, D, H>;
   __shared__ __attribute__((aligned(16))) char lds[C::TI * C::STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -166,10 +194,28 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
 #pragma unroll
           for (int q = 0; q < 4 * C::MB; ++q) v[q] = silu_f(v[q]) * inv;
         }
-        if (item < n_items) {
-          bf16_t* o = cache + (item * H + head0 + hh) * ELL + g * 4 * C::MB;
+        if constexpr (I8) {
+          int8_t qv[4 * C::MB];
+          const float sc = quantize_i8<4 * C::MB>(v, qv);
+          if (item < n_items) {
+            int8_t* o = static_cast<int8_t*>(cache_out) + (item * H + head0 + hh) * ELL + g * 4 * C::MB;
 #pragma unroll
-          for (int q = 0; q < C::MB / 2; ++q) st8(o + 8 * q, v + 8 * q);
+            for (int q = 0; q < C::MB / 2; ++q) {
+              uint2 pk;
+              pk.x = (uint32_t)(uint8_t)qv[8 * q] | ((uint32_t)(uint8_t)qv[8 * q + 1] << 8) |
+                     ((uint32_t)(uint8_t)qv[8 * q + 2] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 3] << 24);
+              pk.y = (uint32_t)(uint8_t)qv[8 * q + 4] | ((uint32_t)(uint8_t)qv[8 * q + 5] << 8) |
+                     ((uint32_t)(uint8_t)qv[8 * q + 6] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 7] << 24);
+              *reinterpret_cast<uint2*>(o + 8 * q) = pk;
+            }
+            if (g == 0) qscale[item * H + head0 + hh] = sc;
+          }
+        } else {
+          if (item < n_items) {
+            bf16_t* o = static_cast<bf16_t*>(cache_out) + (item * H + head0 + hh) * ELL + g * 4 * C::MB;
+#pragma unroll
+            for (int q = 0; q < C::MB / 2; ++q) st8(o + 8 * q, v + 8 * q);
+          }
         }
       }
     }
@@ -194,8 +240,20 @@ struct CsCfg {
   static_assert(ELL % 32 == 0, "ell");
 };
 
-template <int ELL, int H>
-__global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cache, int64_t n_items,
+// 8 int8 codes -> 8 bf16 values (exact: |code| <= 127)
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint2 pk) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[j] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((pk.x >> (8 * j)) & 0xff)));
+    o[4 + j] = static_cast<__bf16>(static_cast<float>(static_cast<int8_t>((pk.y >> (8 * j)) & 0xff)));
+  }
+  return o;
+}
+
+template <int ELL, int H, bool I8 = false>
+__global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache_in,
+                                                  const float* __restrict__ qscale, int64_t n_items,
                                                   const bf16_t* __restrict__ lp,
                                                   const int64_t* __restrict__ ids,
                                                   const int64_t* __restrict__ off_g, int B,
@@ -203,6 +261,9 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
                                                   int* bad, int64_t tiles_per_wave) {
   using C = CsCfg<ELL, H>;
   constexpr int D = C::D, KB = C::KB;
+  // a wave serves HG heads of its candidates: it holds the L^P operands of
+  // those heads only, so large head counts do not exhaust the registers
+  constexpr int HG = H < 4 ? H : 4, NG = H / HG;
   __shared__ int64_t off_s[C::MAXB + 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
@@ -213,12 +274,15 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
   const int64_t* off = in_lds ? off_s : off_g;
 
   const int64_t ntiles = (total_M + 15) >> 4;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
+  const int64_t gw_all = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
+  const int hg = static_cast<int>(gw_all % NG);
+  const int64_t gw = gw_all / NG;
+  const int hbase = hg * HG;
   const int64_t t0 = gw * tiles_per_wave;
   const int64_t t1 = t0 + tiles_per_wave < ntiles ? t0 + tiles_per_wave : ntiles;
   if (t0 >= t1) return;
 
-  bf16x8 a[H][2][KB];
+  bf16x8 a[HG][2][KB];
   int cur = -1;
   int u = find_owner(off, B, t0 * 16);
 
@@ -230,14 +294,170 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
       while (ul + 1 < B && off[ul + 1] <= i) ++ul;
     const int64_t id = valid ? ids[i] : -1;
     const bool okid = valid && id >= 0 && id < n_items;
-    if (valid && !okid && g == 0 && bad != nullptr) atomicAdd(bad, 1);
+    if (valid && !okid && g == 0 && hg == 0 && bad != nullptr) atomicAdd(bad, 1);
 
-    bf16x8 bw[H][KB];
+    bf16x8 bw[HG][KB];
+    float qs[HG];
 #pragma unroll
-    for (int h = 0; h < H; ++h)
+    for (int hh = 0; hh < HG; ++hh) {
+      const int h = hbase + hh;
+      if constexpr (I8) {
+        const int8_t* row = static_cast<const int8_t*>(cache_in) + (id * H + h) * ELL + 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        bw[h][kb] = okid ? ld16(cache + (id * H + h) * ELL + kb * 32 + 8 * g) : zero8();
+        for (int kb = 0; kb < KB; ++kb)
+          bw[hh][kb] = okid ? i8x8_to_bf16(*reinterpret_cast<const uint2*>(row + kb * 32)) : zero8();
+        qs[hh] = okid ? qscale[id * H + h] : 0.f;
+      } else {
+        const bf16_t* row = static_cast<const bf16_t*>(cache_in) + (id * H + h) * ELL + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bw[hh][kb] = okid ? ld16(row + kb * 32) : zero8();
+        qs[hh] = 1.f;
+      }
+    }
+
+    const int last = static_cast<int>((total_M - 1 - t * 16) < 15 ? (total_M - 1 - t * 16) : 15);
+    const int ufirst = __shfl(ul, 0);
+    const int ulast = __shfl(ul, last);
+    for (int uu = ufirst; uu <= ulast; ++uu) {
+      if (!__any(valid && ul == uu)) continue;
+      if (uu != cur) {
+        const bf16_t* lb = lp + static_cast<int64_t>(uu) * ELL * D;
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int col = (hbase + hh) * 32 + 8 * (r >> 2) + 4 * c + (r & 3);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                a[hh][c][kb][j] = __builtin_bit_cast(__bf16, lb[static_cast<int64_t>(kb * 32 + 8 * g + j) * D + col]);
+          }
+        cur = uu;
+      }
+      const bool mine = valid && ul == uu;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc0 = mma(a[hh][0][kb], bw[hh][kb], acc0);
+          acc1 = mma(a[hh][1][kb], bw[hh][kb], acc1);
+        }
+        if (mine) {
+          const float sc = qs[hh];
+          const float v[8] = {acc0[0] * sc, acc0[1] * sc, acc0[2] * sc, acc0[3] * sc,
+                              acc1[0] * sc, acc1[1] * sc, acc1[2] * sc, acc1[3] * sc};
+          st8(out + i * D + (hbase + hh) * 32 + 8 * g, v);
+        }
+      }
+    }
+    u = __shfl(ul, last);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Uncached scoring (cold start), d_h = 32: per 16-candidate tile, gather the
+// items' rows, logits S^T = K_h T^T (links x candidates) against link keys
+// staged in LDS, phi over the links, then O^T = L^P_h^T P^T as in
+// cand_score.  Link order of the score blocks: M-block c, row 4*g + j ->
+// link (c/2)*32 + 8*g + 4*(c%2) + j, so the probabilities of each lane are
+// the K slices of the value product's B operand.
+// ---------------------------------------------------------------------------
+template <int ELL, int D, int H>
+struct UcCfg {
+  static constexpr int KB = D / 32, MB = ELL / 16, KBL = ELL / 32;
+  static constexpr int LDK = D + 8;  // padded key row
+  static constexpr size_t lds_bytes = static_cast<size_t>(H) * ELL * LDK * 2;
+  static_assert(D == 32 * H && ELL % 32 == 0, "shape");
+};
+
+template <int ELL, int D, int H>
+__global__ __launch_bounds__(256) void cand_score_uncached(
+    const bf16_t* __restrict__ items, int64_t n_items, const bf16_t* __restrict__ keys,
+    const bf16_t* __restrict__ lp, const int64_t* __restrict__ ids, const int64_t* __restrict__ off,
+    int B, int64_t total_M, bf16_t* __restrict__ out, int* bad, float scale, int phi,
+    int64_t tiles_per_wave) {
+  using C = UcCfg<ELL, D, H>;
+  constexpr int KB = C::KB, MB = C::MB, KBL = C::KBL, LDK = C::LDK;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = lane >> 4, r = lane & 15;
+  for (int e = tid; e < H * ELL * (D / 8); e += 256) {
+    const int row = e / (D / 8), c8 = e % (D / 8);
+    *reinterpret_cast<bf16x8*>(Ks + row * LDK + 8 * c8) = ld16(keys + static_cast<int64_t>(row) * D + 8 * c8);
+  }
+  __syncthreads();
+  const bool softmax = (phi == PHI_SOFTMAX);
+  const int64_t ntiles = (total_M + 15) >> 4;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
+  const int64_t t0 = gw * tiles_per_wave;
+  const int64_t t1 = t0 + tiles_per_wave < ntiles ? t0 + tiles_per_wave : ntiles;
+  if (t0 >= t1) return;
+
+  bf16x8 a[H][2][KBL];
+  int cur = -1;
+  int u = find_owner(off, B, t0 * 16);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t i = t * 16 + r;
+    const bool valid = i < total_M;
+    int ul = u;
+    if (valid)
+      while (ul + 1 < B && off[ul + 1] <= i) ++ul;
+    const int64_t id = valid ? ids[i] : -1;
+    const bool okid = valid && id >= 0 && id < n_items;
+    if (valid && !okid && g == 0 && bad != nullptr) atomicAdd(bad, 1);
+    bf16x8 tb[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) tb[kb] = okid ? ld16(items + id * D + kb * 32 + 8 * g) : zero8();
+
+    // probabilities per head as B operands of the value product
+    const bf16_t* Kt = Ks + opaque_zero();
+    bf16x8 pb[H][KBL];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      float v[4 * MB];
+#pragma unroll
+      for (int c = 0; c < MB; ++c) {
+        const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
+        const bf16_t* kr = Kt + (h * ELL + link) * LDK + 8 * g;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = mma(ld16(kr + kb * 32), tb[kb], acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[4 * c + q] = acc[q] * scale;
+      }
+      if (softmax) {
+        float mx = v[0];
+#pragma unroll
+        for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4 * MB; ++q) {
+          v[q] = __expf(v[q] - mx);
+          sum += v[q];
+        }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        const float inv = 1.f / sum;
+#pragma unroll
+        for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
+      } else {
+        constexpr float inv = 1.f / ELL;
+#pragma unroll
+        for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+      }
+#pragma unroll
+      for (int kb = 0; kb < KBL; ++kb) {
+        bf16x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(v[8 * kb + j]);
+        pb[h][kb] = o;
+      }
+    }
 
     const int last = static_cast<int>((total_M - 1 - t * 16) < 15 ? (total_M - 1 - t * 16) : 15);
     const int ufirst = __shfl(ul, 0);
@@ -252,7 +472,7 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
           for (int c = 0; c < 2; ++c) {
             const int col = h * 32 + 8 * (r >> 2) + 4 * c + (r & 3);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int kb = 0; kb < KBL; ++kb)
 #pragma unroll
               for (int j = 0; j < 8; ++j)
                 a[h][c][kb][j] = __builtin_bit_cast(__bf16, lb[static_cast<int64_t>(kb * 32 + 8 * g + j) * D + col]);
@@ -264,12 +484,14 @@ __global__ __launch_bounds__(256) void cand_score(const bf16_t* __restrict__ cac
       for (int h = 0; h < H; ++h) {
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          acc0 = mma(a[h][0][kb], bw[h][kb], acc0);
-          acc1 = mma(a[h][1][kb], bw[h][kb], acc1);
+        for (int kb = 0; kb < KBL; ++kb) {
+          acc0 = mma(a[h][0][kb], pb[h][kb], acc0);
+          acc1 = mma(a[h][1][kb], pb[h][kb], acc1);
         }
         if (mine) {
-          const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+          const float zf = okid ? 1.f : 0.f;  // out-of-range ids give zero rows
+          const float v[8] = {acc0[0] * zf, acc0[1] * zf, acc0[2] * zf, acc0[3] * zf,
+                              acc1[0] * zf, acc1[1] * zf, acc1[2] * zf, acc1[3] * zf};
           st8(out + i * D + h * 32 + 8 * g, v);
         }
       }

@@ -23,36 +23,37 @@ __device__ __forceinline__ int64_t vp_index(int64_t row, int col, int D) {
   return (row >> 3) * static_cast<int64_t>(D) * 8 + static_cast<int64_t>(col) * 8 + (row & 7);
 }
 
+// Pairwise (tree) sum of N values: a log-depth dependency chain instead of
+// a serial one.
+template <int N>
+__device__ __forceinline__ float tree_sum(const float* v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else {
+    return tree_sum<N / 2>(v) + tree_sum<N - N / 2>(v + N / 2);
+  }
+}
+
 // LayerNorm (no affine, eps 1e-5) of the row a lane group holds: v[] are
 // this lane's values of the row; the other values are in lanes ^16, ^32.
 template <int N>
 __device__ __forceinline__ void ln_rows(float* v, int D) {
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) s += v[i];
+  float s = tree_sum<N>(v);
   s += __shfl_xor(s, 16);
   s += __shfl_xor(s, 32);
   const float mu = s / D;
-  float q = 0.f;
+  float t[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const float t = v[i] - mu;
-    q += t * t;
+    const float u = v[i] - mu;
+    t[i] = u * u;
   }
+  float q = tree_sum<N>(t);
   q += __shfl_xor(q, 16);
   q += __shfl_xor(q, 32);
   const float rs = rsqrtf(q / D + 1e-5f);
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = (v[i] - mu) * rs;
-}
-
-// An opaque zero: offsetting a weight pointer by it inside a loop keeps the
-// compiler from hoisting every weight-fragment load of the loop body out of
-// the loop (which would hold all weights in registers and spill).
-__device__ __forceinline__ int opaque_zero() {
-  int z = 0;
-  asm volatile("" : "+v"(z));
-  return z;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* v) {

@@ -172,6 +172,46 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
                               const int64_t* cand_offsets, int64_t total_M, void* out,
                               int32_t* bad_id_count, void* stream);
 
+/* Int8 QK cache (LIME summary page, Tables 10 and 12: int8 lookup with
+ * dequantisation, int8 cache sizes; the scheme is not given there).  Same
+ * weights as lime_qk_cache_build, stored per (item, head) as symmetric
+ * codes with one float32 scale:
+ *   qscale[m, h] = max_k |w_k| / 127,  codes[m, h, k] = round-half-even(w_k * 127 / max_k |w_k|)
+ * (an all-zero row gets scale 0 and codes 0).  codes [n_items, heads, ell]
+ * int8 and qscale [n_items, heads] float32 are device buffers owned by the
+ * caller; dtype is the element type of items and link_keys.  Errors and
+ * limits as lime_qk_cache_build; qscale must be 4-byte aligned.            */
+lime_status_t lime_qk_cache_build_i8(lime_dtype_t dtype, lime_phi_t phi, float scale,
+                                     int64_t n_items, int32_t d, int32_t heads, int32_t ell,
+                                     const void* items, const void* link_keys, int8_t* codes,
+                                     float* qscale, void* stream);
+
+/* Candidate scoring from the int8 cache: as lime_cand_score with the cached
+ * row dequantised, out[i, h-cols] = qscale[id,h] * sum_k codes[id,h,k] *
+ * links_pers[b, k, h-cols].  dtype is the element type of links_pers and
+ * out.  Out-of-range ids: zero rows, counted in bad_id_count.              */
+lime_status_t lime_cand_score_i8(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                 int32_t heads, const int8_t* codes, const float* qscale,
+                                 int64_t n_items, const void* links_pers, const int64_t* cand_ids,
+                                 const int64_t* cand_offsets, int64_t total_M, void* out,
+                                 int32_t* bad_id_count, void* stream);
+
+/* Uncached (cold-start) scoring: the cache formula evaluated per candidate
+ * from the item rows, then the weighted sum (LIME summary page, Table 10,
+ * "Uncached global"; LIME notes, limitations: items without cached weights
+ * fall back to online computation).
+ *   out[i, h-cols] = sum_k phi_k(scale * link_keys[h,k,:] . items[id_i,:])
+ *                          * links_pers[b, k, h-cols]
+ * items [n_items, d], link_keys [heads, ell, d], links_pers [B, ell, d],
+ * out [total_M, d], all of element type dtype.  Out-of-range ids give zero
+ * rows and are counted in bad_id_count.  Limits as lime_qk_cache_build and
+ * lime_cand_score.                                                        */
+lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                       int32_t ell, int32_t d, int32_t heads, const void* items,
+                                       int64_t n_items, const void* link_keys, const void* links_pers,
+                                       const int64_t* cand_ids, const int64_t* cand_offsets,
+                                       int64_t total_M, void* out, int32_t* bad_id_count, void* stream);
+
 /* Static string naming a status code. */
 const char* lime_status_string(lime_status_t status);
 

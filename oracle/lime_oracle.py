@@ -43,6 +43,14 @@ Readings where the pages are silent (each is a choice of this oracle):
 * The candidate-side query/key projections fold into a per-head key tensor
   link_keys[h] in R^{ell x d}; values are the head slices of L^P.
 * An out-of-range candidate id yields a zero output row and is counted.
+* Int8 cache (the pages give "Int8 lookup+dequant" and int8 cache sizes,
+  LIME summary page, Tables 10 and 12, but no scheme): symmetric codes in
+  [-127, 127] with one float32 scale per (item, head), scale = max|w|/127,
+  code = round-half-even(w * 127/max|w|).  Codes are an integer decision
+  made in float32, as the kernel makes it.
+* Uncached scoring (the pages' "Uncached global" column, Table 10; the
+  cold-start fallback in the limitations section) is the cache formula
+  evaluated per candidate and then the same weighted sum.
 
 Parity unpinned: the layer internals beyond attention (LN placement, the
 SwiGLU MLP, residual order) are readings; they are pinned only by brute
@@ -56,7 +64,8 @@ import numpy as np
 __all__ = [
     "layer_norm", "silu", "phi_weights", "attend", "xor_attention",
     "xor_attention_dense", "xor_mask", "xor_layer", "xor_fwd",
-    "qk_cache_build", "cand_score",
+    "qk_cache_build", "cand_score", "quantize_i8", "dequantize_i8",
+    "cand_score_i8", "cand_score_uncached",
 ]
 
 LN_EPS = 1e-5
@@ -236,3 +245,47 @@ def cand_score(cache, links_pers, cand_ids, cand_offsets, n_items: int | None = 
         blk[ok] = o.reshape(-1, d)
         out[sl] = blk
     return out, bad
+
+
+def quantize_i8(cache):
+    """Symmetric int8 codes and float32 scales per (item, head) of a cache
+    [n, H, ell] (reading: scheme unstated on the pages).  The decision is
+    taken in float32: w32 = float32(w), m = max|w32|, code = rint(w32 *
+    (127/m)) clipped to [-127, 127], scale = m/127; an all-zero row gets
+    scale 0 and codes 0."""
+    w = np.asarray(cache, dtype=np.float64).astype(np.float32)
+    m = np.abs(w).max(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        inv = np.where(m > 0, np.float32(127.0) / m, np.float32(0.0)).astype(np.float32)
+    q = np.clip(np.rint((w * inv).astype(np.float32)), -127, 127).astype(np.int8)
+    scale = (m[..., 0] / np.float32(127.0)).astype(np.float32)
+    return q, scale
+
+
+def dequantize_i8(codes, scales):
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def cand_score_i8(codes, scales, links_pers, cand_ids, cand_offsets, n_items=None):
+    """Scoring from the int8 cache: dequantise the gathered rows, then the
+    same weighted sum as cand_score (LIME summary page, Table 10: int8
+    lookup + dequant)."""
+    return cand_score(dequantize_i8(codes, scales), links_pers, cand_ids, cand_offsets,
+                      n_items=n_items)
+
+
+def cand_score_uncached(items, link_keys, scale: float, phi: str, links_pers, cand_ids,
+                        cand_offsets):
+    """Scoring without a cache: the cache row of each candidate's item is
+    computed on the spot (LIME summary page, Table 10, "Uncached global"),
+    then the weighted sum.  Out-of-range ids give zero rows and are
+    counted."""
+    t = np.asarray(items)
+    ids = np.asarray(cand_ids, dtype=np.int64)
+    n = t.shape[0]
+    ok = (ids >= 0) & (ids < n)
+    uniq, inv = np.unique(ids[ok], return_inverse=True)
+    rows = qk_cache_build(t[uniq], link_keys, scale, phi)
+    remap = np.full(ids.shape[0], -1, dtype=np.int64)
+    remap[ok] = inv
+    return cand_score(rows, links_pers, remap, cand_offsets, n_items=len(uniq))

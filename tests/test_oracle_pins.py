@@ -425,6 +425,54 @@ def test_cache_size_matches_table12():
         assert per_item * g["items"] * g["bytes_per_weight"] / 1e9 == pytest.approx(gb, rel=1e-9)
 
 
+# ---------------------------------------------------------------- int8 cache, uncached scoring
+
+def test_int8_codes_within_half_a_step():
+    """|dequantised - w| <= scale/2 (the rounding bound), codes in [-127, 127],
+    the largest magnitude of each row maps to +-127 exactly."""
+    rng = _rng(21)
+    w = np.concatenate([rng.standard_normal((50, 3, 32)) * 0.05,
+                        np.abs(rng.standard_normal((5, 3, 32))) / 32], axis=0)
+    w[7, 1] = 0.0
+    q, s = O.quantize_i8(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (55, 3)
+    w32 = w.astype(np.float32).astype(np.float64)
+    err = np.abs(O.dequantize_i8(q, s) - w32)
+    assert np.all(err <= s[..., None].astype(np.float64) * (0.5 + 1e-6) + 1e-12)
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    mx = np.abs(q.astype(int)).max(-1)
+    assert np.all(mx[s > 0] == 127) and np.all(q[7, 1] == 0) and s[7, 1] == 0
+
+
+def test_int8_scoring_is_scoring_of_dequantised_cache():
+    rng = _rng(22)
+    cache = np.abs(rng.standard_normal((40, 2, 8))) / 8
+    q, s = O.quantize_i8(cache)
+    lp = rng.standard_normal((3, 8, 16))
+    ids = rng.integers(0, 40, size=20)
+    off = np.array([0, 5, 5, 20])
+    a, _ = O.cand_score_i8(q, s, lp, ids, off)
+    b, _ = _brute_cand(q.astype(np.float64) * s[..., None], lp, ids, off, 40)
+    assert np.abs(a - b).max() < 1e-12
+    # and within the quantisation error of the float scores
+    c, _ = O.cand_score(cache, lp, ids, off)
+    assert np.abs(a - c).max() <= (s.max() / 2) * np.abs(lp).sum(1).max() + 1e-12
+
+
+def test_uncached_equals_cache_then_score():
+    rng = _rng(23)
+    T = rng.standard_normal((30, 8))
+    K = rng.standard_normal((2, 4, 8))
+    lp = rng.standard_normal((2, 4, 8))
+    ids = rng.integers(-2, 32, size=11)
+    off = np.array([0, 6, 11])
+    for phi in ("softmax", "silu_mean"):
+        a, na = O.cand_score_uncached(T, K, 0.4, phi, lp, ids, off)
+        b, nb = _brute_cand(O.qk_cache_build(T, K, 0.4, phi), lp, ids, off, 30)
+        assert na == nb == int(((ids < 0) | (ids >= 30)).sum())
+        assert np.abs(a - b).max() < 1e-12
+
+
 # ---------------------------------------------------------------- mutation tests
 
 def _mutations():
