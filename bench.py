@@ -45,6 +45,8 @@ def parse():
                     help="approximate CPU budget of the oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps eagerly instead of replaying a HIP graph of one step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing the int8 and uncached candidate-side variants")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -190,6 +192,47 @@ def main():
         per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "GB/s": round(v["bytes"] / tk / 1e9, 1),
                        "TFLOP/s": round(v["flops"] / tk / 1e12, 2)}
 
+    # ---- the pages' other candidate-side variants (not part of the step):
+    # int8 cache build and scoring, uncached scoring (LIME summary page,
+    # Table 10 columns), each timed like the calls above
+    extras = {}
+    if not args.no_extras:
+        codes = torch.empty((w.n_items, w.heads, w.ell), dtype=torch.int8, device="cuda")
+        qsc = torch.empty((w.n_items, w.heads), dtype=torch.float32, device="cuda")
+        out2 = torch.empty_like(out)
+
+        def build_i8():
+            L.qk_cache_build_i8(items, keys, phi=w.phi, scale=scale, codes=codes, qscale=qsc)
+
+        def score_i8():
+            L.cand_score_i8(codes, qsc, lp, ids_d, coff_d, out=out2)
+
+        def score_uncached():
+            L.cand_score_uncached(items, keys, lp, ids_d, coff_d, phi=w.phi, scale=scale, out=out2)
+
+        build_i8()
+        torch.cuda.synchronize()
+        hl = w.heads * w.ell
+        ex_bytes = {
+            "lime_qk_cache_build_i8": w.n_items * (w.d * es + hl + 4 * w.heads),
+            "lime_cand_score_i8": n_cand * (hl + 4 * w.heads + w.d * es + 8),
+            "lime_cand_score_uncached": n_cand * (w.d * es + w.d * es + 8),
+        }
+        for k, fn in (("lime_qk_cache_build_i8", build_i8), ("lime_cand_score_i8", score_i8),
+                      ("lime_cand_score_uncached", score_uncached)):
+            g = capture(fn, args.steps)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t_ms = e0.elapsed_time(e1) / args.steps
+            del g
+            extras[k] = {"us": round(t_ms * 1e3, 2),
+                         "GB/s": round(ex_bytes[k] / (t_ms * 1e-3) / 1e9, 1),
+                         "per_s": round((w.n_items if "build" in k else n_cand) / (t_ms * 1e-3), 1)}
+
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -220,6 +263,7 @@ def main():
         "items_per_s": w.n_items / (ms_step * 1e-3),
         "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
         "per_call": per_call,
+        "variants": extras,
         "xor_fwd_plan": plan,
         "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
         "roofline": roofline,

@@ -313,8 +313,19 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
                          P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
     } else {
-      hipLaunchKernelGGL((mfma::qkv_proj<D>), dim3(static_cast<unsigned>(P.R_pad / 128 + (P.R_pad % 128 ? 1 : 0))),
-                         dim3(256), 0, st, Xin, R, P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+      // weights streamed through LDS, persistent workgroups
+      auto k = mfma::qkv_proj_stream<D>;
+      constexpr size_t lds = mfma::StreamCfg<D>::lds_bytes;
+      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(lds)) == hipSuccess;
+      (void)attr;
+      static const int per_cu = blocks_per_cu_lds(k, mfma::StreamCfg<D>::NT, lds);
+      const int64_t ntiles = (P.R_pad + 255) / 256;
+      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+      if (grid > ntiles) grid = ntiles;
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
     }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
     hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), dim3(static_cast<unsigned>(static_cast<int64_t>(B) * P.S)),
@@ -345,8 +356,20 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
     } else {
-      hipLaunchKernelGGL((mfma::post_block<D, D, RPW>), dim3(static_cast<unsigned>((pw + 3) / 4)), dim3(256), 0, st,
-                         Yr, Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
+      (void)pw;
+      auto k = mfma::post_block_stream<D>;
+      using PC = mfma::PostStreamCfg<D>;
+      constexpr size_t lds = PC::lds_bytes;
+      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   static_cast<int>(lds)) == hipSuccess;
+      (void)attr;
+      static const int per_cu = blocks_per_cu_lds(k, PC::NT, lds);
+      const int64_t ntiles = (rows_post + 16 * PC::NW - 1) / (16 * PC::NW);
+      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+      if (grid > ntiles) grid = ntiles;
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, Yr, Xin,
+                         Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
     }
@@ -699,7 +722,7 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
       LIME_CHECK_LAUNCH("uncached scoring (mfma)");                                                    \
       return ok();                                                                                     \
     }
-    LIME_UC(32, 64, 2) LIME_UC(32, 128, 4) LIME_UC(64, 128, 4) LIME_UC(32, 256, 8)
+    LIME_UC(32, 64, 2) LIME_UC(32, 128, 4) LIME_UC(64, 128, 4) LIME_UC(32, 256, 8) LIME_UC(64, 256, 8)
 #undef LIME_UC
   }
   const dim3 grid(static_cast<unsigned>((total_M + 63) / 64), heads);

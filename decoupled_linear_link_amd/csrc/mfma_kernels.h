@@ -368,7 +368,9 @@ template <int ELL, int D, int H>
 struct UcCfg {
   static constexpr int KB = D / 32, MB = ELL / 16, KBL = ELL / 32;
   static constexpr int LDK = D + 8;  // padded key row
-  static constexpr size_t lds_bytes = static_cast<size_t>(H) * ELL * LDK * 2;
+  // keys staged in LDS when they fit; otherwise read from global (L2)
+  static constexpr bool KLDS = static_cast<size_t>(H) * ELL * LDK * 2 <= 96 * 1024;
+  static constexpr size_t lds_bytes = KLDS ? static_cast<size_t>(H) * ELL * LDK * 2 : 0;
   static_assert(D == 32 * H && ELL % 32 == 0, "shape");
 };
 
@@ -380,15 +382,25 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
     int64_t tiles_per_wave) {
   using C = UcCfg<ELL, D, H>;
   constexpr int KB = C::KB, MB = C::MB, KBL = C::KBL, LDK = C::LDK;
+  (void)LDK;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
-  for (int e = tid; e < H * ELL * (D / 8); e += 256) {
-    const int row = e / (D / 8), c8 = e % (D / 8);
-    *reinterpret_cast<bf16x8*>(Ks + row * LDK + 8 * c8) = ld16(keys + static_cast<int64_t>(row) * D + 8 * c8);
+  const bf16_t* Ks;
+  int ldk;
+  if constexpr (C::KLDS) {
+    bf16_t* ks = reinterpret_cast<bf16_t*>(smem);
+    for (int e = tid; e < H * ELL * (D / 8); e += 256) {
+      const int row = e / (D / 8), c8 = e % (D / 8);
+      *reinterpret_cast<bf16x8*>(ks + row * LDK + 8 * c8) = ld16(keys + static_cast<int64_t>(row) * D + 8 * c8);
+    }
+    __syncthreads();
+    Ks = ks;
+    ldk = LDK;
+  } else {
+    Ks = keys;
+    ldk = D;
   }
-  __syncthreads();
   const bool softmax = (phi == PHI_SOFTMAX);
   const int64_t ntiles = (total_M + 15) >> 4;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
@@ -421,7 +433,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
 #pragma unroll
       for (int c = 0; c < MB; ++c) {
         const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-        const bf16_t* kr = Kt + (h * ELL + link) * LDK + 8 * g;
+        const bf16_t* kr = Kt + (h * ELL + link) * ldk + 8 * g;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) acc = mma(ld16(kr + kb * 32), tb[kb], acc);

@@ -663,6 +663,295 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Row
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming variants for widths whose weights do not fit in LDS
+// (d = 256).  A workgroup of 8 waves takes a tile of rows (32 per wave for
+// the projection, 16 per wave for the post-attention block) and streams
+// the weights through two LDS buffers of 64 padded rows: while the waves
+// multiply their register-resident rows by chunk c, every thread loads
+// chunk c+1 into registers and writes it to the other buffer.  Weight
+// traffic from L2 is then one pass per tile instead of one per wave.
+// ---------------------------------------------------------------------------
+template <int D>
+struct StreamCfg {
+  static constexpr int NW = 8, NT = 64 * NW;
+  static constexpr int CR = 64;                       // weight rows per chunk
+  static constexpr int LDW = D + 8;                   // padded row
+  static constexpr int CPT = CR * (D / 8) / NT;       // 16-byte pieces per thread per chunk
+  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * LDW * 2;
+  static_assert((CR * (D / 8)) % NT == 0, "chunk split");
+};
+
+// chunk loader: rows [r0, r0 + CR) of a [*, K] weight matrix (K == D here)
+template <int D>
+__device__ __forceinline__ void chunk_load(bf16x8 (&reg)[StreamCfg<D>::CPT], const bf16_t* __restrict__ W,
+                                           int r0, int tid) {
+  constexpr int C8 = D / 8;
+  W += opaque_zero();  // loop-invariant loads: keep them where they are issued
+#pragma unroll
+  for (int i = 0; i < StreamCfg<D>::CPT; ++i) {
+    const int e = tid + i * StreamCfg<D>::NT;
+    reg[i] = ld16(W + static_cast<int64_t>(r0 + e / C8) * D + 8 * (e % C8));
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void chunk_store(const bf16x8 (&reg)[StreamCfg<D>::CPT], bf16_t* buf, int tid) {
+  constexpr int C8 = D / 8, LDW = StreamCfg<D>::LDW;
+#pragma unroll
+  for (int i = 0; i < StreamCfg<D>::CPT; ++i) {
+    const int e = tid + i * StreamCfg<D>::NT;
+    *reinterpret_cast<bf16x8*>(buf + (e / C8) * LDW + 8 * (e % C8)) = reg[i];
+  }
+}
+
+// LN + QKV projection, weights streamed: 12 chunks of 64 rows of w_qkv per
+// 256-row tile (chunks 0..7: Q|K column pairs, 8..11: V blocks).
+template <int D>
+__global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_t R_pad,
+                                                       const bf16_t* __restrict__ W,
+                                                       bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
+  using C = StreamCfg<D>;
+  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW;
+  constexpr int NCH = 3 * D / CR, NQK = 2 * D / CR;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t ntiles = (R_pad + 32 * NW - 1) / (32 * NW);
+  const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int64_t total = my_tiles * NCH;
+  if (total <= 0) return;
+  bf16x8 reg[C::CPT];
+  chunk_load<D>(reg, W, 0, tid);
+  chunk_store<D>(reg, buf0, tid);
+  __syncthreads();
+  bf16x8 hb[2][KB];
+  bool active = false;
+  int64_t row0 = 0;
+  for (int64_t c = 0; c < total; ++c) {
+    const int k = static_cast<int>(c % NCH);
+    if (k == 0) {
+      const int64_t tile = blockIdx.x + (c / NCH) * gridDim.x;
+      row0 = tile * 32 * NW + 32 * w;
+      active = row0 < R_pad;
+      if (active) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+          float v[8 * KB];
+          if (row < R) {
+            const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 x = ld16(xr + kb * 32);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
+          }
+          ln_rows<8 * KB>(v, D);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+        }
+      }
+    }
+    const bool more = c + 1 < total;
+    if (more) chunk_load<D>(reg, W, static_cast<int>(((c + 1) % NCH) * CR), tid);
+    const bf16_t* wb = buf0 + (c & 1) * (CR * LDW) + opaque_zero();
+    if (active) {
+      if (k < NQK) {
+        // output columns [64k, 64k + 64) of Q|K: two 32-column pairs
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          floatx4 acc[2][2] = {};
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const bf16_t* wr = wb + (32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3)) * LDW + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 a = ld16(wr + kb * 32);
+              acc[cc][0] = mma(a, hb[0][kb], acc[cc][0]);
+              acc[cc][1] = mma(a, hb[1][kb], acc[cc][1]);
+            }
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+            const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
+                                acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+            st8(QK + row * (2 * D) + CR * k + 32 * pp + 8 * g, v);
+          }
+        }
+      } else {
+        // V columns [64(k-NQK), +64): four 16-column blocks, operands swapped
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          const bf16_t* wr = wb + (16 * nn + r) * LDW + 8 * g;
+          floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 b = ld16(wr + kb * 32);
+            acc0 = mma(hb[0][kb], b, acc0);
+            acc1 = mma(hb[1][kb], b, acc1);
+          }
+          const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+          st8(Vp + vp_index(row0 + 8 * g, CR * (k - NQK) + 16 * nn + r, D), v);
+        }
+      }
+    }
+    if (more) chunk_store<D>(reg, buf0 + ((c + 1) & 1) * (CR * LDW), tid);
+    __syncthreads();
+  }
+}
+
+// Post-attention block, weights streamed: 16 chunks of 64 weight rows per
+// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
+// each: one pair), 12..15 w_down (two pairs each).  One wave owns 16 rows.
+template <int D>
+struct PostStreamCfg {
+  static constexpr int NW = 4, NT = 64 * NW, CR = 64, LDW = D + 8;
+  static constexpr int CPT = CR * (D / 8) / NT;
+  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * LDW * 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+                                                         const bf16_t* __restrict__ Wo,
+                                                         const bf16_t* __restrict__ Wg,
+                                                         const bf16_t* __restrict__ Wu,
+                                                         const bf16_t* __restrict__ Wd) {
+  using C = PostStreamCfg<D>;
+  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW, NCH = 16;
+  static_assert(D == 256, "chunk schedule is written for d = 256");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t ntiles = (nrows + 16 * NW - 1) / (16 * NW);
+  const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  if (my_tiles <= 0) return;
+
+  // chunk k of the schedule: 64 weight rows (gate/up chunks: 32 of each).
+  // Thread tid loads rows tid / 32 + 8 i, i < 8, so i < 4 falls in the first
+  // 32 rows.  Chunk bases are uniform; the per-lane part is one 32-bit
+  // offset, recomputed per chunk so that no per-chunk address stays live.
+  static_assert(C::NT / (D / 8) == 8 && C::CPT == 8, "load pattern assumes 8 rows per step");
+  auto load_chunk_regs = [&](bf16x8 (&reg)[C::CPT], int k) {
+    const int off0 = (tid >> 5) * D + 8 * (tid & 31) + opaque_zero();
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const bf16_t* base;
+      int off;
+      if (k < 4) { base = Wo + 64 * k * D; off = off0 + 8 * i * D; }
+      else if (k < 12) { base = (i < 4 ? Wg : Wu) + 32 * (k - 4) * D; off = off0 + 8 * (i & 3) * D; }
+      else { base = Wd + 64 * (k - 12) * D; off = off0 + 8 * i * D; }
+      reg[i] = ld16(base + off);
+    }
+  };
+
+  auto store_regs = [&](const bf16x8 (&reg)[C::CPT], bf16_t* buf) {
+    constexpr int C8 = D / 8;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int e = tid + i * C::NT;
+      *reinterpret_cast<bf16x8*>(buf + (e / C8) * LDW + 8 * (e % C8)) = reg[i];
+    }
+  };
+  bf16x8 reg[C::CPT];
+  load_chunk_regs(reg, 0);
+  store_regs(reg, buf0);
+  __syncthreads();
+  for (int64_t it = 0; it < my_tiles; ++it) {
+    const int64_t tile = blockIdx.x + it * gridDim.x;
+    const int64_t row = tile * 16 * NW + 16 * w + r;
+    const bool rowok = row < nrows;
+    bf16x8 yb[1][KB];
+    float x1[1][D / 4];
+    {
+      const bf16_t* yr = rowok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
+      const bf16_t* xr = rowok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        yb[0][kb] = rowok ? ld16(yr + kb * 32) : zero8();
+        const bf16x8 x = rowok ? ld16(xr + kb * 32) : zero8();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] = static_cast<float>(x[q]);
+      }
+    }
+    bf16x8 gb[KB], mb[KB];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const bool more = (k + 1 < NCH) || (it + 1 < my_tiles);
+      if (more) load_chunk_regs(reg, (k + 1) % NCH);
+      const bf16_t* wb = buf0 + (k & 1) * (CR * LDW) + opaque_zero();
+      if (k < 4 || k >= 12) {
+        // x1 += (Y or M) W^T for column pairs 2k', 2k'+1
+        const int kk = k < 4 ? k : k - 12;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          floatx4 acc[2] = {};
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const bf16_t* wr = wb + (32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3)) * LDW + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              acc[cc] = mma(ld16(wr + kb * 32), k < 4 ? yb[0][kb] : mb[kb], acc[cc]);
+          }
+          const int p = 2 * kk + pp;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            x1[0][8 * p + q] += acc[0][q];
+            x1[0][8 * p + 4 + q] += acc[1][q];
+          }
+          // bound the fragment loads the scheduler keeps in flight
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (k == 3) {
+          float t[8 * KB];
+#pragma unroll
+          for (int i = 0; i < 8 * KB; ++i) t[i] = x1[0][i];
+          ln_rows<8 * KB>(t, D);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) gb[kb] = pack8(t + 8 * kb);
+        }
+      } else {
+        // gate/up column pair q2 = k - 4: rows [0,32) gate, [32,64) up
+        floatx4 ag[2] = {}, au[2] = {};
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int orow = 8 * (r >> 2) + 4 * cc + (r & 3);
+          const bf16_t* gr = wb + orow * LDW + 8 * g;
+          const bf16_t* ur = wb + (32 + orow) * LDW + 8 * g;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            ag[cc] = mma(ld16(gr + kb * 32), gb[kb], ag[cc]);
+            au[cc] = mma(ld16(ur + kb * 32), gb[kb], au[cc]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = silu_f(ag[0][q]) * au[0][q];
+          v[4 + q] = silu_f(ag[1][q]) * au[1][q];
+        }
+        mb[k - 4] = pack8(v);
+      }
+      if (more) store_regs(reg, buf0 + ((k + 1) & 1) * (CR * LDW));
+      __syncthreads();
+    }
+    if (rowok) {
+      bf16_t* orow = row_out<bf16_t>(Out, row);
+      if (orow != nullptr)
+#pragma unroll
+        for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[0][8 * p]);
+    }
+  }
+}
+
 // ===========================================================================
 // User-resident kernel: one workgroup (8 waves) per user, all layers in one
 // launch, for users whose ell + N_b rows fit in LDS.  Local rows: [0, ell)
