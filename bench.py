@@ -47,6 +47,9 @@ def parse():
                     help="launch the timed steps eagerly instead of replaying a HIP graph of one step")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the int8 and uncached candidate-side variants")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the cache build after the user side on one stream "
+                         "instead of beside it on a second stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -103,10 +106,22 @@ def main():
     def score(stream=None):
         L.cand_score(cache, lp, ids_d, coff_d, out=out, stream=stream)
 
-    def step(stream=None):
-        user(stream)
-        build(stream)
-        score(stream)
+    # The cache build does not depend on any user, so it runs on a second
+    # stream beside the user side; scoring waits for both.
+    side = torch.cuda.Stream()
+
+    def step():
+        main_s = torch.cuda.current_stream()
+        if args.serial:
+            user()
+            build()
+        else:
+            side.wait_stream(main_s)
+            with torch.cuda.stream(side):
+                build()
+            user()
+            main_s.wait_stream(side)
+        score()
 
     for _ in range(args.warmup):
         step()
@@ -265,7 +280,9 @@ def main():
         "per_call": per_call,
         "variants": extras,
         "xor_fwd_plan": plan,
-        "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
+        "launch": ("eager" if args.no_graph else "one hip-graph replay of the K captured steps")
+                  + ("; one stream" if args.serial else
+                     "; cache build on a second stream beside the user side"),
         "roofline": roofline,
     }
 

@@ -52,6 +52,17 @@ Readings where the pages are silent (each is a choice of this oracle):
   cold-start fallback in the limitations section) is the cache formula
   evaluated per candidate and then the same weighted sum.
 
+* LIME-MHA (LIME summary page, Fig. 2; LIME notes, experiments table:
+  "single-layer decoupled"): only the links -> history cross attention
+  runs; history rows are not updated by any layer and pass through.  The
+  link rows keep the rest of the layer (W_o + residual, gated MLP).
+* LIME-XOR+Window (LIME notes, Key design 3; Table 13): besides the ell
+  links, history row p also attends the history rows q with
+  1 <= |p - q| <= w (its neighbours before and after, itself excluded),
+  under one joint phi over the union.  The default half-width w = ell / 2
+  gives each row 2 ell keys, the context size the notes state.  The
+  silu_mean normaliser counts the union.  Link rows are unchanged.
+
 Parity unpinned: the layer internals beyond attention (LN placement, the
 SwiGLU MLP, residual order) are readings; they are pinned only by brute
 force against this module's own definitions, not by any number the pages
@@ -65,8 +76,13 @@ __all__ = [
     "layer_norm", "silu", "phi_weights", "attend", "xor_attention",
     "xor_attention_dense", "xor_mask", "xor_layer", "xor_fwd",
     "qk_cache_build", "cand_score", "quantize_i8", "dequantize_i8",
-    "cand_score_i8", "cand_score_uncached",
+    "cand_score_i8", "cand_score_uncached", "VARIANTS", "window_neighbours",
+    "default_window",
 ]
+
+# user-side variants: plain XOR attention, LIME-MHA (links -> history only),
+# LIME-XOR+Window (history rows also see a local window of history rows)
+VARIANTS = ("xor", "mha", "xor_window")
 
 LN_EPS = 1e-5
 
@@ -117,34 +133,71 @@ def attend(q, k, v, scale: float, phi: str) -> np.ndarray:
     return phi_weights(scale * (q @ k.T), phi) @ v
 
 
-def xor_attention(q, k, v, n_links: int, heads: int, scale: float, phi: str) -> np.ndarray:
+def default_window(n_links: int) -> int:
+    """Half-width of the LIME-XOR+Window neighbourhood: ell / 2 on each
+    side, so that a history row sees ell links plus ell neighbours."""
+    return max(1, n_links // 2)
+
+
+def window_neighbours(p: int, n: int, window: int) -> np.ndarray:
+    """History positions q in [0, n) with 1 <= |p - q| <= window."""
+    q = np.arange(max(0, p - window), min(n, p + window + 1))
+    return q[q != p]
+
+
+def xor_attention(q, k, v, n_links: int, heads: int, scale: float, phi: str,
+                  variant: str = "xor", window: int = 0) -> np.ndarray:
     """Decoupled XOR attention for one user (LIME notes, Key design 2, XORA
     equation): rows [0, n_links) are the context links, the rest history.
     History rows attend to the links only; link rows attend to the history
-    only."""
+    only.  variant "mha" drops the history -> links branch (history rows get
+    no attention output); "xor_window" lets history row p also attend the
+    history rows of ``window_neighbours`` with one phi over the union (LIME
+    notes, Key design 3)."""
+    if variant not in VARIANTS:
+        raise ValueError(variant)
     rows, d = q.shape
     dh = d // heads
+    n = rows - n_links
     y = np.zeros((rows, d))
     L, E = slice(0, n_links), slice(n_links, rows)
     for h in range(heads):
         c = slice(h * dh, (h + 1) * dh)
-        y[E, c] = attend(q[E, c], k[L, c], v[L, c], scale, phi)   # MHA(E, L^C, L^C)
         y[L, c] = attend(q[L, c], k[E, c], v[E, c], scale, phi)   # MHA(L^C, E, E)
+        if variant == "xor":
+            y[E, c] = attend(q[E, c], k[L, c], v[L, c], scale, phi)   # MHA(E, L^C, L^C)
+        elif variant == "xor_window":
+            for p in range(n):
+                keys = np.concatenate([np.arange(n_links), n_links + window_neighbours(p, n, window)])
+                i = n_links + p
+                y[i:i + 1, c] = attend(q[i:i + 1, c], k[keys, c], v[keys, c], scale, phi)
     return y
 
 
-def xor_mask(n_links: int, rows: int) -> np.ndarray:
-    """M[i, j] = [i is a link] xor [j is a link] (block anti-diagonal)."""
+def xor_mask(n_links: int, rows: int, variant: str = "xor", window: int = 0) -> np.ndarray:
+    """M[i, j] = [i is a link] xor [j is a link] (block anti-diagonal).
+    "mha" keeps only the link rows of it; "xor_window" adds the history
+    band 1 <= |i - j| <= window."""
     is_link = np.arange(rows) < n_links
-    return is_link[:, None] ^ is_link[None, :]
+    m = is_link[:, None] ^ is_link[None, :]
+    if variant == "mha":
+        m &= is_link[:, None]
+    elif variant == "xor_window":
+        i = np.arange(rows)
+        dist = np.abs(i[:, None] - i[None, :])
+        m |= (~is_link[:, None]) & (~is_link[None, :]) & (dist >= 1) & (dist <= window)
+    elif variant != "xor":
+        raise ValueError(variant)
+    return m
 
 
-def xor_attention_dense(q, k, v, n_links: int, heads: int, scale: float, phi: str) -> np.ndarray:
+def xor_attention_dense(q, k, v, n_links: int, heads: int, scale: float, phi: str,
+                        variant: str = "xor", window: int = 0) -> np.ndarray:
     """The same attention as dense masked self-attention over the whole
     concatenated sequence (the form the XOR mask defines)."""
     rows, d = q.shape
     dh = d // heads
-    m = xor_mask(n_links, rows)
+    m = xor_mask(n_links, rows, variant, window)
     cnt = m.sum(axis=1, keepdims=True)
     y = np.zeros((rows, d))
     for h in range(heads):
@@ -165,39 +218,51 @@ def xor_attention_dense(q, k, v, n_links: int, heads: int, scale: float, phi: st
 
 
 def xor_layer(x, lw: dict, n_links: int, heads: int, scale: float, phi: str,
-              dense: bool = False) -> np.ndarray:
+              dense: bool = False, variant: str = "xor", window: int = 0) -> np.ndarray:
     """One LIME-XOR layer (LIME notes, Key design 2: residual + gated MLP;
     training strategy: LN before the projections).  ``lw`` holds float64
-    weights in [out, in] layout."""
+    weights in [out, in] layout.  With variant "mha" the history rows pass
+    through unchanged."""
     d = x.shape[1]
     h = layer_norm(x)
     qkv = h @ lw["w_qkv"].T
     q, k, v = qkv[:, :d], qkv[:, d:2 * d], qkv[:, 2 * d:]
     att = xor_attention_dense if dense else xor_attention
-    y = att(q, k, v, n_links, heads, scale, phi)
-    x = x + y @ lw["w_o"].T
-    g = layer_norm(x)
-    return x + (silu(g @ lw["w_gate"].T) * (g @ lw["w_up"].T)) @ lw["w_down"].T
+    y = att(q, k, v, n_links, heads, scale, phi, variant, window)
+    x1 = x + y @ lw["w_o"].T
+    g = layer_norm(x1)
+    out = x1 + (silu(g @ lw["w_gate"].T) * (g @ lw["w_up"].T)) @ lw["w_down"].T
+    if variant == "mha":
+        out[n_links:] = x[n_links:]
+    return out
 
 
 def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, scale: float, phi: str,
-            users=None, dense: bool = False):
+            users=None, dense: bool = False, variant: str = "xor", window: int | None = None):
     """User-side encoder: stacked XOR layers over [L^C_b ; E_b] for each user.
 
     links_ctx [B, ell, d], hist [sum N, d], hist_offsets [B+1], weights a
     list of per-layer dicts.  Returns (links_pers [B', ell, d], hist_out list
-    of [N_b, d] arrays) for the users in ``users`` (default all)."""
+    of [N_b, d] arrays) for the users in ``users`` (default all).  variant
+    and window select LIME-MHA or LIME-XOR+Window (window defaults to
+    ell / 2 for the latter)."""
     lc = _f64(links_ctx)
     hs = hist
     off = np.asarray(hist_offsets, dtype=np.int64)
     W = [{k: _f64(v) for k, v in lw.items()} for lw in weights]
     B, ell, _ = lc.shape
+    if variant not in VARIANTS:
+        raise ValueError(variant)
+    if variant == "xor_window":
+        window = default_window(ell) if window is None else int(window)
+    else:
+        window = 0
     users = range(B) if users is None else users
     lp, ho = [], []
     for b in users:
         x = np.concatenate([lc[b], _f64(hs[off[b]:off[b + 1]])], axis=0)
         for lw in W:
-            x = xor_layer(x, lw, ell, heads, scale, phi, dense=dense)
+            x = xor_layer(x, lw, ell, heads, scale, phi, dense=dense, variant=variant, window=window)
         lp.append(x[:ell])
         ho.append(x[ell:])
     return np.stack(lp), ho

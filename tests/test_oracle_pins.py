@@ -6,7 +6,10 @@ XORA equation), library routines (torch's scaled_dot_product_attention,
 layer_norm, softmax, silu, linear in float64 on the CPU), exact identities
 (SiLU(s) - SiLU(-s) = s), closed-form special cases, brute force over
 scalars on tiny inputs, and the cache-size arithmetic of the LIME summary
-page, Table 12.  The mutation tests at the end plant plausible mistakes in
+page, Table 12.  The LIME-MHA and LIME-XOR+Window variants are pinned the
+same way: brute force from each variant's description, dense masked
+attention, torch SDPA with an explicit boolean mask, and invariances
+(window symmetry, locality, first-layer agreement with LIME-XOR).  The mutation tests at the end plant plausible mistakes in
 the oracle and check that some pin fails for each.
 """
 import json
@@ -153,7 +156,17 @@ def pin_layer_vs_torch(seed=4):
     return err
 
 
-def _brute_layer(x, lw, ell, heads, scale, phi):
+def _brute_allowed(i, rows, ell, variant, window):
+    """Keys row i may attend, written from the variant's description."""
+    if variant == "mha" and i >= ell:
+        return None  # history rows pass through the layer untouched
+    keys = [j for j in range(rows) if (i < ell) != (j < ell)]
+    if variant == "xor_window" and i >= ell:
+        keys += [j for j in range(ell, rows) if j != i and abs(j - i) <= window]
+    return keys
+
+
+def _brute_layer(x, lw, ell, heads, scale, phi, variant="xor", window=0):
     """One layer by scalar loops (tiny inputs only)."""
     rows, d = len(x), len(x[0])
     dh = d // heads
@@ -172,8 +185,12 @@ def _brute_layer(x, lw, ell, heads, scale, phi):
     h = [ln(list(r)) for r in x]
     qkv = [mv(lw["w_qkv"], r) for r in h]
     y = [[0.0] * d for _ in range(rows)]
+    passthrough = set()
     for i in range(rows):
-        allowed = [j for j in range(rows) if (i < ell) != (j < ell)]
+        allowed = _brute_allowed(i, rows, ell, variant, window)
+        if allowed is None:
+            passthrough.add(i)
+            continue
         if not allowed:
             continue
         for hd in range(heads):
@@ -189,7 +206,10 @@ def _brute_layer(x, lw, ell, heads, scale, phi):
                 y[i][c] = sum(w[t] * qkv[allowed[t]][2 * d + c] for t in range(len(allowed)))
     x2 = [[x[i][c] + mv(lw["w_o"], y[i])[c] for c in range(d)] for i in range(rows)]
     out = []
-    for r in x2:
+    for i, r in enumerate(x2):
+        if i in passthrough:
+            out.append(list(x[i]))
+            continue
         g = ln(r)
         gate, up = mv(lw["w_gate"], g), mv(lw["w_up"], g)
         mid = [gate[t] * sig(gate[t]) * up[t] for t in range(len(gate))]
@@ -209,6 +229,78 @@ def pin_layer_brute_force(seed=5):
             a = O.xor_layer(x, lw, ell, heads, 0.9, phi)
             b = _brute_layer(x.tolist(), lwl, ell, heads, 0.9, phi)
             err = max(err, float(np.abs(a - b).max()))
+    return err
+
+
+def pin_variant_layer_brute_force(seed=9):
+    """LIME-MHA and LIME-XOR+Window layers against scalar brute force."""
+    rng = _rng(seed)
+    err = 0.0
+    for ell, n, d, dff, heads, window in ((2, 6, 4, 4, 2, 2), (3, 5, 6, 4, 3, 1), (2, 4, 4, 4, 1, 5)):
+        x = rng.standard_normal((ell + n, d))
+        lw = _weights(rng, d, dff)
+        lwl = {k: v.tolist() for k, v in lw.items()}
+        for phi in ("softmax", "silu_mean"):
+            for variant in ("mha", "xor_window"):
+                a = O.xor_layer(x, lw, ell, heads, 0.9, phi, variant=variant, window=window)
+                b = _brute_layer(x.tolist(), lwl, ell, heads, 0.9, phi, variant, window)
+                err = max(err, float(np.abs(a - b).max()))
+    return err
+
+
+def pin_variants_dense_equals_decoupled(seed=10):
+    """Both variants: the decoupled form equals dense attention under the
+    variant's mask, for single layers and whole stacks."""
+    rng = _rng(seed)
+    err = 0.0
+    for ell in (1, 4):
+        for n in (0, 1, 2, 7, 12):
+            for heads, d in ((1, 4), (2, 8)):
+                for phi in ("softmax", "silu_mean"):
+                    q, k, v = _qkv(rng, ell + n, d)
+                    for variant, window in (("mha", 0), ("xor_window", 1), ("xor_window", 3)):
+                        a = O.xor_attention(q, k, v, ell, heads, 0.7, phi, variant, window)
+                        b = O.xor_attention_dense(q, k, v, ell, heads, 0.7, phi, variant, window)
+                        err = max(err, float(np.abs(a - b).max()))
+    B, ell, d, heads = 3, 4, 8, 2
+    off = np.array([0, 9, 9, 12])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((12, d))
+    W = [_weights(rng, d, d) for _ in range(2)]
+    for phi in ("softmax", "silu_mean"):
+        for variant in ("mha", "xor_window"):
+            a, ha = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi, variant=variant, window=2)
+            b, hb = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi, dense=True, variant=variant, window=2)
+            err = max(err, float(np.abs(a - b).max()))
+            for x, y in zip(ha, hb):
+                if x.size:
+                    err = max(err, float(np.abs(x - y).max()))
+    return err
+
+
+def pin_window_softmax_vs_sdpa(seed=11):
+    """LIME-XOR+Window with softmax: every row equals torch's
+    scaled_dot_product_attention over all rows with a boolean mask built
+    from the variant's description (links <-> history, plus the history
+    band 1 <= |i - j| <= w)."""
+    rng = _rng(seed)
+    ell, n, d, heads, scale, window = 3, 10, 8, 2, 0.6, 2
+    dh = d // heads
+    q, k, v = _qkv(rng, ell + n, d)
+    y = O.xor_attention(q, k, v, ell, heads, scale, "softmax", "xor_window", window)
+    rows = ell + n
+    mask = torch.zeros((rows, rows), dtype=torch.bool)
+    for i in range(rows):
+        for j in range(rows):
+            cross = (i < ell) != (j < ell)
+            band = i >= ell and j >= ell and 1 <= abs(i - j) <= window
+            mask[i, j] = cross or band
+    err = 0.0
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    for h in range(heads):
+        c = slice(h * dh, (h + 1) * dh)
+        ref = F.scaled_dot_product_attention(t(q[:, c]), t(k[:, c]), t(v[:, c]), attn_mask=mask, scale=scale)
+        err = max(err, float(np.abs(y[:, c] - ref.numpy()).max()))
     return err
 
 
@@ -276,6 +368,9 @@ ALL_PINS = {
     "cache_vs_torch": (pin_cache_vs_torch, 1e-12),
     "cache_silu_odd": (pin_cache_silu_odd, 1e-12),
     "cand_brute_force": (pin_cand_brute_force, 1e-12),
+    "variant_layer_brute_force": (pin_variant_layer_brute_force, 1e-11),
+    "variants_dense_equals_decoupled": (pin_variants_dense_equals_decoupled, 1e-11),
+    "window_softmax_vs_sdpa": (pin_window_softmax_vs_sdpa, 1e-12),
 }
 
 
@@ -475,6 +570,78 @@ def test_uncached_equals_cache_then_score():
 
 # ---------------------------------------------------------------- mutation tests
 
+def test_window_zero_is_plain_xor():
+    rng = _rng(30)
+    ell, n, d, heads = 3, 7, 8, 2
+    q, k, v = _qkv(rng, ell + n, d)
+    for phi in ("softmax", "silu_mean"):
+        a = O.xor_attention(q, k, v, ell, heads, 0.5, phi, "xor_window", 0)
+        b = O.xor_attention(q, k, v, ell, heads, 0.5, phi)
+        assert np.abs(a - b).max() < 1e-14
+
+
+def test_mha_first_layer_links_equal_xor_and_history_passes():
+    """In the first layer the link rows see only LN(E) and LN(L^C), so
+    LIME-MHA and LIME-XOR agree on them; LIME-MHA leaves history rows as
+    they came in, whatever the depth."""
+    rng = _rng(31)
+    B, ell, d, heads = 2, 4, 8, 2
+    off = np.array([0, 6, 11])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((11, d))
+    W = [_weights(rng, d, d) for _ in range(3)]
+    for phi in ("softmax", "silu_mean"):
+        a, _ = O.xor_fwd(lc, hs, off, W[:1], heads, 0.5, phi, variant="mha")
+        b, _ = O.xor_fwd(lc, hs, off, W[:1], heads, 0.5, phi)
+        assert np.abs(a - b).max() < 1e-13
+        _, ho = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi, variant="mha")
+        for bb, x in enumerate(ho):
+            assert np.array_equal(x, hs[off[bb]:off[bb + 1]])
+
+
+def test_window_reversal_symmetry():
+    """The window reaches equally far before and after: reversing every
+    history keeps L^P and reverses the history outputs."""
+    rng = _rng(32)
+    B, ell, d, heads = 2, 4, 8, 2
+    lens = [9, 5]
+    off = np.array([0, 9, 14])
+    lc = rng.standard_normal((B, ell, d))
+    hs = rng.standard_normal((14, d))
+    rev = np.concatenate([hs[off[b]:off[b + 1]][::-1] for b in range(B)])
+    W = [_weights(rng, d, d) for _ in range(2)]
+    for phi in ("softmax", "silu_mean"):
+        a, ha = O.xor_fwd(lc, hs, off, W, heads, 0.5, phi, variant="xor_window", window=2)
+        b, hb = O.xor_fwd(lc, rev, off, W, heads, 0.5, phi, variant="xor_window", window=2)
+        assert np.abs(a - b).max() < 1e-12
+        for x, y, nb in zip(ha, hb, lens):
+            assert x.shape[0] == nb and np.abs(x - y[::-1]).max() < 1e-12
+
+
+def test_window_changes_history_rows_only_through_neighbours():
+    """Perturbing history row j's key and value changes the attention
+    output of every link row and of the history rows within w of j, and of
+    no other row."""
+    rng = _rng(33)
+    ell, n, d, heads, window = 2, 12, 4, 1, 2
+    q, k, v = _qkv(rng, ell + n, d)
+    y0 = O.xor_attention(q, k, v, ell, heads, 0.5, "softmax", "xor_window", window)
+    k2, v2 = k.copy(), v.copy()
+    j = ell + 9
+    k2[j] += 1.0
+    v2[j] -= 1.0
+    y1 = O.xor_attention(q, k2, v2, ell, heads, 0.5, "softmax", "xor_window", window)
+    changed = np.nonzero(np.abs(y1 - y0).max(axis=1) > 0)[0]
+    expect = set(range(ell)) | {i for i in range(ell, ell + n) if 1 <= abs(i - j) <= window}
+    assert set(changed.tolist()) == expect
+
+
+def test_default_window_gives_two_ell_keys():
+    ell = 32
+    w = O.default_window(ell)
+    assert len(O.window_neighbours(100, 1000, w)) + ell == 2 * ell
+
+
 def _mutations():
     def silu_norm_off(s, phi):
         n = s.shape[-1]
@@ -504,7 +671,16 @@ def _mutations():
     def silu_sign(s):
         return -s * O._sigmoid(-s)
 
+    def window_with_self(p, n, window):
+        q = np.arange(max(0, p - window), min(n, p + window + 1))
+        return q
+
+    def window_one_sided(p, n, window):
+        return np.arange(max(0, p - window), p)
+
     return {
+        "window includes the row itself": ("window_neighbours", window_with_self),
+        "window reaches only backwards": ("window_neighbours", window_one_sided),
         "silu normaliser off by one": ("phi_weights", silu_norm_off),
         "softmax denominator perturbed": ("phi_weights", no_max_shift_wrong_sum),
         "LayerNorm with unbiased variance": ("layer_norm", ln_unbiased),
@@ -514,7 +690,7 @@ def _mutations():
     }
 
 
-ORIG = {k: getattr(O, k) for k in ("phi_weights", "layer_norm", "attend", "silu")}
+ORIG = {k: getattr(O, k) for k in ("phi_weights", "layer_norm", "attend", "silu", "window_neighbours")}
 
 
 @pytest.mark.parametrize("name", sorted(_mutations()))
