@@ -47,9 +47,6 @@ def parse():
                     help="launch the timed steps eagerly instead of replaying a HIP graph of one step")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the int8 and uncached candidate-side variants")
-    ap.add_argument("--serial", action="store_true",
-                    help="run the cache build after the user side on one stream "
-                         "instead of beside it on a second stream")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -106,21 +103,9 @@ def main():
     def score(stream=None):
         L.cand_score(cache, lp, ids_d, coff_d, out=out, stream=stream)
 
-    # The cache build does not depend on any user, so it runs on a second
-    # stream beside the user side; scoring waits for both.
-    side = torch.cuda.Stream()
-
     def step():
-        main_s = torch.cuda.current_stream()
-        if args.serial:
-            user()
-            build()
-        else:
-            side.wait_stream(main_s)
-            with torch.cuda.stream(side):
-                build()
-            user()
-            main_s.wait_stream(side)
+        user()
+        build()
         score()
 
     for _ in range(args.warmup):
@@ -207,9 +192,10 @@ def main():
         per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "GB/s": round(v["bytes"] / tk / 1e9, 1),
                        "TFLOP/s": round(v["flops"] / tk / 1e12, 2)}
 
-    # ---- the pages' other candidate-side variants (not part of the step):
-    # int8 cache build and scoring, uncached scoring (LIME summary page,
-    # Table 10 columns), each timed like the calls above
+    # ---- the pages' other variants (not part of the step): the user-side
+    # LIME-MHA and LIME-XOR+Window; int8 cache build and scoring, uncached
+    # scoring (LIME summary page, Table 10 columns); each timed like the
+    # calls above
     extras = {}
     if not args.no_extras:
         codes = torch.empty((w.n_items, w.heads, w.ell), dtype=torch.int8, device="cuda")
@@ -233,6 +219,30 @@ def main():
             "lime_cand_score_i8": n_cand * (hl + 4 * w.heads + w.d * es + 8),
             "lime_cand_score_uncached": n_cand * (w.d * es + w.d * es + 8),
         }
+        lp2 = torch.empty_like(lp)
+
+        def user_variant(variant):
+            def run():
+                L.xor_fwd(lc, hs, hoff, wts, heads=w.heads, phi=w.phi, scale=scale, max_N=max_N,
+                          links_pers=lp2, workspace=ws, variant=variant)
+            return run
+
+        # the user-side variants (LIME-MHA; LIME-XOR+Window with ell/2
+        # neighbours on each side), timed like the user side of the step
+        for k, fn in (("lime_xor_fwd_variant[mha]", user_variant("mha")),
+                      ("lime_xor_fwd_variant[xor_window]", user_variant("xor_window"))):
+            fn()
+            torch.cuda.synchronize()
+            g = capture(fn, args.steps)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t_ms = e0.elapsed_time(e1) / args.steps
+            del g
+            extras[k] = {"us": round(t_ms * 1e3, 2), "users_per_s": round(w.B / (t_ms * 1e-3), 1)}
         for k, fn in (("lime_qk_cache_build_i8", build_i8), ("lime_cand_score_i8", score_i8),
                       ("lime_cand_score_uncached", score_uncached)):
             g = capture(fn, args.steps)
@@ -280,9 +290,7 @@ def main():
         "per_call": per_call,
         "variants": extras,
         "xor_fwd_plan": plan,
-        "launch": ("eager" if args.no_graph else "one hip-graph replay of the K captured steps")
-                  + ("; one stream" if args.serial else
-                     "; cache build on a second stream beside the user side"),
+        "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
         "roofline": roofline,
     }
 

@@ -5,7 +5,8 @@ kernels of liblime.so.  Tensors are torch device tensors; calls enqueue on
 torch's current stream and return without synchronising.  The functions
 mirror the C ABI in include/lime.h:
 
-    xor_fwd          -> lime_xor_fwd          (user side, LIME-XOR layers)
+    xor_fwd          -> lime_xor_fwd          (user side, LIME-XOR layers;
+                        variant="mha" / "xor_window" -> lime_xor_fwd_variant)
     qk_cache_build   -> lime_qk_cache_build   (offline QK cache)
     cand_score       -> lime_cand_score       (online candidate scoring)
 
@@ -21,7 +22,7 @@ import torch
 
 __all__ = [
     "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "xor_fwd_plan", "qk_cache_build",
-    "qk_cache_build_i8", "cand_score", "cand_score_i8", "cand_score_uncached", "PHI", "DTYPE", "EXPORTED",
+    "qk_cache_build_i8", "cand_score", "cand_score_i8", "cand_score_uncached", "PHI", "DTYPE", "VARIANT", "EXPORTED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,12 +36,13 @@ if not os.path.exists(lib_path):
 lib = ctypes.CDLL(lib_path)
 
 PHI = {"softmax": 0, "silu_mean": 1}
+VARIANT = {"xor": 0, "mha": 1, "xor_window": 2}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
           3: "LIME_ERR_WORKSPACE", 4: "LIME_ERR_HIP"}
 
 # every symbol include/lime.h declares
-EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_workspace_size", "lime_xor_fwd_plan",
+EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_variant", "lime_xor_fwd_workspace_size", "lime_xor_fwd_plan",
             "lime_qk_cache_build", "lime_qk_cache_build_i8", "lime_cand_score", "lime_cand_score_i8",
             "lime_cand_score_uncached", "lime_status_string", "lime_last_error")
 
@@ -65,6 +67,8 @@ lib.lime_xor_fwd.restype = ctypes.c_int
 lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _vp, _vp, _vp, _i64, _i32, ctypes.POINTER(LayerWeights), _vp, _vp,
                              _vp, ctypes.c_size_t, _vp]
+lib.lime_xor_fwd_variant.restype = ctypes.c_int
+lib.lime_xor_fwd_variant.argtypes = [ctypes.c_int, _i32] + lib.lime_xor_fwd.argtypes
 lib.lime_qk_cache_build.restype = ctypes.c_int
 lib.lime_qk_cache_build.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i64, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]
@@ -138,11 +142,16 @@ def xor_fwd_plan(dtype, B, ell, d, heads, layers, d_ff, total_N, max_N, with_his
 
 def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
             scale: float | None = None, max_N: int | None = None, want_hist: bool = False,
-            links_pers=None, hist_out=None, workspace=None, stream=None):
+            links_pers=None, hist_out=None, workspace=None, stream=None,
+            variant: str = "xor", window: int | None = None):
     """Stacked LIME-XOR layers.  links_ctx [B, ell, d], hist [total_N, d],
     hist_offsets [B+1] int64 (device), weights: list of per-layer dicts with
     w_qkv [3d, d], w_o [d, d], w_gate/w_up [d_ff, d], w_down [d, d_ff].
+    variant "mha" (LIME-MHA, links -> history only) or "xor_window"
+    (LIME-XOR+Window, window neighbours on each side, default ell // 2).
     Returns (links_pers [B, ell, d], hist_out [total_N, d] or None)."""
+    if variant not in VARIANT:
+        raise ValueError(f"variant must be one of {sorted(VARIANT)}")
     _want(links_ctx, "links_ctx", dims=3)
     dt = links_ctx.dtype
     _want(hist, "hist", dt, 2)
@@ -170,10 +179,15 @@ def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu
     need = xor_fwd_workspace_size(dt, B, ell, d, heads, d_ff, total_N, max_N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=links_ctx.device)
-    _check(lib.lime_xor_fwd(DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
-                            _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
-                            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel(),
-                            _stream(stream)), "lime_xor_fwd")
+    args = (DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
+            _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
+            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel(), _stream(stream))
+    if variant == "xor" and window is None:
+        _check(lib.lime_xor_fwd(*args), "lime_xor_fwd")
+    else:
+        if window is None:
+            window = max(1, ell // 2) if variant == "xor_window" else 0
+        _check(lib.lime_xor_fwd_variant(VARIANT[variant], int(window), *args), "lime_xor_fwd_variant")
     return links_pers, hist_out
 
 

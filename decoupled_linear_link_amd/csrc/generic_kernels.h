@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void xor_attn(const T* __restrict__ qkv, T* __
                                                 const int64_t* __restrict__ off, int B, int ell,
                                                 int d, int H, int S, int64_t chunk,
                                                 int64_t total_N, float scale, int phi,
-                                                int do_e_branch) {
+                                                int do_e_branch, int half) {
   const int b = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t ld = 3 * static_cast<int64_t>(d);
@@ -151,17 +151,29 @@ __global__ __launch_bounds__(256) void xor_attn(const T* __restrict__ qkv, T* __
   const int64_t hi = (s == S - 1) ? u1 : u0 + clamp64((s + 1) * chunk, 0, n);
   const T* links = qkv + static_cast<int64_t>(b) * ell * ld + h * DH;  // Q of link 0, head h
 
-  // ---- E-branch: history rows -> links
+  // ---- E-branch: history rows -> links (and, with half > 0, the history
+  // rows q of the same user with 1 <= |q - j| <= half: LIME-XOR+Window)
   if (do_e_branch) {
     for (int64_t j = lo + tid; j < hi; j += 256) {
       const T* row = qkv + (nlr + j) * ld + h * DH;
       float q[DH];
 #pragma unroll
       for (int c = 0; c < DH; ++c) q[c] = Elt<T>::ld(row + c) * scale;
+      // keys: the ell links, then the window rows (none when half = 0)
+      const int64_t w0 = j - half > u0 ? j - half : u0;
+      const int64_t w1 = j + half < u1 - 1 ? j + half : u1 - 1;
+      const int64_t nwin = half > 0 ? w1 - w0 + 1 : 0;
+      auto key_row = [&](int64_t t) -> const T* {
+        if (t < ell) return links + t * ld + d;
+        int64_t qr = w0 + (t - ell);
+        if (qr >= j) ++qr;  // skip the row itself
+        return qkv + (nlr + qr) * ld + d + h * DH;
+      };
+      const int64_t nkeys = ell + (nwin > 0 ? nwin - 1 : 0);
       float m = -INFINITY;
       if (phi == PHI_SOFTMAX) {
-        for (int k = 0; k < ell; ++k) {
-          const T* kr = links + k * ld + d;
+        for (int64_t k = 0; k < nkeys; ++k) {
+          const T* kr = key_row(k);
           float sc = 0.f;
 #pragma unroll
           for (int c = 0; c < DH; ++c) sc += q[c] * Elt<T>::ld(kr + c);
@@ -171,8 +183,8 @@ __global__ __launch_bounds__(256) void xor_attn(const T* __restrict__ qkv, T* __
       float l = 0.f, acc[DH];
 #pragma unroll
       for (int c = 0; c < DH; ++c) acc[c] = 0.f;
-      for (int k = 0; k < ell; ++k) {
-        const T* kr = links + k * ld + d;
+      for (int64_t k = 0; k < nkeys; ++k) {
+        const T* kr = key_row(k);
         float sc = 0.f;
 #pragma unroll
         for (int c = 0; c < DH; ++c) sc += q[c] * Elt<T>::ld(kr + c);

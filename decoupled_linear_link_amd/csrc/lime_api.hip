@@ -174,11 +174,20 @@ bool xor_mfma_ok(lime_dtype_t dtype, int ell, int d, int heads, int d_ff) {
          (d == 64 || d == 128 || d == 256) && d_ff == d;
 }
 
+// the user-side variant a call runs (LIME-XOR, LIME-MHA, LIME-XOR+Window)
+struct VariantArgs {
+  bool links_only = false;  // LIME-MHA: history rows are never updated
+  int half = 0;             // LIME-XOR+Window: neighbours on each side (0: none)
+};
+
+// widest window the matrix-core kernels serve for this ell
+int mfma_max_half(int ell) { return (mfma::win_nkw(ell) - 32) / 2; }
+
 XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
-                 int32_t d_ff, int64_t total_N, int32_t max_N) {
+                 int32_t d_ff, int64_t total_N, int32_t max_N, bool allow_mfma = true) {
   XorPlan p;
   const size_t es = dtype == LIME_F32 ? 4 : 2;
-  p.mfma = xor_mfma_ok(dtype, ell, d, heads, d_ff);
+  p.mfma = allow_mfma && xor_mfma_ok(dtype, ell, d, heads, d_ff);
   if (p.mfma && d <= 128) {
     const int64_t RT = (ell + static_cast<int64_t>(max_N) + 31) / 32 * 32;
     const int64_t per_row = (d + 4) * 4 + (2 * d + 8) * 2 + d * 2 + (d + 8) * 2;
@@ -230,12 +239,27 @@ int max_dynamic_lds() {
   return v;
 }
 
+template <int ELL, int D, int NKW>
+void launch_resident(int B, size_t lds, hipStream_t st, const void* links_ctx, const void* hist,
+                     const int64_t* off, int64_t total_N, int RT, int layers, const mfma::LayerSet& ls,
+                     float scale, lime_phi_t phi, void* links_pers, void* hist_out, const VariantArgs& va) {
+  auto k = mfma::xor_fwd_resident<ELL, D, NKW>;
+  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               160 * 1024) == hipSuccess;
+  (void)attr;
+  hipLaunchKernelGGL(k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
+                     static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
+                     static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
+                     static_cast<bf16_t*>(hist_out), va.links_only ? 1 : 0, va.half);
+}
+
 // user-resident kernel: one workgroup per user, all layers, when the rows fit
 template <int ELL, int D>
 bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int layers,
                       const void* links_ctx, const void* hist, const int64_t* off, int64_t total_N,
                       int32_t max_N, const lime_layer_weights_t* w, void* links_pers, void* hist_out,
-                      hipStream_t st, lime_status_t* status) {
+                      const VariantArgs& va, hipStream_t st, lime_status_t* status) {
   if constexpr (D > 128) {
     return false;
   } else {
@@ -244,11 +268,6 @@ bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int 
   const size_t lds = mfma::ResCfg<ELL, D>::lds_bytes(RT);
   static const int limit = max_dynamic_lds();
   if (lds > static_cast<size_t>(limit) || lds > 160 * 1024) return false;
-  auto k = mfma::xor_fwd_resident<ELL, D>;
-  static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               160 * 1024) == hipSuccess;
-  (void)attr;
   mfma::LayerSet ls{};
   for (int l = 0; l < layers; ++l) {
     ls.p[l][0] = static_cast<const bf16_t*>(w[l].w_qkv);
@@ -257,10 +276,12 @@ bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int 
     ls.p[l][3] = static_cast<const bf16_t*>(w[l].w_up);
     ls.p[l][4] = static_cast<const bf16_t*>(w[l].w_down);
   }
-  hipLaunchKernelGGL(k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
-                     static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
-                     static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
-                     static_cast<bf16_t*>(hist_out));
+  if (va.half > 0)
+    launch_resident<ELL, D, mfma::win_nkw(ELL)>(B, lds, st, links_ctx, hist, off, total_N, RT, layers, ls, scale,
+                                                 phi, links_pers, hist_out, va);
+  else
+    launch_resident<ELL, D, 0>(B, lds, st, links_ctx, hist, off, total_N, RT, layers, ls, scale, phi,
+                               links_pers, hist_out, va);
   hipError_t e = hipGetLastError();
   *status = (e == hipSuccess) ? ok() : fail(LIME_ERR_HIP, "user-resident xor: %s", hipGetErrorString(e));
   (void)P;
@@ -274,11 +295,12 @@ template <int ELL, int D>
 lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B, int layers,
                            const void* links_ctx, const void* hist, const int64_t* off,
                            int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
-                           void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+                           void* links_pers, void* hist_out, const VariantArgs& va, char* ws,
+                           hipStream_t st) {
   if (P.resident) {
     lime_status_t status = LIME_OK;
     if (run_xor_resident<ELL, D>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, max_N, w,
-                                 links_pers, hist_out, st, &status))
+                                 links_pers, hist_out, va, st, &status))
       return status;
   }
   constexpr int H = D / 32;
@@ -293,9 +315,11 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   const Rows Yr{Y, Y + nlr * D, nlr, D};
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
-    const bool full = !last || hist_out != nullptr;
+    const bool full = !va.links_only && (!last || hist_out != nullptr);
     const int64_t rows_post = full ? R : nlr;
-    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, D} : Xws;
+    // LIME-MHA never updates history rows: every layer reads the input E
+    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, D}
+                     : va.links_only ? Rows{X, const_cast<void*>(hist), nlr, D} : Xws;
     const Rows Xout = last ? Rows{links_pers, hist_out, nlr, D} : Xws;
     if constexpr (D <= 128) {
       // weights staged in LDS, persistent workgroups (one per CU)
@@ -328,10 +352,16 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                          P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
     }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
-    hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), dim3(static_cast<unsigned>(static_cast<int64_t>(B) * P.S)),
-                       dim3(64 * H), 0, st,
-                       QK, Vp, Y, part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi),
-                       full ? 1 : 0);
+    {
+      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * P.S));
+      if (va.half > 0 && full)
+        hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL)>), grid, dim3(64 * H), 0, st, QK, Vp, Y,
+                           part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi), 1, va.half,
+                           P.R_pad);
+      else
+        hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, B, P.S,
+                           P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
+    }
     LIME_CHECK_LAUNCH("xor attention (mfma)");
     {
       const int64_t n = static_cast<int64_t>(B) * H * ELL * 32;
@@ -382,9 +412,10 @@ lime_status_t dispatch_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, i
                                 int layers, const void* links_ctx, const void* hist,
                                 const int64_t* off, int64_t total_N, int32_t max_N,
                                 const lime_layer_weights_t* w,
-                                void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+                                void* links_pers, void* hist_out, const VariantArgs& va, char* ws,
+                                hipStream_t st) {
 #define LIME_XM(E, DD) \
-  if (ell == E && d == DD) return run_xor_mfma<E, DD>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, max_N, w, links_pers, hist_out, ws, st);
+  if (ell == E && d == DD) return run_xor_mfma<E, DD>(P, phi, scale, B, layers, links_ctx, hist, off, total_N, max_N, w, links_pers, hist_out, va, ws, st);
   LIME_XM(32, 64) LIME_XM(32, 128) LIME_XM(32, 256)
   LIME_XM(64, 64) LIME_XM(64, 128) LIME_XM(64, 256)
 #undef LIME_XM
@@ -396,7 +427,7 @@ lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int
                               int d, int H, int layers, int d_ff, const void* links_ctx,
                               const void* hist, const int64_t* off, int64_t total_N,
                               const lime_layer_weights_t* w, void* links_pers, void* hist_out,
-                              char* ws, hipStream_t st) {
+                              const VariantArgs& va, char* ws, hipStream_t st) {
   using namespace gen;
   T* X = reinterpret_cast<T*>(ws + P.o_x);
   T* QKV = reinterpret_cast<T*>(ws + P.o_qkv);
@@ -415,9 +446,10 @@ lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int
 
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
-    const bool full = !last || hist_out != nullptr;
+    const bool full = !va.links_only && (!last || hist_out != nullptr);
     const int64_t rows_post = full ? R : nlr;
-    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, d} : Xws;
+    const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, d}
+                     : va.links_only ? Rows{X, const_cast<void*>(hist), nlr, d} : Xws;
     const Rows Xfinal = last ? Rows{links_pers, hist_out, nlr, d} : Xws;
     const T* Wqkv = static_cast<const T*>(w[l].w_qkv);
 
@@ -425,7 +457,7 @@ lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int
                        int64_t(0), R, d, Wqkv, nullptr, 3 * d, none, QKVr);
     LIME_CHECK_LAUNCH("qkv projection");
     hipLaunchKernelGGL((xor_attn<T, DH>), dim3(B, H, P.S), blk, 0, st, QKV, Y, part, off, B, ell,
-                       d, H, P.S, P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0);
+                       d, H, P.S, P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0, va.half);
     LIME_CHECK_LAUNCH("xor attention");
     {
       const int64_t n = static_cast<int64_t>(B) * H * ell * DH;
@@ -454,12 +486,13 @@ lime_status_t dispatch_xor_generic(int dh, const XorPlan& P, lime_phi_t phi, flo
                                    int ell, int d, int H, int layers, int d_ff,
                                    const void* links_ctx, const void* hist, const int64_t* off,
                                    int64_t total_N, const lime_layer_weights_t* w,
-                                   void* links_pers, void* hist_out, char* ws, hipStream_t st) {
+                                   void* links_pers, void* hist_out, const VariantArgs& va, char* ws,
+                                   hipStream_t st) {
   switch (dh) {
-    case 16: return run_xor_generic<T, 16>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
-    case 32: return run_xor_generic<T, 32>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
-    case 64: return run_xor_generic<T, 64>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
-    case 128: return run_xor_generic<T, 128>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, ws, st);
+    case 16: return run_xor_generic<T, 16>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, va, ws, st);
+    case 32: return run_xor_generic<T, 32>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, va, ws, st);
+    case 64: return run_xor_generic<T, 64>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, va, ws, st);
+    case 128: return run_xor_generic<T, 128>(P, phi, scale, B, ell, d, H, layers, d_ff, links_ctx, hist, off, total_N, w, links_pers, hist_out, va, ws, st);
   }
   return fail(LIME_ERR_UNSUPPORTED, "d_h %d", dh);
 }
@@ -484,7 +517,10 @@ const char* lime_last_error(void) { return g_err.c_str(); }
 size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
                                    int32_t heads, int32_t d_ff, int64_t total_N, int32_t max_N) {
   if (check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N) != LIME_OK) return 0;
-  return plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N).total;
+  // the matrix-core layout, or the generic one a variant may fall back to
+  const size_t a = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N, true).total;
+  const size_t b = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N, false).total;
+  return a > b ? a : b;
 }
 
 int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
@@ -520,8 +556,39 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
                            int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
                            void* links_pers, void* hist_out, void* workspace,
                            size_t workspace_bytes, void* stream) {
+  return lime_xor_fwd_variant(LIME_VARIANT_XOR, 0, dtype, phi, scale, B, ell, d, heads, layers, d_ff,
+                              links_ctx, hist, hist_offsets, total_N, max_N, w, links_pers, hist_out,
+                              workspace, workspace_bytes, stream);
+}
+
+lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_dtype_t dtype,
+                                   lime_phi_t phi, float scale, int32_t B, int32_t ell, int32_t d,
+                                   int32_t heads, int32_t layers, int32_t d_ff,
+                                   const void* links_ctx, const void* hist,
+                                   const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
+                                   const lime_layer_weights_t* w, void* links_pers,
+                                   void* hist_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   lime_status_t st = check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N);
   if (st != LIME_OK) return st;
+  VariantArgs va;
+  switch (variant) {
+    case LIME_VARIANT_XOR:
+      if (window != 0) return fail(LIME_ERR_INVALID_ARG, "window must be 0 for LIME_VARIANT_XOR");
+      break;
+    case LIME_VARIANT_MHA:
+      if (window != 0) return fail(LIME_ERR_INVALID_ARG, "window must be 0 for LIME_VARIANT_MHA");
+      if (hist_out) return fail(LIME_ERR_INVALID_ARG, "LIME_VARIANT_MHA does not update history rows: hist_out must be NULL");
+      va.links_only = true;
+      break;
+    case LIME_VARIANT_XOR_WINDOW:
+      if (window < 1 || window > 4096)
+        return fail(LIME_ERR_INVALID_ARG, "window must be in [1, 4096] for LIME_VARIANT_XOR_WINDOW (got %d)", window);
+      va.half = window;
+      break;
+    default:
+      return fail(LIME_ERR_INVALID_ARG, "bad variant %d", (int)variant);
+  }
   if (phi != LIME_PHI_SOFTMAX && phi != LIME_PHI_SILU_MEAN) return fail(LIME_ERR_INVALID_ARG, "bad phi %d", (int)phi);
   if (!std::isfinite(scale)) return fail(LIME_ERR_INVALID_ARG, "scale must be finite");
   if (layers < 1) return fail(LIME_ERR_INVALID_ARG, "layers must be >= 1 (got %d)", layers);
@@ -538,7 +605,9 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
         !aligned16(lw.w_up) || !aligned16(lw.w_down))
       return fail(LIME_ERR_INVALID_ARG, "weights of layer %d not 16-byte aligned", l);
   }
-  const XorPlan P = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  // windows wider than the matrix-core kernels serve run on the generic ones
+  const bool allow_mfma = va.half <= mfma_max_half(ell);
+  const XorPlan P = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N, allow_mfma);
   if (!workspace) return fail(LIME_ERR_WORKSPACE, "workspace is null");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(LIME_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -550,12 +619,12 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
   const int dh = d / heads;
   if (P.mfma)
     return dispatch_xor_mfma(P, phi, scale, B, ell, d, layers, links_ctx, hist, hist_offsets, total_N,
-                             max_N, w, links_pers, hist_out, ws, s);
+                             max_N, w, links_pers, hist_out, va, ws, s);
   if (dtype == LIME_F32)
     return dispatch_xor_generic<float>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
-                                       hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
+                                       hist, hist_offsets, total_N, w, links_pers, hist_out, va, ws, s);
   return dispatch_xor_generic<bf16_t>(dh, P, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx,
-                                      hist, hist_offsets, total_N, w, links_pers, hist_out, ws, s);
+                                      hist, hist_offsets, total_N, w, links_pers, hist_out, va, ws, s);
 }
 
 static lime_status_t qk_cache_impl(bool i8, lime_dtype_t dtype, lime_phi_t phi, float scale,

@@ -175,13 +175,60 @@ __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const 
   c.ve[1] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
 }
 
-// E-branch: history rows c0 + [0, 32) attend to the ell links; rows in
-// [lo, hi) are written to Y.
-template <int ELL, int D>
+// LIME-XOR+Window (LIME notes, "Key design 3"): history row j also attends
+// the rows q of its user with 1 <= |q - j| <= half.  For a 32-row chunk at
+// c0 the keys of both 16-row blocks lie in [c0 - ceil8(half), +NKW) when
+// NKW >= 32 + 2 ceil8(half); NKW = 64 serves half <= 16 (ell = 32) and
+// NKW = 96 serves half <= 32 (ell = 64).
+struct WinArgs {
+  int64_t u0 = 0, u1 = 0;  // the user's history rows (history index space)
+  int64_t rmax = 0;        // rows of the QK / packed-V buffers (multiple of 8)
+  int half = 0;            // neighbours on each side
+};
+
+template <int NKW>
+struct WinOps {
+  static constexpr int MBW = NKW / 16, KBW = NKW / 32;
+  bf16x8 kw[MBW];      // A: window keys, rows in the link-block order
+  bf16x8 vw[2][KBW];   // A: window values transposed, k = keys
+};
+template <>
+struct WinOps<0> {};
+
+constexpr int win_nkw(int ell) { return ell == 32 ? 64 : 96; }
+
+__device__ __forceinline__ int64_t win_key0(int64_t c0, int half) { return c0 - ((half + 7) & ~7); }
+
+// Window operands of the chunk at c0 (history index) for head h.  Buffer
+// rows outside [0, rmax) are clamped: such keys are always masked, and
+// every buffer row holds finite values.
+template <int NKW, int D>
+__device__ __forceinline__ void load_window(WinOps<NKW>& w, const bf16_t* QK, const bf16_t* Vp, int64_t hrow,
+                                            int64_t key0, int64_t rmax, int h, int r, int g, int ldqk) {
+#pragma unroll
+  for (int c = 0; c < WinOps<NKW>::MBW; ++c) {
+    const int t = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
+    const int64_t row = clamp64(hrow + key0 + t, 0, rmax - 1);
+    w.kw[c] = ld16(QK + row * ldqk + D + h * 32 + 8 * g);
+  }
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+    for (int kb = 0; kb < WinOps<NKW>::KBW; ++kb) {
+      const int64_t row = clamp64(hrow + key0 + 32 * kb + 8 * g, 0, rmax - 8);
+      w.vw[c2][kb] = ld16(Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
+    }
+}
+
+// E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
+// NKW > 0, to their window); rows in [lo, hi) are written to Y.
+template <int ELL, int D, int NKW = 0>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
-                                         float scale, bool softmax, int r, int g, int ldy = D) {
+                                         float scale, bool softmax, int r, int g, int ldy = D,
+                                         const WinOps<NKW>* wo = nullptr, const WinArgs* wa = nullptr) {
   constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
+  constexpr int NWS = NKW > 0 ? NKW / 4 : 1;  // window scores per lane
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int64_t j = c0 + 16 * rb + r;
@@ -192,10 +239,33 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * c + q] = st[q] * scale;
     }
+    float ws[NWS];
+    int nwin = 0;  // this row's window size (its own row excluded)
+    if constexpr (NKW > 0) {
+      const int64_t key0 = win_key0(c0, wa->half);
+#pragma unroll
+      for (int c = 0; c < NKW / 16; ++c) {
+        const floatx4 sw = mma(wo->kw[c], ci.qe[rb], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t kq = key0 + (c >> 1) * 32 + 8 * g + 4 * (c & 1) + q;
+          const int64_t dist = kq > j ? kq - j : j - kq;
+          const bool ok = kq >= wa->u0 && kq < wa->u1 && dist >= 1 && dist <= wa->half;
+          ws[4 * c + q] = ok ? sw[q] * scale : -INFINITY;
+        }
+      }
+      const int64_t a = j - wa->half > wa->u0 ? j - wa->half : wa->u0;
+      const int64_t e = j + wa->half < wa->u1 - 1 ? j + wa->half : wa->u1 - 1;
+      nwin = e > a ? static_cast<int>(e - a) : 0;
+    }
     if (softmax) {
       float mx = v[0];
 #pragma unroll
       for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
+      if constexpr (NKW > 0) {
+#pragma unroll
+        for (int q = 0; q < NWS; ++q) mx = fmaxf(mx, ws[q]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       float sum = 0.f;
@@ -204,15 +274,30 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
         v[q] = __expf(v[q] - mx);
         sum += v[q];
       }
+      if constexpr (NKW > 0) {
+#pragma unroll
+        for (int q = 0; q < NWS; ++q) {
+          ws[q] = __expf(ws[q] - mx);  // 0 for masked keys
+          sum += ws[q];
+        }
+      }
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       const float inv = 1.f / sum;
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
+      if constexpr (NKW > 0) {
+#pragma unroll
+        for (int q = 0; q < NWS; ++q) ws[q] *= inv;
+      }
     } else {
-      constexpr float inv = 1.f / ELL;
+      const float inv = NKW > 0 ? 1.f / static_cast<float>(ELL + nwin) : 1.f / ELL;
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+      if constexpr (NKW > 0) {
+#pragma unroll
+        for (int q = 0; q < NWS; ++q) ws[q] = ws[q] == -INFINITY ? 0.f : silu_f(ws[q]) * inv;
+      }
     }
     floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -220,6 +305,14 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
       const bf16x8 pb = pack8(v + 8 * kb);
       y0 = mma(o.vlt[0][kb], pb, y0);
       y1 = mma(o.vlt[1][kb], pb, y1);
+    }
+    if constexpr (NKW > 0) {
+#pragma unroll
+      for (int kb = 0; kb < NKW / 32; ++kb) {
+        const bf16x8 pb = pack8(ws + 8 * kb);
+        y0 = mma(wo->vw[0][kb], pb, y0);
+        y1 = mma(wo->vw[1][kb], pb, y1);
+      }
     }
     if (j >= lo && j < hi) {
       const float out[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
@@ -450,13 +543,13 @@ __global__ __launch_bounds__(256) void qkv_proj(Rows X, int64_t R, int64_t R_pad
 // so the waves of a workgroup read the same rows at the same time and share
 // each cache line.  Writes the E-branch rows of Y and the L-branch partial
 // [ell][2 + 32] (max, denominator, acc) of (b, h, s).
-template <int ELL, int H>
+template <int ELL, int H, int NKW = 0>
 __global__ __launch_bounds__(64 * H) void xor_attn(const bf16_t* __restrict__ QK,
                                                    const bf16_t* __restrict__ Vp,
                                                    bf16_t* __restrict__ Y, float* __restrict__ part,
                                                    const int64_t* __restrict__ off, int B, int S,
                                                    int64_t chunk, int64_t total_N, float scale,
-                                                   int phi, int do_e) {
+                                                   int phi, int do_e, int half, int64_t rmax) {
   constexpr int D = 32 * H, MB = ELL / 16;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
@@ -481,7 +574,16 @@ __global__ __launch_bounds__(64 * H) void xor_attn(const bf16_t* __restrict__ QK
   for (; c0 < hi; c0 += 32) {
     // issue the next chunk's loads before computing this one
     if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
-    if (do_e) e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g);
+    if (do_e) {
+      if constexpr (NKW > 0) {
+        WinOps<NKW> wo;
+        load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, 2 * D);
+        const WinArgs wa{u0, u1, rmax, half};
+        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g, D, &wo, &wa);
+      } else {
+        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g);
+      }
+    }
     l_branch<ELL>(st, o, cur, c0, lo, hi, scale, softmax, r, g);
     cur = nxt;
   }
@@ -1003,11 +1105,11 @@ __device__ __forceinline__ const bf16_t* wsrc(const LayerSet& w, int l, int set,
   return w.p[l][m] + static_cast<int64_t>(row % D) * D + 8 * c8;
 }
 
-template <int ELL, int D>
+template <int ELL, int D, int NKW = 0>
 __global__ __launch_bounds__(512) void xor_fwd_resident(
     const bf16_t* __restrict__ links_ctx, const bf16_t* __restrict__ hist,
     const int64_t* __restrict__ off, int64_t total_N, int RT, int layers, LayerSet w, float scale, int phi,
-    bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out) {
+    bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out, int links_only, int half) {
   using C = ResCfg<ELL, D>;
   constexpr int H = D / 32, KB = D / 32, XS = C::XS, NW = C::NW, NT = C::NT;
   constexpr bool WL = C::WL;
@@ -1086,7 +1188,9 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
 
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
-    const bool full = !last || hist_out != nullptr;
+    // history rows get attention and the post block unless nothing can
+    // read them (links-only variant; last layer without hist_out)
+    const bool full = !links_only && (!last || hist_out != nullptr);
     const bf16_t* lq = WL ? Wq : w.p[l][0];
     const int ldd = WL ? LDW : D;
     // ---- LN + QKV: items (chunk, part)
@@ -1143,7 +1247,14 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       } else {
         ChunkOps ci;
         load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g, LQK);
-        e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY);
+        if constexpr (NKW > 0) {
+          WinOps<NKW> wo;
+          load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, LQK);
+          const WinArgs wa{0, n, RT, half};
+          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY, &wo, &wa);
+        } else {
+          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY);
+        }
       }
     }
     __syncthreads();

@@ -2,7 +2,8 @@
  * lime.h — C ABI of the LIME inference hot path on AMD Instinct MI355X
  * (gfx950).
  *
- * Three operations, following the LIME pages:
+ * Three operations, following the LIME pages (plus the int8, uncached and
+ * user-side variant forms declared further down):
  *
  *   lime_xor_fwd        user side: stacked LIME-XOR layers over the context
  *                       links L^C and the user history E, giving the
@@ -67,6 +68,13 @@ typedef enum { LIME_F32 = 0, LIME_BF16 = 1 } lime_dtype_t;
 
 typedef enum { LIME_PHI_SOFTMAX = 0, LIME_PHI_SILU_MEAN = 1 } lime_phi_t;
 
+/* User-side variants (see lime_xor_fwd_variant). */
+typedef enum {
+  LIME_VARIANT_XOR = 0,        /* LIME-XOR: both cross attentions          */
+  LIME_VARIANT_MHA = 1,        /* LIME-MHA: links -> history only          */
+  LIME_VARIANT_XOR_WINDOW = 2  /* LIME-XOR+Window: XOR plus a local window */
+} lime_variant_t;
+
 /* Weights of one LIME-XOR layer, device pointers, all in [out, in] row-major
  * layout (y = x . W^T), element type = the call's dtype:
  *   w_qkv  [3d, d]   rows 0..d-1 give Q, d..2d-1 give K, 2d..3d-1 give V
@@ -127,6 +135,37 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale,
                            const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
                            const lime_layer_weights_t* w, void* links_pers, void* hist_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The user-side encoder in one of the pages' variants.  Arguments,
+ * layouts, workspace (lime_xor_fwd_workspace_size) and errors as
+ * lime_xor_fwd, plus:
+ *   variant  LIME_VARIANT_XOR: exactly lime_xor_fwd.  `window` must be 0.
+ *            LIME_VARIANT_MHA: LIME-MHA (LIME summary page, Fig. 2 and the
+ *              scaling paragraph of the LIME notes' experiments; the
+ *              notes' results table calls it single-layer decoupled): only
+ *              the links -> history cross attention runs.  History rows
+ *              are never updated; every layer reads the input E, and the
+ *              link rows go through W_o, residual and gated MLP as in
+ *              lime_xor_fwd.  `window` must be 0 and hist_out NULL.
+ *            LIME_VARIANT_XOR_WINDOW: LIME-XOR+Window (LIME notes, "Key
+ *              design 3"; Table 13): history row p of a user attends its
+ *              ell links AND the history rows q of the same user with
+ *              1 <= |p - q| <= window (neighbours before and after, itself
+ *              excluded), under one phi over the union; with silu_mean the
+ *              normaliser counts the union.  Link rows are unchanged.
+ *   window   neighbours on each side, 1 <= window <= 4096 for
+ *            LIME_VARIANT_XOR_WINDOW (window = ell / 2 gives each history
+ *            row 2*ell keys, the context size the notes state).
+ * Windows up to 16 (ell = 32) or 32 (ell = 64) run on the matrix-core
+ * kernels; larger ones on the generic kernels.                             */
+lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_dtype_t dtype,
+                                   lime_phi_t phi, float scale, int32_t B, int32_t ell, int32_t d,
+                                   int32_t heads, int32_t layers, int32_t d_ff,
+                                   const void* links_ctx, const void* hist,
+                                   const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
+                                   const lime_layer_weights_t* w, void* links_pers,
+                                   void* hist_out, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Launch plan lime_xor_fwd would use for these sizes (host only, no GPU
  * work): returns the number of kernel launches of one call (0 on invalid

@@ -86,6 +86,30 @@ def test_xor_fwd_rejects(L, kw, code):
     assert L.lib.lime_last_error().decode() != ""
 
 
+def _call_variant(L, variant, window, a):
+    arr = (L.LayerWeights * max(1, a["layers"]))()
+    for i in range(max(1, a["layers"])):
+        arr[i] = L.LayerWeights(P, P, P, P, P)
+    a["w"] = arr
+    return L.lib.lime_xor_fwd_variant(variant, window, a["dtype"], a["phi"], a["scale"], a["B"], a["ell"],
+                                      a["d"], a["heads"], a["layers"], a["d_ff"], a["links_ctx"], a["hist"],
+                                      a["off"], a["total_N"], a["max_N"], a["w"], a["lp"], a["ho"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("variant,window,kw,code", [
+    (3, 0, {}, 1), (-1, 0, {}, 1),            # bad variant
+    (0, 4, {}, 1), (1, 2, {}, 1),             # window given where none applies
+    (1, 0, dict(ho=P), 1),                    # LIME-MHA never writes history rows
+    (2, 0, {}, 1), (2, -3, {}, 1), (2, 5000, {}, 1),
+    (2, 16, dict(ws=None), 3), (1, 0, dict(ws_bytes=64), 3), (2, 16, dict(d=65), 1),
+])
+def test_xor_fwd_variant_rejects(L, variant, window, kw, code):
+    a = _xor_args(**kw)
+    assert _call_variant(L, variant, window, a) == code
+    assert L.lib.lime_last_error().decode() != ""
+
+
 def test_xor_fwd_null_weight(L):
     arr = (L.LayerWeights * 2)()
     arr[0] = L.LayerWeights(P, P, P, P, P)
