@@ -28,6 +28,35 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
+// Workgroup barrier for kernels whose waves share data through LDS only:
+// it orders LDS accesses and waits for them, but leaves global loads
+// (register prefetches) and global stores in flight across the barrier,
+// where __syncthreads() would wait for every outstanding memory operation.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48), the lane groups that share a row of an MFMA operand.  The gfx950
+// row-swap instructions give each pair's two values to both lanes, so a
+// step is one VALU op instead of an LDS permute round trip; the adds pair
+// the same values as a butterfly of xor-shuffles, so results are equal.
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ floatx4 mma(const bf16x8& a, const bf16x8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -91,8 +120,7 @@ __device__ __forceinline__ float quantize_i8(const float* v, int8_t* q) {
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = rows_max(m);
   const float inv = m > 0.f ? 127.f / m : 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -146,7 +174,7 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
       const int row = e / C::CPR, col = e % C::CPR;
       *reinterpret_cast<uint4*>(lds + row * C::STRIDE + col * 16) = pf[i];
     }
-    __syncthreads();
+    lds_barrier();
     const int64_t nxt = tile + gridDim.x;
     if (nxt < ntiles) gload(nxt);
 
@@ -176,16 +204,14 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
           float mx = v[0];
 #pragma unroll
           for (int q = 1; q < 4 * C::MB; ++q) mx = fmaxf(mx, v[q]);
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mx = rows_max(mx);
           float s = 0.f;
 #pragma unroll
           for (int q = 0; q < 4 * C::MB; ++q) {
             v[q] = __expf(v[q] - mx);
             s += v[q];
           }
-          s += __shfl_xor(s, 16);
-          s += __shfl_xor(s, 32);
+          s = rows_sum(s);
           const float inv = 1.f / s;
 #pragma unroll
           for (int q = 0; q < 4 * C::MB; ++q) v[q] *= inv;
@@ -219,7 +245,7 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -270,7 +296,7 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
   const bool in_lds = B <= C::MAXB;
   if (in_lds)
     for (int i = tid; i <= B; i += 256) off_s[i] = off_g[i];
-  __syncthreads();
+  lds_barrier();
   const int64_t* off = in_lds ? off_s : off_g;
 
   const int64_t ntiles = (total_M + 15) >> 4;
@@ -394,7 +420,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
       const int row = e / (D / 8), c8 = e % (D / 8);
       *reinterpret_cast<bf16x8*>(ks + row * LDK + 8 * c8) = ld16(keys + static_cast<int64_t>(row) * D + 8 * c8);
     }
-    __syncthreads();
+    lds_barrier();
     Ks = ks;
     ldk = LDK;
   } else {
@@ -444,16 +470,14 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
         float mx = v[0];
 #pragma unroll
         for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = rows_max(mx);
         float sum = 0.f;
 #pragma unroll
         for (int q = 0; q < 4 * MB; ++q) {
           v[q] = __expf(v[q] - mx);
           sum += v[q];
         }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
+        sum = rows_sum(sum);
         const float inv = 1.f / sum;
 #pragma unroll
         for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;

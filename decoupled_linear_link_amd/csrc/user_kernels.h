@@ -39,8 +39,7 @@ __device__ __forceinline__ float tree_sum(const float* v) {
 template <int N>
 __device__ __forceinline__ void ln_rows(float* v, int D) {
   float s = tree_sum<N>(v);
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
+  s = rows_sum(s);
   const float mu = s / D;
   float t[N];
 #pragma unroll
@@ -49,8 +48,7 @@ __device__ __forceinline__ void ln_rows(float* v, int D) {
     t[i] = u * u;
   }
   float q = tree_sum<N>(t);
-  q += __shfl_xor(q, 16);
-  q += __shfl_xor(q, 32);
+  q = rows_sum(q);
   const float rs = rsqrtf(q / D + 1e-5f);
 #pragma unroll
   for (int i = 0; i < N; ++i) v[i] = (v[i] - mu) * rs;
@@ -266,8 +264,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
 #pragma unroll
         for (int q = 0; q < NWS; ++q) mx = fmaxf(mx, ws[q]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows_max(mx);
       float sum = 0.f;
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) {
@@ -281,8 +278,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
           sum += ws[q];
         }
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = rows_sum(sum);
       const float inv = 1.f / sum;
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
@@ -367,8 +363,7 @@ __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o,
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (valid[q]) mc = fmaxf(mc, p[q]);
-      mc = fmaxf(mc, __shfl_xor(mc, 16));
-      mc = fmaxf(mc, __shfl_xor(mc, 32));
+      mc = rows_max(mc);
       const float mn = fmaxf(st.m[nb], mc);
       const float alpha = (st.m[nb] == -INFINITY) ? 0.f : __expf(st.m[nb] - mn);
       float ls = 0.f;
@@ -377,8 +372,7 @@ __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o,
         p[q] = valid[q] ? __expf(p[q] - mn) : 0.f;
         ls += p[q];
       }
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
+      ls = rows_sum(ls);
       st.l[nb] = st.l[nb] * alpha + ls;
       st.m[nb] = mn;
       // acc rows are links 16*nb + 4*g + jj; their factor sits in lane 4*g + jj
@@ -672,7 +666,7 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
   stage_rows(Wl, W, 3 * D, D, threadIdx.x, NW * 64);
-  __syncthreads();
+  lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int64_t nblk = R_pad / 32;
@@ -728,7 +722,7 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Row
   stage_rows(Wgl, Wg, DFF, D, threadIdx.x, NW * 64);
   stage_rows(Wul, Wu, DFF, D, threadIdx.x, NW * 64);
   stage_rows(Wdl, Wd, D, DFF, threadIdx.x, NW * 64);
-  __syncthreads();
+  lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int64_t nblk = (nrows + RPW - 1) / RPW;
@@ -827,7 +821,7 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
   bf16x8 reg[C::CPT];
   chunk_load<D>(reg, W, 0, tid);
   chunk_store<D>(reg, buf0, tid);
-  __syncthreads();
+  lds_barrier();
   bf16x8 hb[2][KB];
   bool active = false;
   int64_t row0 = 0;
@@ -905,7 +899,7 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
       }
     }
     if (more) chunk_store<D>(reg, buf0 + ((c + 1) & 1) * (CR * LDW), tid);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -965,7 +959,7 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
   bf16x8 reg[C::CPT];
   load_chunk_regs(reg, 0);
   store_regs(reg, buf0);
-  __syncthreads();
+  lds_barrier();
   for (int64_t it = 0; it < my_tiles; ++it) {
     const int64_t tile = blockIdx.x + it * gridDim.x;
     const int64_t row = tile * 16 * NW + 16 * w + r;
@@ -1043,7 +1037,7 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
         mb[k - 4] = pack8(v);
       }
       if (more) store_regs(reg, buf0 + ((k + 1) & 1) * (CR * LDW));
-      __syncthreads();
+      lds_barrier();
     }
     if (rowok) {
       bf16_t* orow = row_out<bf16_t>(Out, row);
@@ -1184,7 +1178,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
   }
   store_set(0);
   store_set(1);
-  __syncthreads();
+  lds_barrier();
 
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
@@ -1213,7 +1207,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       if (it & 1) v_part<D>(hb, lq + opaque_zero(), ldd, Vps, row0, r, g);
       else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, LQK);
     }
-    __syncthreads();
+    lds_barrier();
     // ---- attention: items = per head, the L-branch and the E-branch chunks
     if (!last) store_set(0);  // w_qkv region is free: next layer's projection
     const int echunks = full ? (n + 31) / 32 : 0;
@@ -1257,7 +1251,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- post-attention block per 16-row block
     if (!last) load_set(l + 1, 1);
     const bf16_t* lo_w = WL ? Wp : w.p[l][1];
@@ -1292,7 +1286,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
           for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[0][8 * kb]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (!last) {
       store_set(1);  // post-weight region is free: next layer's post weights
       // visible before the next post phase: two barriers follow
