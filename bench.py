@@ -258,6 +258,28 @@ def main():
                          "GB/s": round(ex_bytes[k] / (t_ms * 1e-3) / 1e9, 1),
                          "per_s": round((w.n_items if "build" in k else n_cand) / (t_ms * 1e-3), 1)}
 
+    # achievable HBM bandwidth next to the 8 TB/s peak: a plain 1 GiB
+    # device-to-device copy (read + write bytes counted), timed like the calls
+    # (skipped in counter-calibration runs, whose only copies must be the
+    # calibration copies below)
+    copy_gbs = None
+    if not args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+    if a["bound"] == "hbm" and copy_gbs:
+        roofline["achievable_copy_GBs"] = round(copy_gbs, 1)
+        roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the HBM byte counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -292,6 +314,7 @@ def main():
         "xor_fwd_plan": plan,
         "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
         "roofline": roofline,
+        "hbm_copy_GBs": round(copy_gbs, 1) if copy_gbs else None,
     }
 
     if not args.no_cpu_baseline:

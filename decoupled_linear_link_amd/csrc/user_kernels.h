@@ -1068,6 +1068,20 @@ struct LayerSet {
   const bf16_t* p[RES_MAX_LAYERS][5];
 };
 
+// 8 consecutive floats of an LDS row as two 16-byte accesses (the row
+// strides keep every such piece 16-byte aligned)
+__device__ __forceinline__ void lds_ld8f(const float* p, float* v) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void lds_st8f(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 template <int ELL, int D>
 struct ResCfg {
   static constexpr int NW = 8;
@@ -1173,8 +1187,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = static_cast<float>(x[q]);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) Xs[row * XS + 8 * c8 + q] = v[q];
+    lds_st8f(Xs + row * XS + 8 * c8, v);
   }
   store_set(0);
   store_set(1);
@@ -1197,9 +1210,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         const int row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
         float v[8 * KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int q = 0; q < 8; ++q) v[8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
+        for (int kb = 0; kb < KB; ++kb) lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, v + 8 * kb);
         ln_rows<8 * KB>(v, D);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
@@ -1267,17 +1278,19 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         yb[0][kb] = row < rows ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
-#pragma unroll
-        for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] = Xs[row * XS + kb * 32 + 8 * g + q];
+        lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
       }
       const int z = opaque_zero();
       post_rows<D, D, 1>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
       const bool real = row < rows;
       if (!last) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+          float o[8];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) Xs[row * XS + kb * 32 + 8 * g + q] = real ? x1[0][8 * kb + q] : 0.f;
+          for (int q = 0; q < 8; ++q) o[q] = real ? x1[0][8 * kb + q] : 0.f;
+          lds_st8f(Xs + row * XS + kb * 32 + 8 * g, o);
+        }
       } else if (real) {
         bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
                                 : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
