@@ -65,6 +65,15 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// 4 floats as bf16 (8 bytes)
+__device__ __forceinline__ void st4(bf16_t* p, const floatx4& v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(v[j]);
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll

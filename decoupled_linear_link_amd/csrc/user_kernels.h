@@ -121,6 +121,43 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
   v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
+// LN + QKV of one 16-row block whose lane (r, g) holds row row0 + r,
+// columns 32 kb + 8 g .. +8 (the post block's layout) in x.  Q|K land as
+// 16-byte row pieces; V (operands swapped) as 8-byte pieces of 4 rows of
+// one column in the packed layout (row0 a multiple of 8).
+template <int D>
+__device__ __forceinline__ void qkv_rows16(const float* x, const bf16_t* __restrict__ W, int ldw,
+                                           bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk) {
+  constexpr int KB = D / 32;
+  float v[8 * KB];
+#pragma unroll
+  for (int i = 0; i < 8 * KB; ++i) v[i] = x[i];
+  ln_rows<8 * KB>(v, D);
+  bf16x8 hb[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) hb[kb] = pack8(v + 8 * kb);
+#pragma unroll 2
+  for (int p = 0; p < 2 * D / 32; ++p) {
+    floatx4 acc[2] = {};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16_t* wr = W + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[c] = mma(ld16(wr + kb * 32), hb[kb], acc[c]);
+    }
+    const float o[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+    st8(QK + (row0 + r) * ldqk + 32 * p + 8 * g, o);
+  }
+#pragma unroll 2
+  for (int nn = 0; nn < D / 16; ++nn) {
+    const bf16_t* wr = W + static_cast<int64_t>(2 * D + 16 * nn + r) * ldw + 8 * g;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) acc = mma(hb[kb], ld16(wr + kb * 32), acc);
+    st4(Vp + vp_index(row0 + 4 * g, 16 * nn + r, D), acc);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // XOR attention pieces for one (user, head h).  Link rows start at `lrow`,
 // history row j is row `hrow + j` of QK / Vp / Y.
@@ -1193,15 +1230,12 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
   store_set(1);
   lds_barrier();
 
-  for (int l = 0; l < layers; ++l) {
-    const bool last = (l == layers - 1);
-    // history rows get attention and the post block unless nothing can
-    // read them (links-only variant; last layer without hist_out)
-    const bool full = !links_only && (!last || hist_out != nullptr);
-    const bf16_t* lq = WL ? Wq : w.p[l][0];
-    const int ldd = WL ? LDW : D;
-    // ---- LN + QKV: items (chunk, part)
-    if (!last) load_set(l + 1, 0);
+  const int ldd = WL ? LDW : D;
+  // ---- layer 0: LN + QKV over chunk items (chunk, part); later layers get
+  // their projection from the previous layer's post phase
+  {
+    if (layers > 1) load_set(1, 0);
+    const bf16_t* lq = WL ? Wq : w.p[0][0];
     for (int it = wv; it < 2 * nchunks; it += NW) {
       const int row0 = (it >> 1) * 32;
       bf16x8 hb[2][KB];
@@ -1219,8 +1253,18 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, LQK);
     }
     lds_barrier();
-    // ---- attention: items = per head, the L-branch and the E-branch chunks
-    if (!last) store_set(0);  // w_qkv region is free: next layer's projection
+  }
+
+  for (int l = 0; l < layers; ++l) {
+    const bool last = (l == layers - 1);
+    // history rows get attention and the post block unless nothing can
+    // read them (links-only variant; last layer without hist_out)
+    const bool full = !links_only && (!last || hist_out != nullptr);
+    // ---- attention: items = per head, the L-branch and the E-branch chunks.
+    // The weight regions are free here: stage layer l's post weights (from
+    // layer 1 on) and layer l+1's projection weights.
+    if (l > 0) store_set(1);
+    if (!last) store_set(0);
     const int echunks = full ? (n + 31) / 32 : 0;
     const int items = H * (1 + echunks);
     for (int it = wv; it < items; it += NW) {
@@ -1263,35 +1307,43 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       }
     }
     lds_barrier();
-    // ---- post-attention block per 16-row block
-    if (!last) load_set(l + 1, 1);
+    // ---- post-attention block per 16-row block, and in every layer but the
+    // last the next layer's LN + QKV of the same rows, straight from the
+    // registers (rows the post block skips are re-projected as they are)
+    if (!last) {
+      load_set(l + 1, 1);
+      if (l + 2 < layers) load_set(l + 2, 0);
+    }
     const bf16_t* lo_w = WL ? Wp : w.p[l][1];
     const bf16_t* lg_w = WL ? Wp + D * LDW : w.p[l][2];
     const bf16_t* lu_w = WL ? Wp + 2 * D * LDW : w.p[l][3];
     const bf16_t* ld_w = WL ? Wp + 3 * D * LDW : w.p[l][4];
-    const int prow_end = full ? rows : ELL;
-    const int pblocks = (prow_end + 15) / 16;
+    const bf16_t* lq_next = last ? nullptr : (WL ? Wq : w.p[l + 1][0]);
+    const int prow_end = full ? rows : ELL;  // a multiple of 16 when not every row
+    const int pblocks = ((last ? prow_end : rows) + 15) / 16;
     for (int it = wv; it < pblocks; it += NW) {
       const int row = it * 16 + r;
-      bf16x8 yb[1][KB];
+      const bool real = row < rows;
+      const bool do_post = it * 16 < prow_end;
       float x1[1][D / 4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        yb[0][kb] = row < rows ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
-        lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
+      for (int kb = 0; kb < KB; ++kb) lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
+      if (do_post) {
+        bf16x8 yb[1][KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) yb[0][kb] = real ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
+        const int z = opaque_zero();
+        post_rows<D, D, 1>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) x1[0][i] = real ? x1[0][i] : 0.f;
       }
-      const int z = opaque_zero();
-      post_rows<D, D, 1>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
-      const bool real = row < rows;
       if (!last) {
+        if (do_post) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          float o[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) o[q] = real ? x1[0][8 * kb + q] : 0.f;
-          lds_st8f(Xs + row * XS + kb * 32 + 8 * g, o);
+          for (int kb = 0; kb < KB; ++kb) lds_st8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
         }
-      } else if (real) {
+        qkv_rows16<D>(x1[0], lq_next + opaque_zero(), ldd, QKs, Vps, it * 16, r, g, LQK);
+      } else if (do_post && real) {
         bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
                                 : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
         if (dst)
@@ -1300,10 +1352,6 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       }
     }
     lds_barrier();
-    if (!last) {
-      store_set(1);  // post-weight region is free: next layer's post weights
-      // visible before the next post phase: two barriers follow
-    }
   }
 }
 
