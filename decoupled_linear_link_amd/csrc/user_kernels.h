@@ -121,40 +121,56 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
   v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
-// LN + QKV of one 16-row block whose lane (r, g) holds row row0 + r,
-// columns 32 kb + 8 g .. +8 (the post block's layout) in x.  Q|K land as
-// 16-byte row pieces; V (operands swapped) as 8-byte pieces of 4 rows of
-// one column in the packed layout (row0 a multiple of 8).
-template <int D>
-__device__ __forceinline__ void qkv_rows16(const float* x, const bf16_t* __restrict__ W, int ldw,
-                                           bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk) {
+// LN + QKV of RB 16-row blocks: lane (r, g) of block rb holds row
+// row0 + 16 rb + r, columns 32 kb + 8 g .. +8 (the post block's layout) in
+// x[rb].  Q|K land as 16-byte row pieces; V (operands swapped) as 8-byte
+// pieces of 4 rows of one column in the packed layout (row0 a multiple of 8).
+template <int D, int RB>
+__device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16_t* __restrict__ W, int ldw,
+                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk) {
   constexpr int KB = D / 32;
-  float v[8 * KB];
+  bf16x8 hb[RB][KB];
 #pragma unroll
-  for (int i = 0; i < 8 * KB; ++i) v[i] = x[i];
-  ln_rows<8 * KB>(v, D);
-  bf16x8 hb[KB];
+  for (int rb = 0; rb < RB; ++rb) {
+    float v[8 * KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) hb[kb] = pack8(v + 8 * kb);
+    for (int i = 0; i < 8 * KB; ++i) v[i] = x[rb][i];
+    ln_rows<8 * KB>(v, D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+  }
 #pragma unroll 2
   for (int p = 0; p < 2 * D / 32; ++p) {
-    floatx4 acc[2] = {};
+    floatx4 acc[2][RB] = {};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const bf16_t* wr = W + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc[c] = mma(ld16(wr + kb * 32), hb[kb], acc[c]);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ld16(wr + kb * 32);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, hb[rb][kb], acc[c][rb]);
+      }
     }
-    const float o[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
-    st8(QK + (row0 + r) * ldqk + 32 * p + 8 * g, o);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float o[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
+                          acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+      st8(QK + (row0 + 16 * rb + r) * ldqk + 32 * p + 8 * g, o);
+    }
   }
 #pragma unroll 2
   for (int nn = 0; nn < D / 16; ++nn) {
     const bf16_t* wr = W + static_cast<int64_t>(2 * D + 16 * nn + r) * ldw + 8 * g;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[RB] = {};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) acc = mma(hb[kb], ld16(wr + kb * 32), acc);
-    st4(Vp + vp_index(row0 + 4 * g, 16 * nn + r, D), acc);
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 b = ld16(wr + kb * 32);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = mma(hb[rb][kb], b, acc[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) st4(Vp + vp_index(row0 + 16 * rb + 4 * g, 16 * nn + r, D), acc[rb]);
   }
 }
 
@@ -1129,6 +1145,7 @@ struct ResCfg {
   static constexpr int LQK = 2 * D + 8, LY = D + 8;
   static constexpr size_t bytes_per_row = static_cast<size_t>(XS) * 4 + LQK * 2 + D * 2 + LY * 2;
   static constexpr bool WL = D <= 64;  // weights staged in LDS
+  static constexpr int PRB = 1;        // 16-row blocks per post-phase item
   static constexpr int LDW = D + 8;
   static constexpr int QCH = 3 * D * (D / 8);  // 16-byte chunks of w_qkv
   static constexpr int PCH = 4 * D * (D / 8);  // 16-byte chunks of the post weights
@@ -1319,36 +1336,57 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     const bf16_t* lu_w = WL ? Wp + 2 * D * LDW : w.p[l][3];
     const bf16_t* ld_w = WL ? Wp + 3 * D * LDW : w.p[l][4];
     const bf16_t* lq_next = last ? nullptr : (WL ? Wq : w.p[l + 1][0]);
-    const int prow_end = full ? rows : ELL;  // a multiple of 16 when not every row
-    const int pblocks = ((last ? prow_end : rows) + 15) / 16;
-    for (int it = wv; it < pblocks; it += NW) {
-      const int row = it * 16 + r;
-      const bool real = row < rows;
-      const bool do_post = it * 16 < prow_end;
-      float x1[1][D / 4];
+    constexpr int PRB = ResCfg<ELL, D>::PRB;  // 16-row blocks per post item
+    constexpr int PR = 16 * PRB;
+    const int prow_end = full ? rows : ELL;  // a multiple of PR when not every row
+    const int pitems = ((last ? prow_end : rows) + PR - 1) / PR;
+    for (int it = wv; it < pitems; it += NW) {
+      const int row0 = it * PR;
+      const bool do_post = row0 < prow_end;
+      float x1[PRB][D / 4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
+      for (int rb = 0; rb < PRB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          lds_ld8f(Xs + (row0 + 16 * rb + r) * XS + kb * 32 + 8 * g, &x1[rb][8 * kb]);
       if (do_post) {
-        bf16x8 yb[1][KB];
+        bf16x8 yb[PRB][KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) yb[0][kb] = real ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
+        for (int rb = 0; rb < PRB; ++rb) {
+          const int row = row0 + 16 * rb + r;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) yb[rb][kb] = row < rows ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
+        }
         const int z = opaque_zero();
-        post_rows<D, D, 1>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
+        post_rows<D, D, PRB>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
 #pragma unroll
-        for (int i = 0; i < D / 4; ++i) x1[0][i] = real ? x1[0][i] : 0.f;
+        for (int rb = 0; rb < PRB; ++rb) {
+          const bool real = row0 + 16 * rb + r < rows;
+#pragma unroll
+          for (int i = 0; i < D / 4; ++i) x1[rb][i] = real ? x1[rb][i] : 0.f;
+        }
       }
       if (!last) {
         if (do_post) {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) lds_st8f(Xs + row * XS + kb * 32 + 8 * g, &x1[0][8 * kb]);
-        }
-        qkv_rows16<D>(x1[0], lq_next + opaque_zero(), ldd, QKs, Vps, it * 16, r, g, LQK);
-      } else if (do_post && real) {
-        bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
-                                : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
-        if (dst)
+          for (int rb = 0; rb < PRB; ++rb)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[0][8 * kb]);
+            for (int kb = 0; kb < KB; ++kb)
+              lds_st8f(Xs + (row0 + 16 * rb + r) * XS + kb * 32 + 8 * g, &x1[rb][8 * kb]);
+        }
+        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, LQK);
+      } else if (do_post) {
+#pragma unroll
+        for (int rb = 0; rb < PRB; ++rb) {
+          const int row = row0 + 16 * rb + r;
+          if (row < rows) {
+            bf16_t* dst = row < ELL ? links_pers + (static_cast<int64_t>(b) * ELL + row) * D
+                                    : (hist_out ? hist_out + (u0 + row - ELL) * D : nullptr);
+            if (dst)
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[rb][8 * kb]);
+          }
+        }
       }
     }
     lds_barrier();
