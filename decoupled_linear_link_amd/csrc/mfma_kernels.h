@@ -139,6 +139,65 @@ __device__ __forceinline__ float quantize_i8(const float* v, int8_t* q) {
   return m / 127.f;
 }
 
+// phi over the ell links of one (item, head) whose scores a lane group
+// holds (lane (r, g): item r, links 4 MB g .. +4 MB in acc[c][j], link order
+// of the cache kernels' A operands), then the store of the lane's links:
+// bf16 weights, or int8 codes plus the row's float32 scale.
+template <int ELL, bool I8>
+__device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], float scale, int phi, int64_t item,
+                                               int64_t n_items, int H, int head, void* __restrict__ cache_out,
+                                               float* __restrict__ qscale, int g) {
+  constexpr int MB = ELL / 16;
+  float v[4 * MB];
+#pragma unroll
+  for (int c = 0; c < MB; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * c + j] = acc[c][j] * scale;
+  if (phi == PHI_SOFTMAX) {
+    float mx = v[0];
+#pragma unroll
+    for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
+    mx = rows_max(mx);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4 * MB; ++q) {
+      v[q] = __expf(v[q] - mx);
+      s += v[q];
+    }
+    s = rows_sum(s);
+    const float inv = 1.f / s;
+#pragma unroll
+    for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
+  } else {
+    constexpr float inv = 1.f / ELL;
+#pragma unroll
+    for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+  }
+  if constexpr (I8) {
+    int8_t qv[4 * MB];
+    const float sc = quantize_i8<4 * MB>(v, qv);
+    if (item < n_items) {
+      int8_t* o = static_cast<int8_t*>(cache_out) + (item * H + head) * ELL + g * 4 * MB;
+#pragma unroll
+      for (int q = 0; q < MB / 2; ++q) {
+        uint2 pk;
+        pk.x = (uint32_t)(uint8_t)qv[8 * q] | ((uint32_t)(uint8_t)qv[8 * q + 1] << 8) |
+               ((uint32_t)(uint8_t)qv[8 * q + 2] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 3] << 24);
+        pk.y = (uint32_t)(uint8_t)qv[8 * q + 4] | ((uint32_t)(uint8_t)qv[8 * q + 5] << 8) |
+               ((uint32_t)(uint8_t)qv[8 * q + 6] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 7] << 24);
+        *reinterpret_cast<uint2*>(o + 8 * q) = pk;
+      }
+      if (g == 0) qscale[item * H + head] = sc;
+    }
+  } else {
+    if (item < n_items) {
+      bf16_t* o = static_cast<bf16_t*>(cache_out) + (item * H + head) * ELL + g * 4 * MB;
+#pragma unroll
+      for (int q = 0; q < MB / 2; ++q) st8(o + 8 * q, v + 8 * q);
+    }
+  }
+}
+
 template <int ELL, int D, int H, bool I8 = false>
 __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
     const bf16_t* __restrict__ items, const bf16_t* __restrict__ keys, void* __restrict__ cache_out,
@@ -204,54 +263,7 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) acc[c] = mma(a[hh][c][kb], b[kb], acc[c]);
         }
-        float v[4 * C::MB];
-#pragma unroll
-        for (int c = 0; c < C::MB; ++c)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[4 * c + j] = acc[c][j] * scale;
-        if (phi == PHI_SOFTMAX) {
-          float mx = v[0];
-#pragma unroll
-          for (int q = 1; q < 4 * C::MB; ++q) mx = fmaxf(mx, v[q]);
-          mx = rows_max(mx);
-          float s = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4 * C::MB; ++q) {
-            v[q] = __expf(v[q] - mx);
-            s += v[q];
-          }
-          s = rows_sum(s);
-          const float inv = 1.f / s;
-#pragma unroll
-          for (int q = 0; q < 4 * C::MB; ++q) v[q] *= inv;
-        } else {
-          constexpr float inv = 1.f / ELL;
-#pragma unroll
-          for (int q = 0; q < 4 * C::MB; ++q) v[q] = silu_f(v[q]) * inv;
-        }
-        if constexpr (I8) {
-          int8_t qv[4 * C::MB];
-          const float sc = quantize_i8<4 * C::MB>(v, qv);
-          if (item < n_items) {
-            int8_t* o = static_cast<int8_t*>(cache_out) + (item * H + head0 + hh) * ELL + g * 4 * C::MB;
-#pragma unroll
-            for (int q = 0; q < C::MB / 2; ++q) {
-              uint2 pk;
-              pk.x = (uint32_t)(uint8_t)qv[8 * q] | ((uint32_t)(uint8_t)qv[8 * q + 1] << 8) |
-                     ((uint32_t)(uint8_t)qv[8 * q + 2] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 3] << 24);
-              pk.y = (uint32_t)(uint8_t)qv[8 * q + 4] | ((uint32_t)(uint8_t)qv[8 * q + 5] << 8) |
-                     ((uint32_t)(uint8_t)qv[8 * q + 6] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 7] << 24);
-              *reinterpret_cast<uint2*>(o + 8 * q) = pk;
-            }
-            if (g == 0) qscale[item * H + head0 + hh] = sc;
-          }
-        } else {
-          if (item < n_items) {
-            bf16_t* o = static_cast<bf16_t*>(cache_out) + (item * H + head0 + hh) * ELL + g * 4 * C::MB;
-#pragma unroll
-            for (int q = 0; q < C::MB / 2; ++q) st8(o + 8 * q, v + 8 * q);
-          }
-        }
+        cache_epilogue<ELL, I8>(acc, scale, phi, item, n_items, H, head0 + hh, cache_out, qscale, g);
       }
     }
     lds_barrier();
