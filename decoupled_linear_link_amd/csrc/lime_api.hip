@@ -354,9 +354,12 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
     {
       const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * P.S));
+      // the windowed form runs at most 4 heads per workgroup (registers)
+      constexpr int HBW = H > 4 ? 4 : H;
+      const dim3 grid_w(static_cast<unsigned>(static_cast<int64_t>(B) * P.S * (H / HBW)));
       if (va.half > 0 && full)
-        hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL)>), grid, dim3(64 * H), 0, st, QK, Vp, Y,
-                           part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi), 1, va.half,
+        hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
+                           Vp, Y, part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi), 1, va.half,
                            P.R_pad);
       else
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, B, P.S,

@@ -232,16 +232,17 @@ __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const 
 // NKW >= 32 + 2 ceil8(half); NKW = 64 serves half <= 16 (ell = 32) and
 // NKW = 96 serves half <= 32 (ell = 64).
 struct WinArgs {
-  int64_t u0 = 0, u1 = 0;  // the user's history rows (history index space)
-  int64_t rmax = 0;        // rows of the QK / packed-V buffers (multiple of 8)
-  int half = 0;            // neighbours on each side
+  int64_t u0 = 0, u1 = 0;        // the user's history rows (history index space)
+  int64_t rmax = 0;              // rows of the QK / packed-V buffers (multiple of 8)
+  int half = 0;                  // neighbours on each side
+  const bf16_t* Vp = nullptr;    // packed V, read for the value product
+  int64_t hrow = 0;              // buffer row of history row 0
 };
 
 template <int NKW>
 struct WinOps {
   static constexpr int MBW = NKW / 16, KBW = NKW / 32;
   bf16x8 kw[MBW];      // A: window keys, rows in the link-block order
-  bf16x8 vw[2][KBW];   // A: window values transposed, k = keys
 };
 template <>
 struct WinOps<0> {};
@@ -262,13 +263,15 @@ __device__ __forceinline__ void load_window(WinOps<NKW>& w, const bf16_t* QK, co
     const int64_t row = clamp64(hrow + key0 + t, 0, rmax - 1);
     w.kw[c] = ld16(QK + row * ldqk + D + h * 32 + 8 * g);
   }
-#pragma unroll
-  for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-    for (int kb = 0; kb < WinOps<NKW>::KBW; ++kb) {
-      const int64_t row = clamp64(hrow + key0 + 32 * kb + 8 * g, 0, rmax - 8);
-      w.vw[c2][kb] = ld16(Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
-    }
+  (void)Vp;
+}
+
+// A operand of the window's value product for 32 keys kb (V transposed):
+// loaded where it is used, so it is not live through the scores.
+template <int D>
+__device__ __forceinline__ bf16x8 window_v(const WinArgs& wa, int64_t key0, int kb, int c2, int h, int r, int g) {
+  const int64_t row = clamp64(wa.hrow + key0 + 32 * kb + 8 * g, 0, wa.rmax - 8);
+  return ld16(wa.Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
 }
 
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
@@ -356,11 +359,12 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
       y1 = mma(o.vlt[1][kb], pb, y1);
     }
     if constexpr (NKW > 0) {
+      const int64_t key0 = win_key0(c0, wa->half);
 #pragma unroll
       for (int kb = 0; kb < NKW / 32; ++kb) {
         const bf16x8 pb = pack8(ws + 8 * kb);
-        y0 = mma(wo->vw[0][kb], pb, y0);
-        y1 = mma(wo->vw[1][kb], pb, y1);
+        y0 = mma(window_v<D>(*wa, key0, kb, 0, h, r, g), pb, y0);
+        y1 = mma(window_v<D>(*wa, key0, kb, 1, h, r, g), pb, y1);
       }
     }
     if (j >= lo && j < hi) {
@@ -588,21 +592,24 @@ __global__ __launch_bounds__(256) void qkv_proj(Rows X, int64_t R, int64_t R_pad
 
 // XOR attention: one workgroup per (user b, split s) with one wave per head,
 // so the waves of a workgroup read the same rows at the same time and share
-// each cache line.  Writes the E-branch rows of Y and the L-branch partial
+// each cache line (HB heads per workgroup: all of them, or half of 8 for
+// the windowed form, whose registers need the room).  Writes the E-branch rows of Y and the L-branch partial
 // [ell][2 + 32] (max, denominator, acc) of (b, h, s).
-template <int ELL, int H, int NKW = 0>
-__global__ __launch_bounds__(64 * H) void xor_attn(const bf16_t* __restrict__ QK,
-                                                   const bf16_t* __restrict__ Vp,
-                                                   bf16_t* __restrict__ Y, float* __restrict__ part,
-                                                   const int64_t* __restrict__ off, int B, int S,
-                                                   int64_t chunk, int64_t total_N, float scale,
-                                                   int phi, int do_e, int half, int64_t rmax) {
+template <int ELL, int H, int NKW = 0, int HB = H>
+__global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ QK,
+                                                    const bf16_t* __restrict__ Vp,
+                                                    bf16_t* __restrict__ Y, float* __restrict__ part,
+                                                    const int64_t* __restrict__ off, int B, int S,
+                                                    int64_t chunk, int64_t total_N, float scale,
+                                                    int phi, int do_e, int half, int64_t rmax) {
+  static_assert(H % HB == 0, "head groups");
   constexpr int D = 32 * H, MB = ELL / 16;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
-  const int h = threadIdx.x >> 6;
   const int s = static_cast<int>(blockIdx.x % S);
-  const int b = static_cast<int>(blockIdx.x / S);
+  const int64_t bg = blockIdx.x / S;  // (user, head group)
+  const int h = static_cast<int>(bg % (H / HB)) * HB + (threadIdx.x >> 6);
+  const int b = static_cast<int>(bg / (H / HB));
   const int64_t nlr = static_cast<int64_t>(B) * ELL;
   const int64_t u0 = clamp64(off[b], 0, total_N);
   const int64_t u1 = clamp64(off[b + 1], u0, total_N);
@@ -619,20 +626,27 @@ __global__ __launch_bounds__(64 * H) void xor_attn(const bf16_t* __restrict__ QK
   ChunkOps cur, nxt;
   if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g);
   for (; c0 < hi; c0 += 32) {
-    // issue the next chunk's loads before computing this one
-    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+    // issue the next chunk's loads before computing this one (the window's
+    // operands take those registers in the windowed form)
+    if constexpr (NKW == 0) {
+      if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+    }
     if (do_e) {
       if constexpr (NKW > 0) {
         WinOps<NKW> wo;
         load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, 2 * D);
-        const WinArgs wa{u0, u1, rmax, half};
+        const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
         e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g, D, &wo, &wa);
       } else {
         e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g);
       }
     }
     l_branch<ELL>(st, o, cur, c0, lo, hi, scale, softmax, r, g);
-    cur = nxt;
+    if constexpr (NKW == 0) {
+      cur = nxt;
+    } else {
+      if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+    }
   }
   float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
 #pragma unroll
@@ -1316,7 +1330,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         if constexpr (NKW > 0) {
           WinOps<NKW> wo;
           load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, LQK);
-          const WinArgs wa{0, n, RT, half};
+          const WinArgs wa{0, n, RT, half, Vps, ELL};
           e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY, &wo, &wa);
         } else {
           e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY);
