@@ -971,24 +971,35 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
 }
 
 // Post-attention block, weights streamed: 16 chunks of 64 weight rows per
-// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
+// 64-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
 // each: one pair), 12..15 w_down (two pairs each).  One wave owns 16 rows.
+// Chunks travel global -> LDS directly (gfx950 LDS-DMA loads, 16 bytes per
+// lane), so no registers carry them.  LDS rows are unpadded (D bf16) with
+// their 16-byte slots XOR-swizzled by swz(row): the 8 rows one fragment
+// read touches per lane group land in distinct banks.
 template <int D>
 struct PostStreamCfg {
-  static constexpr int NW = 4, NT = 64 * NW, CR = 64, LDW = D + 8;
-  static constexpr int CPT = CR * (D / 8) / NT;
-  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * LDW * 2;
+  static constexpr int NW = 4, NT = 64 * NW, CR = 64;
+  static constexpr int SPR = D / 8;                  // 16-byte slots per row
+  static constexpr int CPT = CR * SPR / NT;          // slots per thread per chunk
+  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * D * 2;
 };
 
+__device__ __forceinline__ int swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
 template <int D>
-__global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+__global__ __launch_bounds__(256, 2) void post_block_stream(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
                                                          const bf16_t* __restrict__ Wo,
                                                          const bf16_t* __restrict__ Wg,
                                                          const bf16_t* __restrict__ Wu,
                                                          const bf16_t* __restrict__ Wd) {
   using C = PostStreamCfg<D>;
-  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW, NCH = 16;
+  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, NCH = 16, SPR = C::SPR;
   static_assert(D == 256, "chunk schedule is written for d = 256");
+  static_assert(C::NT / SPR == 8 && C::CPT == 8, "load pattern assumes 8 rows per step");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -997,36 +1008,40 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
   const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   if (my_tiles <= 0) return;
 
-  // chunk k of the schedule: 64 weight rows (gate/up chunks: 32 of each).
-  // Thread tid loads rows tid / 32 + 8 i, i < 8, so i < 4 falls in the first
-  // 32 rows.  Chunk bases are uniform; the per-lane part is one 32-bit
-  // offset, recomputed per chunk so that no per-chunk address stays live.
-  static_assert(C::NT / (D / 8) == 8 && C::CPT == 8, "load pattern assumes 8 rows per step");
-  auto load_chunk_regs = [&](bf16x8 (&reg)[C::CPT], int k) {
-    const int off0 = (tid >> 5) * D + 8 * (tid & 31) + opaque_zero();
+  // chunk k of the schedule -> LDS buffer: slot e = i * NT + tid of the
+  // chunk, i.e. row 8 i + tid / 32 and swizzled slot tid % 32, is fetched by
+  // this thread with one LDS-DMA load; a wave's 64 lanes fill 1 KB of LDS in
+  // a row.  Chunk bases are uniform; the per-lane part is one 32-bit offset,
+  // recomputed per chunk so that no per-chunk address stays live.
+  auto issue_chunk = [&](int k, bf16_t* buf) {
+    const int lrow = (tid >> 5) + opaque_zero();  // row within an 8-row group
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
+      const int slot = (tid & 31) ^ ((lrow & 3) | ((i & 3) << 2));  // = slot ^ swz(8 i + lrow)
+      const int loff = lrow * D + 8 * slot;
       const bf16_t* base;
-      int off;
-      if (k < 4) { base = Wo + 64 * k * D; off = off0 + 8 * i * D; }
-      else if (k < 12) { base = (i < 4 ? Wg : Wu) + 32 * (k - 4) * D; off = off0 + 8 * (i & 3) * D; }
-      else { base = Wd + 64 * (k - 12) * D; off = off0 + 8 * i * D; }
-      reg[i] = ld16(base + off);
+      if (k < 4) base = Wo + (64 * k + 8 * i) * D;
+      else if (k < 12) base = (i < 4 ? Wg : Wu) + (32 * (k - 4) + 8 * (i & 3)) * D;
+      else base = Wd + (64 * (k - 12) + 8 * i) * D;
+      // (address-space casts: the builtin takes a global source and an LDS
+      // destination; a wave's destination is its uniform 1 KB segment)
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(base + loff), (lds_void_t*)(buf + (i * C::NT + w * 64) * 8),
+                                       16, 0, 0);
     }
+  };
+  // this wave's LDS-DMA loads complete, then the workgroup barrier
+  auto chunk_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+  };
+  // the A fragment of weight row `row`, k-slice kb, of a chunk buffer; every
+  // row this kernel reads as lane (r, g) has swz(row) = r
+  auto frag = [&](const bf16_t* wb, int row, int kb) {
+    return ld16(wb + row * D + 8 * ((4 * kb + g) ^ r));
   };
 
-  auto store_regs = [&](const bf16x8 (&reg)[C::CPT], bf16_t* buf) {
-    constexpr int C8 = D / 8;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int e = tid + i * C::NT;
-      *reinterpret_cast<bf16x8*>(buf + (e / C8) * LDW + 8 * (e % C8)) = reg[i];
-    }
-  };
-  bf16x8 reg[C::CPT];
-  load_chunk_regs(reg, 0);
-  store_regs(reg, buf0);
-  lds_barrier();
+  issue_chunk(0, buf0);
+  chunk_barrier();
   for (int64_t it = 0; it < my_tiles; ++it) {
     const int64_t tile = blockIdx.x + it * gridDim.x;
     const int64_t row = tile * 16 * NW + 16 * w + r;
@@ -1048,8 +1063,8 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
       const bool more = (k + 1 < NCH) || (it + 1 < my_tiles);
-      if (more) load_chunk_regs(reg, (k + 1) % NCH);
-      const bf16_t* wb = buf0 + (k & 1) * (CR * LDW) + opaque_zero();
+      if (more) issue_chunk((k + 1) % NCH, buf0 + ((k + 1) & 1) * (CR * D));
+      const bf16_t* wb = buf0 + (k & 1) * (CR * D) + opaque_zero();
       if (k < 4 || k >= 12) {
         // x1 += (Y or M) W^T for column pairs 2k', 2k'+1
         const int kk = k < 4 ? k : k - 12;
@@ -1058,10 +1073,11 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
           floatx4 acc[2] = {};
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const bf16_t* wr = wb + (32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3)) * LDW + 8 * g;
+            const int wrow = 32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-              acc[cc] = mma(ld16(wr + kb * 32), k < 4 ? yb[0][kb] : mb[kb], acc[cc]);
+              acc[cc] = mma(frag(wb, wrow, kb), k < 4 ? yb[0][kb] : mb[kb], acc[cc]);
+            __builtin_amdgcn_sched_barrier(0);
           }
           const int p = 2 * kk + pp;
 #pragma unroll
@@ -1086,14 +1102,15 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int orow = 8 * (r >> 2) + 4 * cc + (r & 3);
-          const bf16_t* gr = wb + orow * LDW + 8 * g;
-          const bf16_t* ur = wb + (32 + orow) * LDW + 8 * g;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            ag[cc] = mma(ld16(gr + kb * 32), gb[kb], ag[cc]);
-            au[cc] = mma(ld16(ur + kb * 32), gb[kb], au[cc]);
+          for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int kb = kh * KB / 2; kb < (kh + 1) * KB / 2; ++kb) {
+              ag[cc] = mma(frag(wb, orow, kb), gb[kb], ag[cc]);
+              au[cc] = mma(frag(wb, 32 + orow, kb), gb[kb], au[cc]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
         float v[8];
 #pragma unroll
@@ -1103,8 +1120,7 @@ __global__ __launch_bounds__(256) void post_block_stream(Rows Yr, Rows Xres, Row
         }
         mb[k - 4] = pack8(v);
       }
-      if (more) store_regs(reg, buf0 + ((k + 1) & 1) * (CR * LDW));
-      lds_barrier();
+      chunk_barrier();
     }
     if (rowok) {
       bf16_t* orow = row_out<bf16_t>(Out, row);
