@@ -333,34 +333,71 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
   int cur = -1;
   int u = find_owner(off, B, t0 * 16);
 
-  for (int64_t t = t0; t < t1; ++t) {
+  // Software pipeline over the wave's tiles (PIPE): the ids of tile t + 2
+  // and the gathered cache rows of tile t + 1 are in flight while tile t is
+  // computed (the row gather depends on the ids, so they go two stages).
+  // It pays where the registers already limit occupancy (ell = 64) and for
+  // the int8 rows; elsewhere the extra registers cost more waves than the
+  // overlap gains.
+  constexpr bool PIPE = I8 || ELL == 64;
+  auto load_id = [&](int64_t t) -> int64_t {
     const int64_t i = t * 16 + r;
-    const bool valid = i < total_M;
-    int ul = u;
-    if (valid)
-      while (ul + 1 < B && off[ul + 1] <= i) ++ul;
-    const int64_t id = valid ? ids[i] : -1;
-    const bool okid = valid && id >= 0 && id < n_items;
-    if (valid && !okid && g == 0 && hg == 0 && bad != nullptr) atomicAdd(bad, 1);
-
-    bf16x8 bw[HG][KB];
-    float qs[HG];
+    return (t < t1 && i < total_M) ? ids[i] : int64_t(-1);
+  };
+  auto gather = [&](bf16x8 (&bw)[HG][KB], float (&qs)[HG], int64_t id, bool okid) {
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       const int h = hbase + hh;
+      const int64_t idc = okid ? id : 0;
       if constexpr (I8) {
-        const int8_t* row = static_cast<const int8_t*>(cache_in) + (id * H + h) * ELL + 8 * g;
+        const int8_t* row = static_cast<const int8_t*>(cache_in) + (idc * H + h) * ELL + 8 * g;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
           bw[hh][kb] = okid ? i8x8_to_bf16(*reinterpret_cast<const uint2*>(row + kb * 32)) : zero8();
-        qs[hh] = okid ? qscale[id * H + h] : 0.f;
+        qs[hh] = okid ? qscale[idc * H + h] : 0.f;
       } else {
-        const bf16_t* row = static_cast<const bf16_t*>(cache_in) + (id * H + h) * ELL + 8 * g;
+        const bf16_t* row = static_cast<const bf16_t*>(cache_in) + (idc * H + h) * ELL + 8 * g;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) bw[hh][kb] = okid ? ld16(row + kb * 32) : zero8();
         qs[hh] = 1.f;
       }
     }
+  };
+  auto in_range = [&](int64_t id) { return id >= 0 && id < n_items; };
+
+  int64_t id_c = 0, id_n = 0;
+  bool ok_c = false;
+  bf16x8 bw_c[HG][KB];
+  float qs_c[HG];
+  if constexpr (PIPE) {
+    id_c = load_id(t0);
+    id_n = load_id(t0 + 1);
+    ok_c = in_range(id_c);
+    gather(bw_c, qs_c, id_c, ok_c);
+  }
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t i = t * 16 + r;
+    const bool valid = i < total_M;
+    bf16x8 bw_n[HG][KB];
+    float qs_n[HG];
+    int64_t id_nn = 0;
+    bool ok_n = false;
+    if constexpr (PIPE) {
+      // next stages: ids of t + 2, rows of t + 1
+      id_nn = load_id(t + 2);
+      ok_n = in_range(id_n);
+      gather(bw_n, qs_n, id_n, ok_n);
+    } else {
+      id_c = load_id(t);
+      ok_c = in_range(id_c);
+      gather(bw_c, qs_c, id_c, ok_c);
+    }
+
+    int ul = u;
+    if (valid)
+      while (ul + 1 < B && off[ul + 1] <= i) ++ul;
+    if (valid && !ok_c && g == 0 && hg == 0 && bad != nullptr) atomicAdd(bad, 1);
 
     const int last = static_cast<int>((total_M - 1 - t * 16) < 15 ? (total_M - 1 - t * 16) : 15);
     const int ufirst = __shfl(ul, 0);
@@ -388,11 +425,11 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          acc0 = mma(a[hh][0][kb], bw[hh][kb], acc0);
-          acc1 = mma(a[hh][1][kb], bw[hh][kb], acc1);
+          acc0 = mma(a[hh][0][kb], bw_c[hh][kb], acc0);
+          acc1 = mma(a[hh][1][kb], bw_c[hh][kb], acc1);
         }
         if (mine) {
-          const float sc = qs[hh];
+          const float sc = qs_c[hh];
           const float v[8] = {acc0[0] * sc, acc0[1] * sc, acc0[2] * sc, acc0[3] * sc,
                               acc1[0] * sc, acc1[1] * sc, acc1[2] * sc, acc1[3] * sc};
           st8(out + i * D + (hbase + hh) * 32 + 8 * g, v);
@@ -400,6 +437,17 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
       }
     }
     u = __shfl(ul, last);
+    if constexpr (PIPE) {
+      // rotate the pipeline
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        qs_c[hh] = qs_n[hh];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bw_c[hh][kb] = bw_n[hh][kb];
+      }
+      ok_c = ok_n;
+      id_n = id_nn;
+    }
   }
 }
 
