@@ -313,6 +313,9 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
   const Rows Yr{Y, Y + nlr * D, nlr, D};
+  // the projections store Q times the logit scale in log2 units; the
+  // attention kernels then work with base-2 exponentials
+  const float qs = scale * mfma::LOG2E;
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
     const bool full = !va.links_only && (!last || hist_out != nullptr);
@@ -335,7 +338,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
       if (grid > need) grid = need;
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs);
     } else {
       // weights streamed through LDS, persistent workgroups
       auto k = mfma::qkv_proj_stream<D>;
@@ -349,7 +352,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       if (grid > ntiles) grid = ntiles;
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp);
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs);
     }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
     {
@@ -359,11 +362,11 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const dim3 grid_w(static_cast<unsigned>(static_cast<int64_t>(B) * P.S * (H / HBW)));
       if (va.half > 0 && full)
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
-                           Vp, Y, part, off, B, P.S, P.chunk, total_N, scale, static_cast<int>(phi), 1, va.half,
+                           Vp, Y, part, off, B, P.S, P.chunk, total_N, static_cast<int>(phi), 1, va.half,
                            P.R_pad);
       else
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, B, P.S,
-                           P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
+                           P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
     }
     LIME_CHECK_LAUNCH("xor attention (mfma)");
     {

@@ -70,7 +70,8 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
-                                        int ldw, bf16_t* QK, int64_t row0, int r, int g, int ldqk = 2 * D) {
+                                        int ldw, bf16_t* QK, int64_t row0, int r, int g, float qs,
+                                        int ldqk = 2 * D) {
   constexpr int KB = D / 32;
 #pragma unroll 2
   for (int p = 0; p < 2 * D / 32; ++p) {
@@ -85,11 +86,12 @@ __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf1
         acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
       }
     }
+    const float f = p < D / 32 ? qs : 1.f;  // Q columns carry the logit scale
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-      const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
-                          acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+      const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                          acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
       st8(QK + row * ldqk + 32 * p + 8 * g, v);
     }
   }
@@ -116,8 +118,8 @@ __device__ __forceinline__ void v_part(const bf16x8 (&hb)[2][D / 32], const bf16
 
 template <int D>
 __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
-                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g) {
-  qk_part<D>(hb, W, ldw, QK, row0, r, g);
+                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, float qs) {
+  qk_part<D>(hb, W, ldw, QK, row0, r, g, qs);
   v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
@@ -127,7 +129,7 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
 // pieces of 4 rows of one column in the packed layout (row0 a multiple of 8).
 template <int D, int RB>
 __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16_t* __restrict__ W, int ldw,
-                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk) {
+                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk, float qs) {
   constexpr int KB = D / 32;
   bf16x8 hb[RB][KB];
 #pragma unroll
@@ -152,10 +154,11 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
         for (int rb = 0; rb < RB; ++rb) acc[c][rb] = mma(a, hb[rb][kb], acc[c][rb]);
       }
     }
+    const float f = p < D / 32 ? qs : 1.f;  // Q columns carry the logit scale
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float o[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
-                          acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+      const float o[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                          acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
       st8(QK + (row0 + 16 * rb + r) * ldqk + 32 * p + 8 * g, o);
     }
   }
@@ -274,12 +277,27 @@ __device__ __forceinline__ bf16x8 window_v(const WinArgs& wa, int64_t key0, int 
   return ld16(wa.Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
 }
 
+// phi in log2 units.  The projections store Q multiplied by scale*log2(e),
+// so a score y is the logit x in log2 units (x = y ln 2):
+//   softmax  2^(y - max y)                 (the same weights)
+//   silu2(y) = y / (1 + 2^-y) = SiLU(x) / ln 2, the ln 2 going into the
+//   normaliser.  Two VALU ops per logit fewer than scaling every logit and
+//   converting to base e.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_f(float y) { return __builtin_amdgcn_exp2f(y); }
+
+__device__ __forceinline__ float silu2(float y) {
+  return y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-y));
+}
+
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
 // NKW > 0, to their window); rows in [lo, hi) are written to Y.
 template <int ELL, int D, int NKW = 0>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
-                                         float scale, bool softmax, int r, int g, int ldy = D,
+                                         bool softmax, int r, int g, int ldy = D,
                                          const WinOps<NKW>* wo = nullptr, const WinArgs* wa = nullptr) {
   constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
   constexpr int NWS = NKW > 0 ? NKW / 4 : 1;  // window scores per lane
@@ -291,7 +309,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
     for (int c = 0; c < MB; ++c) {
       const floatx4 st = mma(o.kl[c], ci.qe[rb], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[4 * c + q] = st[q] * scale;
+      for (int q = 0; q < 4; ++q) v[4 * c + q] = st[q];
     }
     float ws[NWS];
     int nwin = 0;  // this row's window size (its own row excluded)
@@ -305,7 +323,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
           const int64_t kq = key0 + (c >> 1) * 32 + 8 * g + 4 * (c & 1) + q;
           const int64_t dist = kq > j ? kq - j : j - kq;
           const bool ok = kq >= wa->u0 && kq < wa->u1 && dist >= 1 && dist <= wa->half;
-          ws[4 * c + q] = ok ? sw[q] * scale : -INFINITY;
+          ws[4 * c + q] = ok ? sw[q] : -INFINITY;
         }
       }
       const int64_t a = j - wa->half > wa->u0 ? j - wa->half : wa->u0;
@@ -324,13 +342,13 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
       float sum = 0.f;
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) {
-        v[q] = __expf(v[q] - mx);
+        v[q] = exp2_f(v[q] - mx);
         sum += v[q];
       }
       if constexpr (NKW > 0) {
 #pragma unroll
         for (int q = 0; q < NWS; ++q) {
-          ws[q] = __expf(ws[q] - mx);  // 0 for masked keys
+          ws[q] = exp2_f(ws[q] - mx);  // 0 for masked keys
           sum += ws[q];
         }
       }
@@ -343,12 +361,12 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
         for (int q = 0; q < NWS; ++q) ws[q] *= inv;
       }
     } else {
-      const float inv = NKW > 0 ? 1.f / static_cast<float>(ELL + nwin) : 1.f / ELL;
+      const float inv = NKW > 0 ? LN2 / static_cast<float>(ELL + nwin) : LN2 / ELL;
 #pragma unroll
-      for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+      for (int q = 0; q < 4 * MB; ++q) v[q] = silu2(v[q]) * inv;
       if constexpr (NKW > 0) {
 #pragma unroll
-        for (int q = 0; q < NWS; ++q) ws[q] = ws[q] == -INFINITY ? 0.f : silu_f(ws[q]) * inv;
+        for (int q = 0; q < NWS; ++q) ws[q] = ws[q] == -INFINITY ? 0.f : silu2(ws[q]) * inv;
       }
     }
     floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
@@ -394,17 +412,19 @@ struct LState {
 };
 
 // L-branch: the links attend to history rows c0 + [0, 32) (those in
-// [lo, hi)); c0 + hrow must be a multiple of 8.
-template <int ELL>
-__device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
-                                         int64_t c0, int64_t lo, int64_t hi, float scale,
-                                         bool softmax, int r, int g) {
+// [lo, hi)); c0 + hrow must be a multiple of 8.  Scores are in log2 units;
+// with silu the accumulators hold sum silu2 * v (the ln 2 factor is applied
+// where they are normalised).  MASK = false: every row of the chunk is in
+// [lo, hi).
+template <int ELL, bool MASK>
+__device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
+                                              int64_t c0, int64_t lo, int64_t hi, bool softmax, int r, int g) {
   constexpr int MB = HeadOps<ELL>::MB;
   bool valid[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int64_t j = c0 + 8 * g + q;  // q = 4*c + jj
-    valid[q] = (j >= lo) && (j < hi);
+    valid[q] = !MASK || ((j >= lo) && (j < hi));
   }
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
@@ -413,7 +433,7 @@ __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o,
     for (int c = 0; c < 2; ++c) {
       const floatx4 sv = mma(ci.ke[c], o.qlt[nb], floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[4 * c + q] = sv[q] * scale;
+      for (int q = 0; q < 4; ++q) p[4 * c + q] = sv[q];
     }
     if (softmax) {
       float mc = -INFINITY;
@@ -422,11 +442,11 @@ __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o,
         if (valid[q]) mc = fmaxf(mc, p[q]);
       mc = rows_max(mc);
       const float mn = fmaxf(st.m[nb], mc);
-      const float alpha = (st.m[nb] == -INFINITY) ? 0.f : __expf(st.m[nb] - mn);
+      const float alpha = (st.m[nb] == -INFINITY) ? 0.f : exp2_f(st.m[nb] - mn);
       float ls = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        p[q] = valid[q] ? __expf(p[q] - mn) : 0.f;
+        p[q] = valid[q] ? exp2_f(p[q] - mn) : 0.f;
         ls += p[q];
       }
       ls = rows_sum(ls);
@@ -441,12 +461,21 @@ __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o,
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) p[q] = valid[q] ? silu_f(p[q]) : 0.f;
+      for (int q = 0; q < 8; ++q) p[q] = valid[q] ? silu2(p[q]) : 0.f;
     }
     const bf16x8 pa = pack8(p);
     st.acc[nb][0] = mma(pa, ci.ve[0], st.acc[nb][0]);
     st.acc[nb][1] = mma(pa, ci.ve[1], st.acc[nb][1]);
   }
+}
+
+template <int ELL>
+__device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
+                                         int64_t c0, int64_t lo, int64_t hi, bool softmax, int r, int g) {
+  if (c0 >= lo && c0 + 32 <= hi)
+    l_branch_rows<ELL, false>(st, o, ci, c0, lo, hi, softmax, r, g);
+  else
+    l_branch_rows<ELL, true>(st, o, ci, c0, lo, hi, softmax, r, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -556,40 +585,6 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
 // Streaming kernels (any history length)
 // ===========================================================================
 
-// LN + QKV projection, 32 rows per wave; rows >= R are zero.
-template <int D>
-__global__ __launch_bounds__(256) void qkv_proj(Rows X, int64_t R, int64_t R_pad,
-                                                const bf16_t* __restrict__ W,
-                                                bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
-  constexpr int KB = D / 32;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * 32;
-  if (row0 >= R_pad) return;
-  bf16x8 hb[2][KB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-    float v[8 * KB];
-    if (row < R) {
-      const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 x = ld16(xr + kb * 32);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
-    }
-    ln_rows<8 * KB>(v, D);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
-  }
-  qkv_chunk<D>(hb, W, D, QK, Vp, row0, r, g);
-}
-
 // XOR attention: one workgroup per (user b, split s) with one wave per head,
 // so the waves of a workgroup read the same rows at the same time and share
 // each cache line (HB heads per workgroup: all of them, or half of 8 for
@@ -600,7 +595,7 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
                                                     const bf16_t* __restrict__ Vp,
                                                     bf16_t* __restrict__ Y, float* __restrict__ part,
                                                     const int64_t* __restrict__ off, int B, int S,
-                                                    int64_t chunk, int64_t total_N, float scale,
+                                                    int64_t chunk, int64_t total_N,
                                                     int phi, int do_e, int half, int64_t rmax) {
   static_assert(H % HB == 0, "head groups");
   constexpr int D = 32 * H, MB = ELL / 16;
@@ -636,12 +631,12 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
         WinOps<NKW> wo;
         load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, 2 * D);
         const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
-        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g, D, &wo, &wa);
+        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, D, &wo, &wa);
       } else {
-        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, scale, softmax, r, g);
+        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g);
       }
     }
-    l_branch<ELL>(st, o, cur, c0, lo, hi, scale, softmax, r, g);
+    l_branch<ELL>(st, o, cur, c0, lo, hi, softmax, r, g);
     if constexpr (NKW == 0) {
       cur = nxt;
     } else {
@@ -651,56 +646,18 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
+    // partials in natural units: max * ln 2; silu sums * ln 2
     if (g == 0) {
       float* pl = p0 + (16 * nb + r) * 34;
-      pl[0] = softmax ? st.m[nb] : 0.f;
+      pl[0] = softmax ? st.m[nb] * LN2 : 0.f;
       pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
     }
+    const float f = softmax ? 1.f : LN2;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        p0[(16 * nb + 4 * g + jj) * 34 + 2 + 16 * c2 + r] = st.acc[nb][c2][jj];
-  }
-}
-
-// Post-attention block, RPW rows per wave, rows [0, nrows).
-template <int D, int DFF, int RPW>
-__global__ __launch_bounds__(256) void post_block(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
-                                                  const bf16_t* __restrict__ Wo,
-                                                  const bf16_t* __restrict__ Wg,
-                                                  const bf16_t* __restrict__ Wu,
-                                                  const bf16_t* __restrict__ Wd) {
-  constexpr int KB = D / 32, RB = RPW / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + w) * RPW;
-  if (row0 >= nrows) return;
-  bf16x8 yb[RB][KB];
-  float x1[RB][D / 4];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = row0 + 16 * rb + r;
-    const bool ok = row < nrows;
-    const bf16_t* yr = ok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
-    const bf16_t* xr = ok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      yb[rb][kb] = ok ? ld16(yr + kb * 32) : zero8();
-      const bf16x8 x = ok ? ld16(xr + kb * 32) : zero8();
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = static_cast<float>(x[q]);
-    }
-  }
-  post_rows<D, DFF, RB>(yb, x1, Wo, Wg, Wu, Wd, D, DFF, r, g);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int64_t row = row0 + 16 * rb + r;
-    if (row >= nrows) continue;
-    bf16_t* orow = row_out<bf16_t>(Out, row);
-    if (orow == nullptr) continue;
-#pragma unroll
-    for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[rb][8 * p]);
+        p0[(16 * nb + 4 * g + jj) * 34 + 2 + 16 * c2 + r] = st.acc[nb][c2][jj] * f;
   }
 }
 
@@ -728,7 +685,8 @@ struct QkvLds {
 template <int D>
 __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64_t R, int64_t R_pad,
                                                     const bf16_t* __restrict__ W,
-                                                    bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
+                                                    bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
+                                                    float qs) {
   constexpr int KB = D / 32, NW = QkvLds<D>::NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
@@ -761,7 +719,7 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
     }
-    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g);
+    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs);
   }
 }
 
@@ -873,7 +831,8 @@ __device__ __forceinline__ void chunk_store(const bf16x8 (&reg)[StreamCfg<D>::CP
 template <int D>
 __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_t R_pad,
                                                        const bf16_t* __restrict__ W,
-                                                       bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp) {
+                                                       bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
+                                                       float qs) {
   using C = StreamCfg<D>;
   constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW;
   constexpr int NCH = 3 * D / CR, NQK = 2 * D / CR;
@@ -940,11 +899,12 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
               acc[cc][1] = mma(a, hb[1][kb], acc[cc][1]);
             }
           }
+          const float f = CR * k < D ? qs : 1.f;  // Q columns carry the logit scale
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
             const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-            const float v[8] = {acc[0][rb][0], acc[0][rb][1], acc[0][rb][2], acc[0][rb][3],
-                                acc[1][rb][0], acc[1][rb][1], acc[1][rb][2], acc[1][rb][3]};
+            const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                                acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
             st8(QK + row * (2 * D) + CR * k + 32 * pp + 8 * g, v);
           }
         }
@@ -1224,6 +1184,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
   const int n = static_cast<int>(u1 - u0);
   const int rows = ELL + n;
   const bool softmax = (phi == PHI_SOFTMAX);
+  const float qs = scale * LOG2E;  // Q carries the logit scale in log2 units
   const int nchunks = RT / 32;
 
   // weight prefetch registers: set 0 (w_qkv) and set 1 (post weights)
@@ -1297,7 +1258,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
       }
       if (it & 1) v_part<D>(hb, lq + opaque_zero(), ldd, Vps, row0, r, g);
-      else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, LQK);
+      else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, qs, LQK);
     }
     lds_barrier();
   }
@@ -1324,7 +1285,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         for (int c0 = 0; c0 < n; c0 += 32) {
           ChunkOps ci;
           load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, LQK);
-          l_branch<ELL>(st, o, ci, c0, 0, n, scale, softmax, r, g);
+          l_branch<ELL>(st, o, ci, c0, 0, n, softmax, r, g);
         }
         // normalise and write the link rows of Y
 #pragma unroll
@@ -1333,7 +1294,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const float dj = __shfl(den, 4 * g + jj);
-            const float inv = dj > 0.f ? 1.f / dj : 0.f;
+            const float inv = dj > 0.f ? (softmax ? 1.f : LN2) / dj : 0.f;
             const int link = 16 * nb + 4 * g + jj;
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2)
@@ -1347,9 +1308,9 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
           WinOps<NKW> wo;
           load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, LQK);
           const WinArgs wa{0, n, RT, half, Vps, ELL};
-          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY, &wo, &wa);
+          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, LY, &wo, &wa);
         } else {
-          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, scale, softmax, r, g, LY);
+          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, LY);
         }
       }
     }
@@ -1404,7 +1365,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
             for (int kb = 0; kb < KB; ++kb)
               lds_st8f(Xs + (row0 + 16 * rb + r) * XS + kb * 32 + 8 * g, &x1[rb][8 * kb]);
         }
-        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, LQK);
+        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, LQK, qs);
       } else if (do_post) {
 #pragma unroll
         for (int rb = 0; rb < PRB; ++rb) {
