@@ -74,6 +74,17 @@ __device__ __forceinline__ void st4(bf16_t* p, const floatx4& v) {
   *reinterpret_cast<bf16x4*>(p) = o;
 }
 
+// The same as a streaming (non-temporal) store: for outputs written once
+// and not read back by the kernel.  Scoring writes its outputs this way so
+// that they do not evict the hot cache rows its gathers reuse.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st8_stream(bf16_t* p, const float* v) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(v[j]);
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, o), reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
@@ -432,7 +443,7 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
           const float sc = qs_c[hh];
           const float v[8] = {acc0[0] * sc, acc0[1] * sc, acc0[2] * sc, acc0[3] * sc,
                               acc1[0] * sc, acc1[1] * sc, acc1[2] * sc, acc1[3] * sc};
-          st8(out + i * D + (hbase + hh) * 32 + 8 * g, v);
+          st8_stream(out + i * D + (hbase + hh) * 32 + 8 * g, v);
         }
       }
     }
@@ -597,7 +608,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
           const float zf = okid ? 1.f : 0.f;  // out-of-range ids give zero rows
           const float v[8] = {acc0[0] * zf, acc0[1] * zf, acc0[2] * zf, acc0[3] * zf,
                               acc1[0] * zf, acc1[1] * zf, acc1[2] * zf, acc1[3] * zf};
-          st8(out + i * D + h * 32 + 8 * g, v);
+          st8_stream(out + i * D + h * 32 + 8 * g, v);
         }
       }
     }

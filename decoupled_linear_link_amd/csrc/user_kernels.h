@@ -618,13 +618,16 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   LState<ELL> st;
   st.init();
   int64_t c0 = lo & ~int64_t(7);
-  ChunkOps cur, nxt;
+  // chunk operands two chunks ahead of the one being computed (the windowed
+  // form, whose own operands take the registers, loads one at a time)
+  ChunkOps cur, nxt, nxt2;
   if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g);
+  if constexpr (NKW == 0) {
+    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+  }
   for (; c0 < hi; c0 += 32) {
-    // issue the next chunk's loads before computing this one (the window's
-    // operands take those registers in the windowed form)
     if constexpr (NKW == 0) {
-      if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+      if (c0 + 64 < hi) load_chunk<D>(nxt2, QK, Vp, nlr, c0 + 64, h, do_e, r, g);
     }
     if (do_e) {
       if constexpr (NKW > 0) {
@@ -639,6 +642,7 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
     l_branch<ELL>(st, o, cur, c0, lo, hi, softmax, r, g);
     if constexpr (NKW == 0) {
       cur = nxt;
+      nxt = nxt2;
     } else {
       if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
     }
