@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void xor_attn(const T* __restrict__ qkv, T* __
 // sum_s l_s e^{m_s-M}; zero when the user has no history.
 template <typename T, int DH>
 __global__ void xor_combine(const float* __restrict__ part, T* __restrict__ Y, int B, int ell,
-                            int d, int H, int S) {
+                            int d, int H, int S, int64_t yrs, int64_t yps) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = static_cast<int64_t>(B) * H * ell * DH;
   if (gid >= total) return;
@@ -284,7 +284,9 @@ __global__ void xor_combine(const float* __restrict__ part, T* __restrict__ Y, i
     num += f * p[2 + c];
   }
   const float v = den > 0.f ? num / den : 0.f;
-  Elt<T>::st(Y + (static_cast<int64_t>(b) * ell + k) * d + h * DH + c, v);
+  // Y row b * ell + k, head h: at h * yps + row * yrs (row-major: yrs = d,
+  // yps = DH; head-planar: yrs = DH, yps = rows * DH)
+  Elt<T>::st(Y + h * yps + (static_cast<int64_t>(b) * ell + k) * yrs + c, v);
 }
 
 // ---------------------------------------------------------------------------

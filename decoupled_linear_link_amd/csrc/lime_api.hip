@@ -312,7 +312,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   float* part = reinterpret_cast<float*>(ws + P.o_part);
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
-  const Rows Yr{Y, Y + nlr * D, nlr, D};
+  // Q|K and Y are head-planar in the workspace (see the kernels' Lay)
   // the projections store Q times the logit scale in log2 units; the
   // attention kernels then work with base-2 exponentials
   const float qs = scale * mfma::LOG2E;
@@ -372,7 +372,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     {
       const int64_t n = static_cast<int64_t>(B) * H * ELL * 32;
       hipLaunchKernelGGL((gen::xor_combine<bf16_t, 32>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                         0, st, part, Y, B, ELL, D, H, P.S);
+                         0, st, part, Y, B, ELL, D, H, P.S, int64_t(32), R * 32);
       LIME_CHECK_LAUNCH("xor combine");
     }
     const int64_t pw = (rows_post + RPW - 1) / RPW;
@@ -387,7 +387,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       const int64_t need = (pw + mfma::PostLds<D, D>::NW - 1) / mfma::PostLds<D, D>::NW;
       if (grid > need) grid = need;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::PostLds<D, D>::NW), lds, st, Yr,
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::PostLds<D, D>::NW), lds, st, Y, R,
                          Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
@@ -404,7 +404,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const int64_t ntiles = (rows_post + 16 * PC::NW - 1) / (16 * PC::NW);
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       if (grid > ntiles) grid = ntiles;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, Yr, Xin,
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, static_cast<const bf16_t*>(Y), R, Xin,
                          Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
@@ -468,7 +468,7 @@ lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int
     {
       const int64_t n = static_cast<int64_t>(B) * H * ell * DH;
       hipLaunchKernelGGL((xor_combine<T, DH>), dim3(static_cast<unsigned>((n + 255) / 256)), blk, 0,
-                         st, part, Y, B, ell, d, H, P.S);
+                         st, part, Y, B, ell, d, H, P.S, static_cast<int64_t>(d), static_cast<int64_t>(DH));
       LIME_CHECK_LAUNCH("xor combine");
     }
     hipLaunchKernelGGL((gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,

@@ -23,6 +23,15 @@ __device__ __forceinline__ int64_t vp_index(int64_t row, int col, int D) {
   return (row >> 3) * static_cast<int64_t>(D) * 8 + static_cast<int64_t>(col) * 8 + (row & 7);
 }
 
+// Layout of a buffer of 32-column head slices: slice p of row `row` starts
+// at element p * ps + row * rs.  For Q|K the slice index is part * H + h
+// (part 0 = Q, 1 = K); for Y it is h.  Row-major rows: rs = row stride,
+// ps = 32.  Head-planar (every slice of every row contiguous by rows, as the
+// streaming kernels use in HBM): rs = 32, ps = rows * 32.
+struct Lay {
+  int64_t rs, ps;
+};
+
 // Pairwise (tree) sum of N values: a log-depth dependency chain instead of
 // a serial one.
 template <int N>
@@ -71,7 +80,7 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 template <int D>
 __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
                                         int ldw, bf16_t* QK, int64_t row0, int r, int g, float qs,
-                                        int ldqk = 2 * D) {
+                                        Lay L) {
   constexpr int KB = D / 32;
 #pragma unroll 2
   for (int p = 0; p < 2 * D / 32; ++p) {
@@ -92,7 +101,7 @@ __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf1
       const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
       const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                           acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-      st8(QK + row * ldqk + 32 * p + 8 * g, v);
+      st8(QK + p * L.ps + row * L.rs + 8 * g, v);
     }
   }
 }
@@ -118,8 +127,9 @@ __device__ __forceinline__ void v_part(const bf16x8 (&hb)[2][D / 32], const bf16
 
 template <int D>
 __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
-                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, float qs) {
-  qk_part<D>(hb, W, ldw, QK, row0, r, g, qs);
+                                          int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, float qs,
+                                          Lay L) {
+  qk_part<D>(hb, W, ldw, QK, row0, r, g, qs, L);
   v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
@@ -129,7 +139,7 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
 // pieces of 4 rows of one column in the packed layout (row0 a multiple of 8).
 template <int D, int RB>
 __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16_t* __restrict__ W, int ldw,
-                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, int ldqk, float qs) {
+                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, Lay L, float qs) {
   constexpr int KB = D / 32;
   bf16x8 hb[RB][KB];
 #pragma unroll
@@ -159,7 +169,7 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
     for (int rb = 0; rb < RB; ++rb) {
       const float o[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                           acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-      st8(QK + (row0 + 16 * rb + r) * ldqk + 32 * p + 8 * g, o);
+      st8(QK + p * L.ps + (row0 + 16 * rb + r) * L.rs + 8 * g, o);
     }
   }
 #pragma unroll 2
@@ -194,12 +204,13 @@ struct HeadOps {
 
 template <int ELL, int D>
 __device__ __forceinline__ void load_head_ops(HeadOps<ELL>& o, const bf16_t* QK, const bf16_t* Vp,
-                                              int64_t lrow, int h, int r, int g, int ldqk = 2 * D) {
+                                              int64_t lrow, int h, int r, int g, Lay L) {
+  constexpr int H = D / 32;
 #pragma unroll
   for (int c = 0; c < HeadOps<ELL>::MB; ++c) {
     const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-    o.kl[c] = ld16(QK + (lrow + link) * ldqk + D + h * 32 + 8 * g);
-    o.qlt[c] = ld16(QK + (lrow + 16 * c + r) * ldqk + h * 32 + 8 * g);
+    o.kl[c] = ld16(QK + (H + h) * L.ps + (lrow + link) * L.rs + 8 * g);
+    o.qlt[c] = ld16(QK + h * L.ps + (lrow + 16 * c + r) * L.rs + 8 * g);
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
@@ -217,14 +228,15 @@ struct ChunkOps {
 
 template <int D>
 __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const bf16_t* Vp, int64_t hrow,
-                                           int64_t c0, int h, bool with_q, int r, int g, int ldqk = 2 * D) {
+                                           int64_t c0, int h, bool with_q, int r, int g, Lay L) {
+  constexpr int H = D / 32;
   if (with_q) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + (hrow + c0 + 16 * rb + r) * ldqk + h * 32 + 8 * g);
+    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + h * L.ps + (hrow + c0 + 16 * rb + r) * L.rs + 8 * g);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    c.ke[k] = ld16(QK + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * ldqk + D + h * 32 + 8 * g);
+    c.ke[k] = ld16(QK + (H + h) * L.ps + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * L.rs + 8 * g);
   c.ve[0] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + r, D));
   c.ve[1] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
 }
@@ -259,12 +271,13 @@ __device__ __forceinline__ int64_t win_key0(int64_t c0, int half) { return c0 - 
 // every buffer row holds finite values.
 template <int NKW, int D>
 __device__ __forceinline__ void load_window(WinOps<NKW>& w, const bf16_t* QK, const bf16_t* Vp, int64_t hrow,
-                                            int64_t key0, int64_t rmax, int h, int r, int g, int ldqk) {
+                                            int64_t key0, int64_t rmax, int h, int r, int g, Lay L) {
+  constexpr int H = D / 32;
 #pragma unroll
   for (int c = 0; c < WinOps<NKW>::MBW; ++c) {
     const int t = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
     const int64_t row = clamp64(hrow + key0 + t, 0, rmax - 1);
-    w.kw[c] = ld16(QK + row * ldqk + D + h * 32 + 8 * g);
+    w.kw[c] = ld16(QK + (H + h) * L.ps + row * L.rs + 8 * g);
   }
   (void)Vp;
 }
@@ -297,7 +310,7 @@ __device__ __forceinline__ float silu2(float y) {
 template <int ELL, int D, int NKW = 0>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
-                                         bool softmax, int r, int g, int ldy = D,
+                                         bool softmax, int r, int g, Lay yl,
                                          const WinOps<NKW>* wo = nullptr, const WinArgs* wa = nullptr) {
   constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
   constexpr int NWS = NKW > 0 ? NKW / 4 : 1;  // window scores per lane
@@ -387,7 +400,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
     }
     if (j >= lo && j < hi) {
       const float out[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
-      st8(Y + (hrow + j) * ldy + h * 32 + 8 * g, out);
+      st8(Y + h * yl.ps + (hrow + j) * yl.rs + 8 * g, out);
     }
   }
 }
@@ -614,29 +627,32 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   const bool softmax = (phi == PHI_SOFTMAX);
 
   HeadOps<ELL> o;
-  load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g);
+  // Q|K and Y are head-planar in HBM: a wave's 16-row slice of one head is
+  // one contiguous 1 KB piece
+  const Lay qkl{32, rmax * 32}, yl{32, (nlr + total_N) * 32};
+  load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g, qkl);
   LState<ELL> st;
   st.init();
   int64_t c0 = lo & ~int64_t(7);
   // chunk operands two chunks ahead of the one being computed (the windowed
   // form, whose own operands take the registers, loads one at a time)
   ChunkOps cur, nxt, nxt2;
-  if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g);
+  if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g, qkl);
   if constexpr (NKW == 0) {
-    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
   }
   for (; c0 < hi; c0 += 32) {
     if constexpr (NKW == 0) {
-      if (c0 + 64 < hi) load_chunk<D>(nxt2, QK, Vp, nlr, c0 + 64, h, do_e, r, g);
+      if (c0 + 64 < hi) load_chunk<D>(nxt2, QK, Vp, nlr, c0 + 64, h, do_e, r, g, qkl);
     }
     if (do_e) {
       if constexpr (NKW > 0) {
         WinOps<NKW> wo;
-        load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, 2 * D);
+        load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, qkl);
         const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
-        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, D, &wo, &wa);
+        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, yl, &wo, &wa);
       } else {
-        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g);
+        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, yl);
       }
     }
     l_branch<ELL>(st, o, cur, c0, lo, hi, softmax, r, g);
@@ -644,7 +660,7 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
       cur = nxt;
       nxt = nxt2;
     } else {
-      if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g);
+      if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
     }
   }
   float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
@@ -723,7 +739,7 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
     }
-    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs);
+    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs, Lay{32, R_pad * 32});
   }
 }
 
@@ -736,7 +752,8 @@ struct PostLds {
 };
 
 template <int D, int DFF, int RPW>
-__global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+__global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(const bf16_t* __restrict__ Y, int64_t yR,
+                                                                             Rows Xres, Rows Out, int64_t nrows,
                                                       const bf16_t* __restrict__ Wo,
                                                       const bf16_t* __restrict__ Wg,
                                                       const bf16_t* __restrict__ Wu,
@@ -764,11 +781,11 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(Row
     for (int rb = 0; rb < RB; ++rb) {
       const int64_t row = row0 + 16 * rb + r;
       const bool ok = row < nrows;
-      const bf16_t* yr = ok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
+      const bf16_t* yr = Y + row * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
       const bf16_t* xr = ok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        yb[rb][kb] = ok ? ld16(yr + kb * 32) : zero8();
+        yb[rb][kb] = ok ? ld16(yr + kb * yR * 32) : zero8();
         const bf16x8 x = ok ? ld16(xr + kb * 32) : zero8();
 #pragma unroll
         for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = static_cast<float>(x[q]);
@@ -909,7 +926,7 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
             const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
             const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                                 acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-            st8(QK + row * (2 * D) + CR * k + 32 * pp + 8 * g, v);
+            st8(QK + ((CR * k) / 32 + pp) * (R_pad * 32) + row * 32 + 8 * g, v);  // head-planar
           }
         }
       } else {
@@ -955,7 +972,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glob_void_t;
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void post_block_stream(Rows Yr, Rows Xres, Rows Out, int64_t nrows,
+__global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __restrict__ Y, int64_t yR,
+                                                            Rows Xres, Rows Out, int64_t nrows,
                                                          const bf16_t* __restrict__ Wo,
                                                          const bf16_t* __restrict__ Wg,
                                                          const bf16_t* __restrict__ Wu,
@@ -1013,11 +1031,11 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(Rows Yr, Rows Xres, 
     bf16x8 yb[1][KB];
     float x1[1][D / 4];
     {
-      const bf16_t* yr = rowok ? row_in<bf16_t>(Yr, row) + 8 * g : nullptr;
+      const bf16_t* yr = Y + row * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
       const bf16_t* xr = rowok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        yb[0][kb] = rowok ? ld16(yr + kb * 32) : zero8();
+        yb[0][kb] = rowok ? ld16(yr + kb * yR * 32) : zero8();
         const bf16x8 x = rowok ? ld16(xr + kb * 32) : zero8();
 #pragma unroll
         for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] = static_cast<float>(x[q]);
@@ -1189,6 +1207,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
   const int rows = ELL + n;
   const bool softmax = (phi == PHI_SOFTMAX);
   const float qs = scale * LOG2E;  // Q carries the logit scale in log2 units
+  const Lay qkl{LQK, 32}, yl{LY, 32};   // row-major LDS rows
   const int nchunks = RT / 32;
 
   // weight prefetch registers: set 0 (w_qkv) and set 1 (post weights)
@@ -1262,7 +1281,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
       }
       if (it & 1) v_part<D>(hb, lq + opaque_zero(), ldd, Vps, row0, r, g);
-      else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, qs, LQK);
+      else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, qs, qkl);
     }
     lds_barrier();
   }
@@ -1282,13 +1301,13 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     for (int it = wv; it < items; it += NW) {
       const int h = it % H, k = it / H;
       HeadOps<ELL> o;
-      load_head_ops<ELL, D>(o, QKs, Vps, 0, h, r, g, LQK);
+      load_head_ops<ELL, D>(o, QKs, Vps, 0, h, r, g, qkl);
       if (k == 0) {
         LState<ELL> st;
         st.init();
         for (int c0 = 0; c0 < n; c0 += 32) {
           ChunkOps ci;
-          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, LQK);
+          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, qkl);
           l_branch<ELL>(st, o, ci, c0, 0, n, softmax, r, g);
         }
         // normalise and write the link rows of Y
@@ -1307,14 +1326,14 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         }
       } else {
         ChunkOps ci;
-        load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g, LQK);
+        load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g, qkl);
         if constexpr (NKW > 0) {
           WinOps<NKW> wo;
-          load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, LQK);
+          load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, qkl);
           const WinArgs wa{0, n, RT, half, Vps, ELL};
-          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, LY, &wo, &wa);
+          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, yl, &wo, &wa);
         } else {
-          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, LY);
+          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, yl);
         }
       }
     }
@@ -1369,7 +1388,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
             for (int kb = 0; kb < KB; ++kb)
               lds_st8f(Xs + (row0 + 16 * rb + r) * XS + kb * 32 + 8 * g, &x1[rb][8 * kb]);
         }
-        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, LQK, qs);
+        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, qkl, qs);
       } else if (do_post) {
 #pragma unroll
         for (int rb = 0; rb < PRB; ++rb) {
