@@ -44,6 +44,10 @@ def compile_flags() -> list[str]:
         "-mcode-object-version=5",
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators in ordinary VGPRs: no accvgpr moves
+        # around every product, and the attention kernels fit two waves per
+        # SIMD
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-Wall", "-Wno-unused-function",
     ]

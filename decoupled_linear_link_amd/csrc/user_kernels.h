@@ -14,6 +14,8 @@
 // all layers in one launch, for histories that fit in LDS).
 #pragma once
 
+#include <type_traits>
+
 #include "mfma_kernels.h"
 
 namespace lime {
@@ -221,7 +223,7 @@ __device__ __forceinline__ void load_head_ops(HeadOps<ELL>& o, const bf16_t* QK,
 
 // Operands of one 32-row chunk of history rows c0 + [0, 32) for head h:
 // Q rows (E-branch B operands), K rows in the L-branch row order (A
-// operands) and two packed V column blocks (B operands).
+// operands) and two packed V column blocks (A operands of V^T P^T).
 struct ChunkOps {
   bf16x8 qe[2], ke[2], ve[2];
 };
@@ -307,10 +309,10 @@ __device__ __forceinline__ float silu2(float y) {
 
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
 // NKW > 0, to their window); rows in [lo, hi) are written to Y.
-template <int ELL, int D, int NKW = 0>
+template <int ELL, int D, bool SM, int NKW = 0>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
-                                         bool softmax, int r, int g, Lay yl,
+                                         int r, int g, Lay yl,
                                          const WinOps<NKW>* wo = nullptr, const WinArgs* wa = nullptr) {
   constexpr int MB = HeadOps<ELL>::MB, KBL = HeadOps<ELL>::KBL;
   constexpr int NWS = NKW > 0 ? NKW / 4 : 1;  // window scores per lane
@@ -343,7 +345,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
       const int64_t e = j + wa->half < wa->u1 - 1 ? j + wa->half : wa->u1 - 1;
       nwin = e > a ? static_cast<int>(e - a) : 0;
     }
-    if (softmax) {
+    if constexpr (SM) {
       float mx = v[0];
 #pragma unroll
       for (int q = 1; q < 4 * MB; ++q) mx = fmaxf(mx, v[q]);
@@ -366,7 +368,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
         }
       }
       sum = rows_sum(sum);
-      const float inv = 1.f / sum;
+      const float inv = __builtin_amdgcn_rcpf(sum);  // sum >= 1 (the max term)
 #pragma unroll
       for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
       if constexpr (NKW > 0) {
@@ -406,8 +408,8 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
 }
 
 // L-branch running state: per link block nb, running max m / denominator l
-// (for the links 16*nb + r of this lane) and acc (links 16*nb + 4*g + q,
-// columns 16*c2 + r).
+// and acc, all for the link 16*nb + r of this lane (acc: columns
+// 16*c2 + 4*g + q), so the rescaling of acc by the new max stays in the lane.
 template <int ELL>
 struct LState {
   static constexpr int MB = ELL / 16;
@@ -429,9 +431,9 @@ struct LState {
 // with silu the accumulators hold sum silu2 * v (the ln 2 factor is applied
 // where they are normalised).  MASK = false: every row of the chunk is in
 // [lo, hi).
-template <int ELL, bool MASK>
+template <int ELL, bool MASK, bool SM>
 __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
-                                              int64_t c0, int64_t lo, int64_t hi, bool softmax, int r, int g) {
+                                              int64_t c0, int64_t lo, int64_t hi, int r, int g) {
   constexpr int MB = HeadOps<ELL>::MB;
   bool valid[8];
 #pragma unroll
@@ -448,7 +450,7 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
 #pragma unroll
       for (int q = 0; q < 4; ++q) p[4 * c + q] = sv[q];
     }
-    if (softmax) {
+    if constexpr (SM) {
       float mc = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -465,30 +467,40 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
       ls = rows_sum(ls);
       st.l[nb] = st.l[nb] * alpha + ls;
       st.m[nb] = mn;
-      // acc rows are links 16*nb + 4*g + jj; their factor sits in lane 4*g + jj
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float f = __shfl(alpha, 4 * g + jj);
-        st.acc[nb][0][jj] *= f;
-        st.acc[nb][1][jj] *= f;
+      for (int q = 0; q < 4; ++q) {
+        st.acc[nb][0][q] *= alpha;
+        st.acc[nb][1][q] *= alpha;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) p[q] = valid[q] ? silu2(p[q]) : 0.f;
     }
-    const bf16x8 pa = pack8(p);
-    st.acc[nb][0] = mma(pa, ci.ve[0], st.acc[nb][0]);
-    st.acc[nb][1] = mma(pa, ci.ve[1], st.acc[nb][1]);
+    // (V^T P^T): P's lane layout (link r, rows 8g..8g+7) is the B operand as
+    // it stands, and the product's columns are the links
+    const bf16x8 pb = pack8(p);
+    st.acc[nb][0] = mma(ci.ve[0], pb, st.acc[nb][0]);
+    st.acc[nb][1] = mma(ci.ve[1], pb, st.acc[nb][1]);
   }
 }
 
-template <int ELL>
+template <int ELL, bool SM>
 __device__ __forceinline__ void l_branch(LState<ELL>& st, const HeadOps<ELL>& o, const ChunkOps& ci,
-                                         int64_t c0, int64_t lo, int64_t hi, bool softmax, int r, int g) {
+                                         int64_t c0, int64_t lo, int64_t hi, int r, int g) {
   if (c0 >= lo && c0 + 32 <= hi)
-    l_branch_rows<ELL, false>(st, o, ci, c0, lo, hi, softmax, r, g);
+    l_branch_rows<ELL, false, SM>(st, o, ci, c0, lo, hi, r, g);
   else
-    l_branch_rows<ELL, true>(st, o, ci, c0, lo, hi, softmax, r, g);
+    l_branch_rows<ELL, true, SM>(st, o, ci, c0, lo, hi, r, g);
+}
+
+// Runs f(std::true_type) for softmax and f(std::false_type) otherwise, so
+// each phi gets straight-line code.
+template <typename F>
+__device__ __forceinline__ void with_phi(bool softmax, F&& f) {
+  if (softmax)
+    f(std::true_type{});
+  else
+    f(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -633,36 +645,43 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g, qkl);
   LState<ELL> st;
   st.init();
-  int64_t c0 = lo & ~int64_t(7);
-  // chunk operands two chunks ahead of the one being computed (the windowed
-  // form, whose own operands take the registers, loads one at a time)
-  ChunkOps cur, nxt, nxt2;
-  if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g, qkl);
-  if constexpr (NKW == 0) {
-    if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
-  }
-  for (; c0 < hi; c0 += 32) {
+  with_phi(softmax, [&](auto phi_tag) {
+    constexpr bool SM = decltype(phi_tag)::value;
+    int64_t c0 = lo & ~int64_t(7);
+    ChunkOps cur, nxt;
+    if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g, qkl);
     if constexpr (NKW == 0) {
-      if (c0 + 64 < hi) load_chunk<D>(nxt2, QK, Vp, nlr, c0 + 64, h, do_e, r, g, qkl);
-    }
-    if (do_e) {
-      if constexpr (NKW > 0) {
-        WinOps<NKW> wo;
-        load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, qkl);
-        const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
-        e_branch<ELL, D, NKW>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, yl, &wo, &wa);
-      } else {
-        e_branch<ELL, D>(o, cur, Y, nlr, c0, lo, hi, h, softmax, r, g, yl);
+      // chunk operands two chunks ahead of the one being computed, in three
+      // buffers that rotate by name
+      ChunkOps nxt2;
+      if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
+      auto step = [&](const ChunkOps& ci, ChunkOps& ahead) {
+        if (c0 + 64 < hi) load_chunk<D>(ahead, QK, Vp, nlr, c0 + 64, h, do_e, r, g, qkl);
+        if (do_e) e_branch<ELL, D, SM>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+        c0 += 32;
+      };
+      while (c0 < hi) {
+        step(cur, nxt2);
+        if (c0 >= hi) break;
+        step(nxt, cur);
+        if (c0 >= hi) break;
+        step(nxt2, nxt);
+      }
+    } else {
+      // the windowed form's own operands take the registers: one chunk at a time
+      for (; c0 < hi; c0 += 32) {
+        if (do_e) {
+          WinOps<NKW> wo;
+          load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, qkl);
+          const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
+          e_branch<ELL, D, SM, NKW>(o, cur, Y, nlr, c0, lo, hi, h, r, g, yl, &wo, &wa);
+        }
+        l_branch<ELL, SM>(st, o, cur, c0, lo, hi, r, g);
+        if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
       }
     }
-    l_branch<ELL>(st, o, cur, c0, lo, hi, softmax, r, g);
-    if constexpr (NKW == 0) {
-      cur = nxt;
-      nxt = nxt2;
-    } else {
-      if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
-    }
-  }
+  });
   float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
@@ -673,11 +692,11 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
       pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
     }
     const float f = softmax ? 1.f : LN2;
+    float* pa = p0 + (16 * nb + r) * 34 + 2 + 4 * g;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        p0[(16 * nb + 4 * g + jj) * 34 + 2 + 16 * c2 + r] = st.acc[nb][c2][jj] * f;
+      for (int q = 0; q < 4; ++q) pa[16 * c2 + q] = st.acc[nb][c2][q] * f;
   }
 }
 
@@ -1305,36 +1324,38 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       if (k == 0) {
         LState<ELL> st;
         st.init();
-        for (int c0 = 0; c0 < n; c0 += 32) {
-          ChunkOps ci;
-          load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, qkl);
-          l_branch<ELL>(st, o, ci, c0, 0, n, softmax, r, g);
-        }
+        with_phi(softmax, [&](auto phi_tag) {
+          for (int c0 = 0; c0 < n; c0 += 32) {
+            ChunkOps ci;
+            load_chunk<D>(ci, QKs, Vps, ELL, c0, h, false, r, g, qkl);
+            l_branch<ELL, decltype(phi_tag)::value>(st, o, ci, c0, 0, n, r, g);
+          }
+        });
         // normalise and write the link rows of Y
 #pragma unroll
         for (int nb = 0; nb < HeadOps<ELL>::MB; ++nb) {
           const float den = softmax ? st.l[nb] : static_cast<float>(n);
+          const float inv = den > 0.f ? (softmax ? 1.f : LN2) / den : 0.f;
+          bf16_t* yr = Ys + (16 * nb + r) * LY + h * 32 + 4 * g;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float dj = __shfl(den, 4 * g + jj);
-            const float inv = dj > 0.f ? (softmax ? 1.f : LN2) / dj : 0.f;
-            const int link = 16 * nb + 4 * g + jj;
+          for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-              Ys[link * LY + h * 32 + 16 * c2 + r] = f32_to_bf16(st.acc[nb][c2][jj] * inv);
-          }
+            for (int q = 0; q < 4; ++q) yr[16 * c2 + q] = f32_to_bf16(st.acc[nb][c2][q] * inv);
         }
       } else {
         ChunkOps ci;
         load_chunk<D>(ci, QKs, Vps, ELL, 32 * (k - 1), h, true, r, g, qkl);
-        if constexpr (NKW > 0) {
-          WinOps<NKW> wo;
-          load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, qkl);
-          const WinArgs wa{0, n, RT, half, Vps, ELL};
-          e_branch<ELL, D, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, yl, &wo, &wa);
-        } else {
-          e_branch<ELL, D>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, softmax, r, g, yl);
-        }
+        with_phi(softmax, [&](auto phi_tag) {
+          constexpr bool SM = decltype(phi_tag)::value;
+          if constexpr (NKW > 0) {
+            WinOps<NKW> wo;
+            load_window<NKW, D>(wo, QKs, Vps, ELL, win_key0(32 * (k - 1), half), RT, h, r, g, qkl);
+            const WinArgs wa{0, n, RT, half, Vps, ELL};
+            e_branch<ELL, D, SM, NKW>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, r, g, yl, &wo, &wa);
+          } else {
+            e_branch<ELL, D, SM>(o, ci, Ys, ELL, 32 * (k - 1), 0, n, h, r, g, yl);
+          }
+        });
       }
     }
     lds_barrier();
