@@ -147,9 +147,10 @@ struct XorPlan {
   bool resident = false;   // matrix-core, one workgroup per user holding all rows
   int64_t nlr = 0, R = 0;  // link rows, all rows
   int64_t R_pad = 0;       // rows of the QK / packed-V buffers (matrix-core path)
-  int S = 1;               // history splits per user
+  int S = 1;               // generic path: history splits per user
   int64_t chunk = 1;       // history rows per split
-  size_t o_x = 0, o_qkv = 0, o_v = 0, o_y = 0, o_h = 0, o_part = 0, total = 0;
+  int64_t G = 0;           // matrix-core path: split slots (an upper bound on the splits)
+  size_t o_x = 0, o_qkv = 0, o_v = 0, o_y = 0, o_h = 0, o_part = 0, o_soff = 0, o_suser = 0, total = 0;
 };
 
 lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
@@ -197,21 +198,21 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
   p.nlr = static_cast<int64_t>(B) * ell;
   p.R = p.nlr + total_N;
   const int dh = d / heads;
-  int64_t S;
   if (p.mfma) {
-    // about 2048 (user, head, split) waves, splits of at least 64 rows
-    S = (2048 + static_cast<int64_t>(B) * heads - 1) / (static_cast<int64_t>(B) * heads);
-    const int64_t smax = (static_cast<int64_t>(max_N) + 63) / 64;
-    if (S > smax) S = smax;
+    // splits of equal row count over all histories (a user's last one
+    // shorter): about 2048 (split, head) waves, at least 64 rows each
+    int64_t c = (total_N * heads + 2047) / 2048;
+    c = (c + 31) / 32 * 32;
+    p.chunk = c < 64 ? 64 : c;
+    p.G = (total_N + p.chunk - 1) / p.chunk + B;  // >= sum over users of max(1, ceil(n_b / chunk))
   } else {
-    S = (static_cast<int64_t>(max_N) + 511) / 512;
+    int64_t S = (static_cast<int64_t>(max_N) + 511) / 512;
+    if (S < 1) S = 1;
+    if (S > 64) S = 64;
+    p.S = static_cast<int>(S);
+    p.chunk = (static_cast<int64_t>(max_N) + S - 1) / S;
+    if (p.chunk < 1) p.chunk = 1;
   }
-  if (S < 1) S = 1;
-  if (S > 64) S = 64;
-  p.S = static_cast<int>(S);
-  p.chunk = (static_cast<int64_t>(max_N) + S - 1) / S;
-  if (p.mfma) p.chunk = (p.chunk + 31) / 32 * 32;
-  if (p.chunk < 1) p.chunk = 1;
   size_t off = 0;
   if (p.mfma) {
     p.R_pad = (p.R + 32 + 31) / 32 * 32;
@@ -219,7 +220,9 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
     p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R_pad) * 2 * d * es);
     p.o_v = off;    off = up256(off + static_cast<size_t>(p.R_pad) * d * es);
     p.o_y = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
-    p.o_part = off; off = up256(off + static_cast<size_t>(B) * heads * p.S * ell * (dh + 2) * 4);
+    p.o_part = off; off = up256(off + static_cast<size_t>(p.G) * heads * ell * mfma::PART_LD * 4);
+    p.o_soff = off; off = up256(off + static_cast<size_t>(B + 1) * 4);
+    p.o_suser = off; off = up256(off + static_cast<size_t>(p.G) * 4);
   } else {
     p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
     p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R) * 3 * d * es);
@@ -310,8 +313,14 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   bf16_t* Vp = reinterpret_cast<bf16_t*>(ws + P.o_v);
   bf16_t* Y = reinterpret_cast<bf16_t*>(ws + P.o_y);
   float* part = reinterpret_cast<float*>(ws + P.o_part);
+  int32_t* soff = reinterpret_cast<int32_t*>(ws + P.o_soff);
+  int32_t* suser = reinterpret_cast<int32_t*>(ws + P.o_suser);
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
+  // the splits of every layer's attention
+  hipLaunchKernelGGL(mfma::split_plan, dim3(1), dim3(mfma::SPLIT_PLAN_NT), 0, st, off, B, total_N, P.chunk,
+                     soff, suser, static_cast<int>(P.G));
+  LIME_CHECK_LAUNCH("split plan");
   // Q|K and Y are head-planar in the workspace (see the kernels' Lay)
   // the projections store Q times the logit scale in log2 units; the
   // attention kernels then work with base-2 exponentials
@@ -356,23 +365,25 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
     {
-      const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * P.S));
+      // one workgroup per (split slot, head group); slots past the last
+      // split return at once
+      const dim3 grid(static_cast<unsigned>(P.G));
       // the windowed form runs at most 4 heads per workgroup (registers)
       constexpr int HBW = H > 4 ? 4 : H;
-      const dim3 grid_w(static_cast<unsigned>(static_cast<int64_t>(B) * P.S * (H / HBW)));
+      const dim3 grid_w(static_cast<unsigned>(P.G * (H / HBW)));
       if (va.half > 0 && full)
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
-                           Vp, Y, part, off, B, P.S, P.chunk, total_N, static_cast<int>(phi), 1, va.half,
+                           Vp, Y, part, off, soff, suser, B, P.chunk, total_N, static_cast<int>(phi), 1, va.half,
                            P.R_pad);
       else
-        hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, B, P.S,
-                           P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
+        hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, soff, suser,
+                           B, P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
     }
     LIME_CHECK_LAUNCH("xor attention (mfma)");
     {
-      const int64_t n = static_cast<int64_t>(B) * H * ELL * 32;
-      hipLaunchKernelGGL((gen::xor_combine<bf16_t, 32>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                         0, st, part, Y, B, ELL, D, H, P.S, int64_t(32), R * 32);
+      const int64_t n = static_cast<int64_t>(B) * H * ELL * 4 * mfma::CSG;
+      hipLaunchKernelGGL((mfma::xor_combine<ELL>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                         part, soff, Y, B, H, R * 32);
       LIME_CHECK_LAUNCH("xor combine");
     }
     const int64_t pw = (rows_post + RPW - 1) / RPW;
@@ -541,10 +552,11 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
     launches = 1;
     snprintf(line, sizeof(line), "user-resident: 1 launch for %d layers, one workgroup per user", layers);
   } else if (P.mfma) {
-    launches = 4 * layers;
+    launches = 4 * layers + 1;
     snprintf(line, sizeof(line),
-             "streaming matrix-core: 4 launches per layer (qkv, xor_attn, combine, post), "
-             "%d splits per user of %lld rows", P.S, static_cast<long long>(P.chunk));
+             "streaming matrix-core: a split plan, then 4 launches per layer (qkv, xor_attn, combine, "
+             "post); splits of %lld history rows, at most %lld splits", static_cast<long long>(P.chunk),
+             static_cast<long long>(P.G));
   } else {
     launches = 6 * layers;
     snprintf(line, sizeof(line),

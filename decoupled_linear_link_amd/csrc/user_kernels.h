@@ -307,6 +307,11 @@ __device__ __forceinline__ float silu2(float y) {
   return y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-y));
 }
 
+// silu2(y) / c in one operation fewer: y / (c + c 2^-y)
+__device__ __forceinline__ float silu2_div(float y, float c) {
+  return y * __builtin_amdgcn_rcpf(__builtin_fmaf(c, __builtin_amdgcn_exp2f(-y), c));
+}
+
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
 // NKW > 0, to their window); rows in [lo, hi) are written to Y.
 template <int ELL, int D, bool SM, int NKW = 0>
@@ -376,12 +381,13 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
         for (int q = 0; q < NWS; ++q) ws[q] *= inv;
       }
     } else {
-      const float inv = NKW > 0 ? LN2 / static_cast<float>(ELL + nwin) : LN2 / ELL;
+      // silu2 * ln 2 / |keys|
+      const float c = NKW > 0 ? static_cast<float>(ELL + nwin) * LOG2E : ELL * LOG2E;
 #pragma unroll
-      for (int q = 0; q < 4 * MB; ++q) v[q] = silu2(v[q]) * inv;
+      for (int q = 0; q < 4 * MB; ++q) v[q] = silu2_div(v[q], c);
       if constexpr (NKW > 0) {
 #pragma unroll
-        for (int q = 0; q < NWS; ++q) ws[q] = ws[q] == -INFINITY ? 0.f : silu2(ws[q]) * inv;
+        for (int q = 0; q < NWS; ++q) ws[q] = ws[q] == -INFINITY ? 0.f : silu2_div(ws[q], c);
       }
     }
     floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
@@ -610,7 +616,63 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
 // Streaming kernels (any history length)
 // ===========================================================================
 
-// XOR attention: one workgroup per (user b, split s) with one wave per head,
+// Splits of the streaming attention.  User b's history is cut into
+// S_b = max(1, ceil(n_b / chunk)) splits of chunk rows (its last one
+// shorter), so every split but the tails carries the same work however
+// ragged the histories are.  split_off[b] = sum of S_b' over b' < b
+// (split_off[B] = the number of splits) and split_user[x] = the user of split
+// x, -1 for x >= split_off[B] up to G.  One workgroup of 1024 threads.
+constexpr int SPLIT_PLAN_NT = 1024;
+constexpr int PART_LD = 36;  // floats per partial row: m, l, 2 spare, acc[32]
+
+__global__ __launch_bounds__(SPLIT_PLAN_NT) void split_plan(const int64_t* __restrict__ off, int B,
+                                                            int64_t total_N, int64_t chunk,
+                                                            int32_t* __restrict__ split_off,
+                                                            int32_t* __restrict__ split_user, int G) {
+  __shared__ int32_t wsum[SPLIT_PLAN_NT / 64];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) {
+    carry_s = 0;
+    split_off[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < B; base += SPLIT_PLAN_NT) {
+    const int b = base + tid;
+    int32_t cnt = 0;
+    if (b < B) {
+      const int64_t u0 = clamp64(off[b], 0, total_N);
+      const int64_t u1 = clamp64(off[b + 1], u0, total_N);
+      const int64_t sb = (u1 - u0 + chunk - 1) / chunk;
+      cnt = sb > 1 ? static_cast<int32_t>(sb) : 1;
+    }
+    // inclusive scan: within the wave, then over the waves
+    int32_t v = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[wv] = v;
+    __syncthreads();
+    int32_t before = carry_s;
+    for (int w = 0; w < wv; ++w) before += wsum[w];
+    // capped at G, which bounds the splits of non-decreasing offsets; with
+    // offsets out of order the users past the cap get no splits
+    const int32_t first = before + v - cnt < G ? before + v - cnt : G;
+    const int32_t last = before + v < G ? before + v : G;
+    if (b < B) {
+      split_off[b + 1] = last;
+      for (int32_t x = first; x < last; ++x) split_user[x] = b;
+    }
+    __syncthreads();
+    if (tid == SPLIT_PLAN_NT - 1) carry_s = last;
+    __syncthreads();
+  }
+  for (int x = carry_s + tid; x < G; x += SPLIT_PLAN_NT) split_user[x] = -1;
+}
+
+// XOR attention: one workgroup per (split x, head group) with one wave per head,
 // so the waves of a workgroup read the same rows at the same time and share
 // each cache line (HB heads per workgroup: all of them, or half of 8 for
 // the windowed form, whose registers need the room).  Writes the E-branch rows of Y and the L-branch partial
@@ -619,23 +681,26 @@ template <int ELL, int H, int NKW = 0, int HB = H>
 __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ QK,
                                                     const bf16_t* __restrict__ Vp,
                                                     bf16_t* __restrict__ Y, float* __restrict__ part,
-                                                    const int64_t* __restrict__ off, int B, int S,
+                                                    const int64_t* __restrict__ off,
+                                                    const int32_t* __restrict__ split_off,
+                                                    const int32_t* __restrict__ split_user, int B,
                                                     int64_t chunk, int64_t total_N,
                                                     int phi, int do_e, int half, int64_t rmax) {
   static_assert(H % HB == 0, "head groups");
   constexpr int D = 32 * H, MB = ELL / 16;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, r = lane & 15;
-  const int s = static_cast<int>(blockIdx.x % S);
-  const int64_t bg = blockIdx.x / S;  // (user, head group)
-  const int h = static_cast<int>(bg % (H / HB)) * HB + (threadIdx.x >> 6);
-  const int b = static_cast<int>(bg / (H / HB));
+  const int64_t x = blockIdx.x / (H / HB);  // split
+  const int h = static_cast<int>(blockIdx.x % (H / HB)) * HB + (threadIdx.x >> 6);
+  const int b = split_user[x];
+  if (b < 0) return;  // past the last split
+  const int64_t s = x - split_off[b];
   const int64_t nlr = static_cast<int64_t>(B) * ELL;
   const int64_t u0 = clamp64(off[b], 0, total_N);
   const int64_t u1 = clamp64(off[b + 1], u0, total_N);
   const int64_t n = u1 - u0;
   const int64_t lo = u0 + clamp64(s * chunk, 0, n);
-  const int64_t hi = (s == S - 1) ? u1 : u0 + clamp64((s + 1) * chunk, 0, n);
+  const int64_t hi = u0 + clamp64((s + 1) * chunk, 0, n);
   const bool softmax = (phi == PHI_SOFTMAX);
 
   HeadOps<ELL> o;
@@ -682,21 +747,92 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
       }
     }
   });
-  float* p0 = part + (((static_cast<int64_t>(b) * H + h) * S + s) * ELL) * 34;
+  float* p0 = part + ((x * H + h) * ELL) * PART_LD;
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
     // partials in natural units: max * ln 2; silu sums * ln 2
+    float* pl = p0 + (16 * nb + r) * PART_LD;
     if (g == 0) {
-      float* pl = p0 + (16 * nb + r) * 34;
       pl[0] = softmax ? st.m[nb] * LN2 : 0.f;
       pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
     }
     const float f = softmax ? 1.f : LN2;
-    float* pa = p0 + (16 * nb + r) * 34 + 2 + 4 * g;
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
+      *reinterpret_cast<floatx4*>(pl + 4 + 16 * c2 + 4 * g) =
+          floatx4{st.acc[nb][c2][0] * f, st.acc[nb][c2][1] * f, st.acc[nb][c2][2] * f, st.acc[nb][c2][3] * f};
+  }
+}
+
+// Merge of the split partials into the link rows of Y (head-planar, row
+// stride 32, head stride yps).  CSG consecutive threads share one output
+// octet (b, h, link k, columns 8 cq ..): thread t folds the splits
+// x0 + t, x0 + t + CSG, ... of user b (four per round, with a running max),
+// then the group merges its CSG partial states by lane exchanges.
+constexpr int CSG = 8;
+
+template <int ELL>
+__global__ __launch_bounds__(256) void xor_combine(const float* __restrict__ part,
+                                                   const int32_t* __restrict__ split_off,
+                                                   bf16_t* __restrict__ Y, int B, int H, int64_t yps) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int t = static_cast<int>(gid % CSG);
+  const int64_t oi = gid / CSG;
+  // a group's CSG lanes leave together (the block size is a multiple of CSG)
+  if (oi >= static_cast<int64_t>(B) * H * ELL * 4) return;
+  const int cq = static_cast<int>(oi & 3);
+  const int k = static_cast<int>((oi >> 2) % ELL);
+  const int h = static_cast<int>((oi / (4 * ELL)) % H);
+  const int b = static_cast<int>(oi / (4 * ELL * static_cast<int64_t>(H)));
+  const int32_t x0 = split_off[b], x1 = split_off[b + 1];
+  const int64_t xs = static_cast<int64_t>(H) * ELL * PART_LD;  // split stride
+  const float* p = part + (static_cast<int64_t>(h) * ELL + k) * PART_LD;
+  float M = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto fold = [&](float m2, float d2, const float* n2) {
+    const float mn = fmaxf(M, m2);
+    const float f1 = M == -INFINITY ? 0.f : __expf(M - mn);
+    const float f2 = m2 == -INFINITY ? 0.f : __expf(m2 - mn);
+    M = mn;
+    den = den * f1 + d2 * f2;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pa[16 * c2 + q] = st.acc[nb][c2][q] * f;
+    for (int q = 0; q < 8; ++q) num[q] = num[q] * f1 + n2[q] * f2;
+  };
+  for (int32_t xb = x0 + t; xb < x1; xb += 4 * CSG) {
+    float2 ml[4];
+    float a[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int32_t x = xb + u * CSG;
+      const int64_t xx = x < x1 ? x : x1 - 1;  // repeats are masked below
+      const float* pu = p + xx * xs;
+      ml[u] = *reinterpret_cast<const float2*>(pu);
+      const floatx4 a0 = *reinterpret_cast<const floatx4*>(pu + 4 + 8 * cq);
+      const floatx4 a1 = *reinterpret_cast<const floatx4*>(pu + 8 + 8 * cq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[u][q] = a0[q];
+        a[u][4 + q] = a1[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (xb + u * CSG < x1) fold(ml[u].x, ml[u].y, a[u]);
+  }
+#pragma unroll
+  for (int o = 1; o < CSG; o <<= 1) {
+    float n2[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) n2[q] = __shfl_xor(num[q], o);
+    const float m2 = __shfl_xor(M, o), d2 = __shfl_xor(den, o);
+    fold(m2, d2, n2);
+  }
+  if (t == 0) {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = num[q] * inv;
+    st8(Y + h * yps + (static_cast<int64_t>(b) * ELL + k) * 32 + 8 * cq, o);
   }
 }
 
