@@ -119,3 +119,29 @@ def test_single_candidate_and_users_without_candidates(L, dt, ell, d, H):
         torch.cuda.synchronize()
         ref, _ = O.cand_score(cache, lp, ids, coff)
         assert_close(host_f64(out), ref, dt, f"single candidate {lens} {dt}")
+
+
+@pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
+def test_streaming_splits_over_many_users(L, phi):
+    """More users than the split plan scans in one pass (1024), ragged and
+    partly empty histories, one user far longer than the rest (many splits
+    against one), on the streaming kernels (a large max_N hint); the oracle
+    checks users from both scan passes, the long user and empty ones."""
+    rng = np.random.default_rng(21)
+    B, ell, d, H = 1500, 32, 64, 2
+    lens = rng.integers(0, 25, size=B)
+    lens[::7] = 0
+    lens[1234] = 3000
+    off, lc, hs, ws = _case(600, B, ell, d, 1, d, lens.tolist(), "bf16")
+    scale = (d // H) ** -0.5
+    print(f"streaming splits: B={B} total_N={int(off[-1])} {phi}", flush=True)
+    lp, ho = L.xor_fwd(dev(lc), dev(hs), dev(off), dev_weights(ws), heads=H, phi=phi, scale=scale,
+                       max_N=4096, want_hist=True)
+    torch.cuda.synchronize()
+    users = [0, 1, 7, 500, 1023, 1024, 1025, 1234, 1400, B - 1]
+    ref, href = O.xor_fwd(lc, hs, off, ws, H, scale, phi, users=users)
+    assert_close(host_f64(lp)[users], ref, "bf16", f"L^P many users {phi}")
+    hos = host_f64(ho)
+    for u, hr in zip(users, href):
+        if len(hr):
+            assert_close(hos[off[u]:off[u + 1]], hr, "bf16", f"hist_out user {u} {phi}")
