@@ -145,3 +145,19 @@ def test_streaming_splits_over_many_users(L, phi):
     for u, hr in zip(users, href):
         if len(hr):
             assert_close(hos[off[u]:off[u + 1]], hr, "bf16", f"hist_out user {u} {phi}")
+
+
+@pytest.mark.parametrize("max_n", [64, 4096])
+def test_out_of_order_offsets_stay_in_bounds(L, max_n):
+    """Offsets that break the prefix-sum precondition (decreasing, and
+    summing past total_N) give unspecified outputs but must not fault: the
+    user-resident kernel (max_N = 64) and the streaming kernels (4096), whose
+    split plan then caps the splits."""
+    B, ell, d, H = 4, 32, 64, 2
+    off, lc, hs, ws = _case(700, B, ell, d, 2, d, [100, 100, 100, 100], "bf16")
+    bad = np.array([0, 300, 100, 400, 400], dtype=np.int64)
+    print(f"out-of-order offsets max_N={max_n}", flush=True)
+    lp, ho = L.xor_fwd(dev(lc), dev(hs), dev(bad), dev_weights(ws), heads=H, phi="softmax",
+                       max_N=max_n, want_hist=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lp.float()).all() and torch.isfinite(ho.float()).all()
