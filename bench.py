@@ -13,9 +13,12 @@ time; users encoded/s and items cached/s are reported alongside.  The K
 timed steps are captured in one HIP graph and replayed once (every kernel
 of every step is a graph node; --no-graph launches them eagerly instead).  The `roofline` object is
 for the kernel with the largest share of step time, its duration measured
-with HIP events on the launch stream around a graph of K back-to-back calls;
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload.
+with HIP events on the launch stream around a graph of K back-to-back calls
+(per-call times are the median of 5 such graphs, the minimum alongside);
+`scoring` has candidate scoring cold (each call after a 512 MiB write and a
+512 MiB read that evict L2 and the Infinity Cache) and warm, for the
+workload's ids and for a uniform-id control with no reuse; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -140,20 +143,28 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
 
-    # ---- per-call average duration: HIP events on the launch stream around
-    # a graph of K back-to-back calls (no host gaps between the kernels)
-    calls = {"lime_xor_fwd": user, "lime_qk_cache_build": build, "lime_cand_score": score}
-    call_ms = {}
-    for k, fn in calls.items():
-        g = capture(fn, args.steps)
+    def time_calls(fn, reps, repeats=5):
+        """Per-call milliseconds (median, min over `repeats`) from HIP events
+        on the launch stream around a graph of `reps` back-to-back calls (no
+        host gaps between the kernels; warm caches)."""
+        g = capture(fn, reps)
         g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        call_ms[k] = e0.elapsed_time(e1) / args.steps
+        ts = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
         del g
+        return float(np.median(ts)), float(min(ts))
+
+    # ---- per-call duration of the three calls
+    calls = {"lime_xor_fwd": user, "lime_qk_cache_build": build, "lime_cand_score": score}
+    call_ms, call_min_ms = {}, {}
+    for k, fn in calls.items():
+        call_ms[k], call_min_ms[k] = time_calls(fn, args.steps)
 
     # roofline of the kernel with the largest share of step time among the
     # calls that are one kernel launch (lime_xor_fwd is one launch on the
@@ -189,8 +200,55 @@ def main():
     per_call = {}
     for k, v in algo.items():
         tk = call_ms[k] * 1e-3
-        per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "GB/s": round(v["bytes"] / tk / 1e9, 1),
+        per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "us_min": round(call_min_ms[k] * 1e3, 2),
+                       "GB/s": round(v["bytes"] / tk / 1e9, 1),
                        "TFLOP/s": round(v["flops"] / tk / 1e12, 2)}
+
+    # ---- scoring cold and with no id reuse.  Cold: every timed call follows
+    # a 512 MiB write and then a 512 MiB read of another buffer, which evict
+    # L2 and the 256 MB Infinity Cache and leave them clean (after the write
+    # alone its dirty lines would be written back during the timed call);
+    # the call is timed alone between HIP events, queued behind that work so
+    # no host latency counts; median and min of 20.  The uniform-id control
+    # draws the same number of candidates uniformly over the catalogue
+    # (seeded), so nearly every gathered cache row is distinct and crosses HBM.
+    scoring = None
+    if not args.no_extras:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        rbuf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        sink = []
+
+        def cold_calls(fn, n=20):
+            ts = []
+            for _ in range(n):
+                scratch.fill_(1)
+                sink.append(rbuf.sum())
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts)), float(min(ts))
+
+        ids_u = dev(np.random.default_rng(20260).integers(0, w.n_items, size=n_cand, dtype=np.int64))
+
+        def score_uniform():
+            L.cand_score(cache, lp, ids_u, coff_d, out=out)
+
+        cs_bytes = algo["lime_cand_score"]["bytes"]
+
+        def entry(med, mn):
+            return {"us": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                    "candidates_per_s": round(n_cand / (med * 1e-3), 1),
+                    "GB/s": round(cs_bytes / (med * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(cs_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+        scoring = {"zipf_cold": entry(*cold_calls(score)),
+                   "uniform_cold": entry(*cold_calls(score_uniform)),
+                   "uniform_warm": entry(*time_calls(score_uniform, args.steps)),
+                   "zipf_warm": entry(call_ms["lime_cand_score"], call_min_ms["lime_cand_score"])}
+        del scratch, rbuf, sink
 
     # ---- the pages' other variants (not part of the step): the user-side
     # LIME-MHA and LIME-XOR+Window; int8 cache build and scoring, uncached
@@ -233,28 +291,13 @@ def main():
                       ("lime_xor_fwd_variant[xor_window]", user_variant("xor_window"))):
             fn()
             torch.cuda.synchronize()
-            g = capture(fn, args.steps)
-            g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            t_ms = e0.elapsed_time(e1) / args.steps
-            del g
-            extras[k] = {"us": round(t_ms * 1e3, 2), "users_per_s": round(w.B / (t_ms * 1e-3), 1)}
+            t_ms, t_min = time_calls(fn, args.steps)
+            extras[k] = {"us": round(t_ms * 1e3, 2), "us_min": round(t_min * 1e3, 2),
+                         "users_per_s": round(w.B / (t_ms * 1e-3), 1)}
         for k, fn in (("lime_qk_cache_build_i8", build_i8), ("lime_cand_score_i8", score_i8),
                       ("lime_cand_score_uncached", score_uncached)):
-            g = capture(fn, args.steps)
-            g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            t_ms = e0.elapsed_time(e1) / args.steps
-            del g
-            extras[k] = {"us": round(t_ms * 1e3, 2),
+            t_ms, t_min = time_calls(fn, args.steps)
+            extras[k] = {"us": round(t_ms * 1e3, 2), "us_min": round(t_min * 1e3, 2),
                          "GB/s": round(ex_bytes[k] / (t_ms * 1e-3) / 1e9, 1),
                          "per_s": round((w.n_items if "build" in k else n_cand) / (t_ms * 1e-3), 1)}
 
@@ -310,6 +353,7 @@ def main():
         "items_per_s": w.n_items / (ms_step * 1e-3),
         "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
         "per_call": per_call,
+        "scoring": scoring,
         "variants": extras,
         "xor_fwd_plan": plan,
         "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
@@ -368,11 +412,24 @@ def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
     per-part rates are scaled to one whole step."""
     import oracle.lime_oracle as O
     import workloads as W
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in pools] or [1])
+        blas = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                         for p in pools if p.get("user_api") == "blas") or "none"
     except Exception:
         cores = 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     off = ui["hist_offsets"]
     frac = 1.0 / 3.0
     # users: a prefix of users
@@ -408,6 +465,7 @@ def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
     n_cand = len(ids)
     t_step = t_user * w.B + t_item * w.n_items + t_cand * n_cand
     return {"value": n_cand / t_step, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"{nu} users, {ni} catalogue items, {int(coff[nc_users])} candidates; "
                       "per-part times scaled to one whole step",
             "users_per_s": 1.0 / t_user, "items_per_s": 1.0 / t_item,

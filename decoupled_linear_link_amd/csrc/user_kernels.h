@@ -672,11 +672,12 @@ __global__ __launch_bounds__(SPLIT_PLAN_NT) void split_plan(const int64_t* __res
   for (int x = carry_s + tid; x < G; x += SPLIT_PLAN_NT) split_user[x] = -1;
 }
 
-// XOR attention: one workgroup per (split x, head group) with one wave per head,
-// so the waves of a workgroup read the same rows at the same time and share
-// each cache line (HB heads per workgroup: all of them, or half of 8 for
-// the windowed form, whose registers need the room).  Writes the E-branch rows of Y and the L-branch partial
-// [ell][2 + 32] (max, denominator, acc) of (b, h, s).
+// XOR attention: one workgroup per (split x, head group) with one wave per
+// head, so the waves of a workgroup read the same rows at the same time and
+// share each cache line (HB heads per workgroup: all of them, or at most 4
+// for the windowed form, whose registers need the room).  Writes the
+// E-branch rows of Y and the L-branch partial rows [ell][PART_LD] (max,
+// denominator, 2 spare, acc) of (split x, head h).
 template <int ELL, int H, int NKW = 0, int HB = H>
 __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ QK,
                                                     const bf16_t* __restrict__ Vp,
@@ -962,12 +963,13 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
 
 // ---------------------------------------------------------------------------
 // Weight-streaming variants for widths whose weights do not fit in LDS
-// (d = 256).  A workgroup of 8 waves takes a tile of rows (32 per wave for
-// the projection, 16 per wave for the post-attention block) and streams
-// the weights through two LDS buffers of 64 padded rows: while the waves
-// multiply their register-resident rows by chunk c, every thread loads
-// chunk c+1 into registers and writes it to the other buffer.  Weight
-// traffic from L2 is then one pass per tile instead of one per wave.
+// (d = 256).  A workgroup takes a tile of rows held in registers and
+// streams the weights through two LDS buffers of 64-row chunks, chunk c + 1
+// loading while the waves multiply by chunk c, so weight traffic from L2 is
+// one pass per tile instead of one per wave.  The projection (8 waves, 32
+// rows each) loads chunks through registers into padded rows; the
+// post-attention block (4 waves, 16 rows each) loads them straight into LDS
+// into unpadded rows with swizzled 16-byte slots.
 // ---------------------------------------------------------------------------
 template <int D>
 struct StreamCfg {
@@ -1273,14 +1275,15 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __rest
 // launch, for users whose ell + N_b rows fit in LDS.  Local rows: [0, ell)
 // links, [ell, ell + N_b) history, zero rows up to RT (multiple of 32).
 //   Xs  [RT][D + 4] float32  residual stream (padded rows)
-//   QKs [RT][2D] bf16 ;  Vps [RT/8][D][8] bf16 ;  Ys [RT][D] bf16
+//   QKs [RT][2D + 8] bf16 (Q | K) ;  Vps [RT/8][D][8] bf16 ;  Ys [RT][D + 8] bf16
 //   (D <= 64) one layer's weights, rows padded by 16 bytes:
 //   Wq [3D][D+8] (w_qkv) ; Wp [4D][D+8] (w_o, w_gate, w_up, w_down)
-// Phases per layer, separated by barriers: LN+QKV (items: 32-row chunk x
-// {Q|K, V}), attention (items: per head the L-branch and each 32-row
-// E-branch chunk), post-attention block (items: 16-row blocks).  The next
-// layer's weights are loaded into registers while the current layer runs
-// and written to LDS once their region is free.
+// Phases, separated by barriers: layer 0's LN + QKV (items: 32-row chunk x
+// {Q|K, V}); then per layer the attention (items: per head the L-branch and
+// each 32-row E-branch chunk) and the post-attention block (items: 16-row
+// blocks), each block followed in registers by the next layer's LN + QKV
+// of the same rows.  The next layer's weights are loaded into registers
+// while the current layer runs and written to LDS once their region is free.
 // ===========================================================================
 constexpr int RES_MAX_LAYERS = 16;
 // per-layer weight pointers passed by value: w_qkv, w_o, w_gate, w_up, w_down
