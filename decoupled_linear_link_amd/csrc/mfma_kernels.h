@@ -85,6 +85,26 @@ __device__ __forceinline__ void st8_stream(bf16_t* p, const float* v) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, o), reinterpret_cast<u32x4_t*>(p));
 }
 
+// phi in log2 units.  A logit x = scale * s is used as y = x log2(e):
+//   softmax  2^(y - max y)                 (the same weights)
+//   silu2(y) = y / (1 + 2^-y) = SiLU(x) / ln 2, the ln 2 going into the
+//   normaliser.  Scaling by scale*log2(e) once replaces the scaling and the
+//   base-e conversion of every exponential.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_f(float y) { return __builtin_amdgcn_exp2f(y); }
+
+__device__ __forceinline__ float silu2(float y) {
+  return y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-y));
+}
+
+// silu2(y) / c in one operation fewer: y / (c + c 2^-y).  With
+// c = n log2(e) this is SiLU(x) / n.
+__device__ __forceinline__ float silu2_div(float y, float c) {
+  return y * __builtin_amdgcn_rcpf(__builtin_fmaf(c, __builtin_amdgcn_exp2f(-y), c));
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
@@ -159,11 +179,13 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
                                                int64_t n_items, int H, int head, void* __restrict__ cache_out,
                                                float* __restrict__ qscale, int g) {
   constexpr int MB = ELL / 16;
+  // logits in log2 units
+  const float k = scale * LOG2E;
   float v[4 * MB];
 #pragma unroll
   for (int c = 0; c < MB; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[4 * c + j] = acc[c][j] * scale;
+    for (int j = 0; j < 4; ++j) v[4 * c + j] = acc[c][j] * k;
   if (phi == PHI_SOFTMAX) {
     float mx = v[0];
 #pragma unroll
@@ -172,17 +194,18 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < 4 * MB; ++q) {
-      v[q] = __expf(v[q] - mx);
+      v[q] = exp2_f(v[q] - mx);
       s += v[q];
     }
     s = rows_sum(s);
-    const float inv = 1.f / s;
+    const float inv = __builtin_amdgcn_rcpf(s);  // s >= 1 (the max term)
 #pragma unroll
     for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
   } else {
-    constexpr float inv = 1.f / ELL;
+    // SiLU(x) / ell
+    constexpr float c = ELL * LOG2E;
 #pragma unroll
-    for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+    for (int q = 0; q < 4 * MB; ++q) v[q] = silu2_div(v[q], c);
   }
   if constexpr (I8) {
     int8_t qv[4 * MB];
@@ -508,6 +531,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
     ldk = D;
   }
   const bool softmax = (phi == PHI_SOFTMAX);
+  const float k2 = scale * LOG2E;
   const int64_t ntiles = (total_M + 15) >> 4;
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
   const int64_t t0 = gw * tiles_per_wave;
@@ -544,7 +568,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) acc = mma(ld16(kr + kb * 32), tb[kb], acc);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[4 * c + q] = acc[q] * scale;
+        for (int q = 0; q < 4; ++q) v[4 * c + q] = acc[q] * k2;  // log2 units
       }
       if (softmax) {
         float mx = v[0];
@@ -554,17 +578,17 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
         float sum = 0.f;
 #pragma unroll
         for (int q = 0; q < 4 * MB; ++q) {
-          v[q] = __expf(v[q] - mx);
+          v[q] = exp2_f(v[q] - mx);
           sum += v[q];
         }
         sum = rows_sum(sum);
-        const float inv = 1.f / sum;
+        const float inv = __builtin_amdgcn_rcpf(sum);  // sum >= 1 (the max term)
 #pragma unroll
         for (int q = 0; q < 4 * MB; ++q) v[q] *= inv;
       } else {
-        constexpr float inv = 1.f / ELL;
+        constexpr float c = ELL * LOG2E;  // SiLU(x) / ell
 #pragma unroll
-        for (int q = 0; q < 4 * MB; ++q) v[q] = silu_f(v[q]) * inv;
+        for (int q = 0; q < 4 * MB; ++q) v[q] = silu2_div(v[q], c);
       }
 #pragma unroll
       for (int kb = 0; kb < KBL; ++kb) {

@@ -292,25 +292,9 @@ __device__ __forceinline__ bf16x8 window_v(const WinArgs& wa, int64_t key0, int 
   return ld16(wa.Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
 }
 
-// phi in log2 units.  The projections store Q multiplied by scale*log2(e),
-// so a score y is the logit x in log2 units (x = y ln 2):
-//   softmax  2^(y - max y)                 (the same weights)
-//   silu2(y) = y / (1 + 2^-y) = SiLU(x) / ln 2, the ln 2 going into the
-//   normaliser.  Two VALU ops per logit fewer than scaling every logit and
-//   converting to base e.
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
-
-__device__ __forceinline__ float exp2_f(float y) { return __builtin_amdgcn_exp2f(y); }
-
-__device__ __forceinline__ float silu2(float y) {
-  return y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-y));
-}
-
-// silu2(y) / c in one operation fewer: y / (c + c 2^-y)
-__device__ __forceinline__ float silu2_div(float y, float c) {
-  return y * __builtin_amdgcn_rcpf(__builtin_fmaf(c, __builtin_amdgcn_exp2f(-y), c));
-}
+// phi in log2 units (exp2_f, silu2 and silu2_div are defined with the
+// cache kernels): the projections store Q multiplied by scale*log2(e), so a
+// score y is the logit x in log2 units.
 
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
 // NKW > 0, to their window); rows in [lo, hi) are written to Y.
