@@ -333,6 +333,9 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     const Rows Xin = (l == 0) ? Rows{const_cast<void*>(links_ctx), const_cast<void*>(hist), nlr, D}
                      : va.links_only ? Rows{X, const_cast<void*>(hist), nlr, D} : Xws;
     const Rows Xout = last ? Rows{links_pers, hist_out, nlr, D} : Xws;
+    // history rows need Q only for their own attention (the E-branch); the
+    // links always need it
+    const int64_t q_rows = full ? P.R_pad : nlr;
     if constexpr (D <= 128) {
       // weights staged in LDS, persistent workgroups (one per CU)
       auto k = mfma::qkv_proj_lds<D>;
@@ -347,7 +350,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
       if (grid > need) grid = need;
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs);
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
     } else {
       // weights streamed through LDS, persistent workgroups
       auto k = mfma::qkv_proj_stream<D>;
@@ -361,7 +364,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       if (grid > ntiles) grid = ntiles;
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs);
+                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
     }
     LIME_CHECK_LAUNCH("qkv projection (mfma)");
     {

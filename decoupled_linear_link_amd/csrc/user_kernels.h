@@ -82,10 +82,10 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 template <int D>
 __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
                                         int ldw, bf16_t* QK, int64_t row0, int r, int g, float qs,
-                                        Lay L) {
+                                        Lay L, bool with_q = true) {
   constexpr int KB = D / 32;
 #pragma unroll 2
-  for (int p = 0; p < 2 * D / 32; ++p) {
+  for (int p = with_q ? 0 : D / 32; p < 2 * D / 32; ++p) {
     floatx4 acc[2][2] = {};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -130,8 +130,8 @@ __device__ __forceinline__ void v_part(const bf16x8 (&hb)[2][D / 32], const bf16
 template <int D>
 __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const bf16_t* __restrict__ W,
                                           int ldw, bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, float qs,
-                                          Lay L) {
-  qk_part<D>(hb, W, ldw, QK, row0, r, g, qs, L);
+                                          Lay L, bool with_q = true) {
+  qk_part<D>(hb, W, ldw, QK, row0, r, g, qs, L, with_q);
   v_part<D>(hb, W, ldw, Vp, row0, r, g);
 }
 
@@ -846,7 +846,7 @@ template <int D>
 __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64_t R, int64_t R_pad,
                                                     const bf16_t* __restrict__ W,
                                                     bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
-                                                    float qs) {
+                                                    float qs, int64_t q_rows) {
   constexpr int KB = D / 32, NW = QkvLds<D>::NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
@@ -879,7 +879,8 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
     }
-    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs, Lay{32, R_pad * 32});
+    // Q only for rows below q_rows (a multiple of 32): the rest need K and V
+    qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs, Lay{32, R_pad * 32}, row0 < q_rows);
   }
 }
 
@@ -994,7 +995,7 @@ template <int D>
 __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_t R_pad,
                                                        const bf16_t* __restrict__ W,
                                                        bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
-                                                       float qs) {
+                                                       float qs, int64_t q_rows) {
   using C = StreamCfg<D>;
   constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW;
   constexpr int NCH = 3 * D / CR, NQK = 2 * D / CR;
@@ -1045,7 +1046,8 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
     const bool more = c + 1 < total;
     if (more) chunk_load<D>(reg, W, static_cast<int>(((c + 1) % NCH) * CR), tid);
     const bf16_t* wb = buf0 + (c & 1) * (CR * LDW) + opaque_zero();
-    if (active) {
+    // Q columns only for rows below q_rows (a multiple of 32)
+    if (active && (CR * k >= D || row0 < q_rows)) {
       if (k < NQK) {
         // output columns [64k, 64k + 64) of Q|K: two 32-column pairs
 #pragma unroll
