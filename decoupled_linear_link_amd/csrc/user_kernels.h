@@ -141,7 +141,8 @@ __device__ __forceinline__ void qkv_chunk(const bf16x8 (&hb)[2][D / 32], const b
 // pieces of 4 rows of one column in the packed layout (row0 a multiple of 8).
 template <int D, int RB>
 __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16_t* __restrict__ W, int ldw,
-                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, Lay L, float qs) {
+                                         bf16_t* QK, bf16_t* Vp, int64_t row0, int r, int g, Lay L, float qs,
+                                         bool with_q = true) {
   constexpr int KB = D / 32;
   bf16x8 hb[RB][KB];
 #pragma unroll
@@ -154,7 +155,7 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
     for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
   }
 #pragma unroll 2
-  for (int p = 0; p < 2 * D / 32; ++p) {
+  for (int p = with_q ? 0 : D / 32; p < 2 * D / 32; ++p) {
     floatx4 acc[2][RB] = {};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -1534,7 +1535,9 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
             for (int kb = 0; kb < KB; ++kb)
               lds_st8f(Xs + (row0 + 16 * rb + r) * XS + kb * 32 + 8 * g, &x1[rb][8 * kb]);
         }
-        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, qkl, qs);
+        // history rows need Q next layer only for their own attention
+        const bool next_full = !links_only && (l + 2 < layers || hist_out != nullptr);
+        qkv_rows<D, PRB>(x1, lq_next + opaque_zero(), ldd, QKs, Vps, row0, r, g, qkl, qs, row0 < ELL || next_full);
       } else if (do_post) {
 #pragma unroll
         for (int rb = 0; rb < PRB; ++rb) {
