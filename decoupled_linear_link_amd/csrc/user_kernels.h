@@ -856,8 +856,15 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int64_t nblk = R_pad / 32;
-  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nblk;
-       blk += static_cast<int64_t>(gridDim.x) * NW) {
+  // whole rounds of 32-row blocks over all the waves; after at least one
+  // such round a short remainder (its 16-row halves fit one round) is taken
+  // as halves by twice as many waves, spread over the workgroups, so no wave
+  // runs a lone extra full block (a half costs most of a block: the chain is
+  // latency-bound, so a split pays only there)
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * NW;
+  int64_t nfull = nblk / nw * nw;
+  if (nfull == 0 || 2 * (nblk - nfull) > nw) nfull = nblk;
+  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nfull; blk += nw) {
     const int64_t row0 = blk * 32;
     bf16x8 hb[2][KB];
 #pragma unroll
@@ -882,6 +889,19 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
     }
     // Q only for rows below q_rows (a multiple of 32): the rest need K and V
     qkv_chunk<D>(hb, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, qs, Lay{32, R_pad * 32}, row0 < q_rows);
+  }
+  for (int64_t hid = static_cast<int64_t>(w) * gridDim.x + blockIdx.x; hid < 2 * (nblk - nfull); hid += nw) {
+    const int64_t row0 = nfull * 32 + 16 * hid;
+    const int64_t row = row0 + r;
+    float x[1][D / 4];
+    const bf16_t* xr = row < R ? row_in<bf16_t>(X, row) + 8 * g : nullptr;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 v = xr ? ld16(xr + kb * 32) : zero8();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[0][8 * kb + j] = static_cast<float>(v[j]);
+    }
+    qkv_rows<D, 1>(x, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, Lay{32, R_pad * 32}, qs, row0 < q_rows);
   }
 }
 
@@ -913,14 +933,13 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
   lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t nblk = (nrows + RPW - 1) / RPW;
-  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nblk;
-       blk += static_cast<int64_t>(gridDim.x) * NW) {
-    const int64_t row0 = blk * RPW;
-    bf16x8 yb[RB][KB];
-    float x1[RB][D / 4];
+  // the post block of NB 16-row blocks from row0
+  auto rows_block = [&](auto nb_tag, int64_t row0) {
+    constexpr int NB = decltype(nb_tag)::value;
+    bf16x8 yb[NB][KB];
+    float x1[NB][D / 4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < NB; ++rb) {
       const int64_t row = row0 + 16 * rb + r;
       const bool ok = row < nrows;
       const bf16_t* yr = Y + row * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
@@ -934,9 +953,9 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
       }
     }
     const int z = opaque_zero();
-    post_rows<D, DFF, RB>(yb, x1, Wol + z, Wgl + z, Wul + z, Wdl + z, D + 8, DFF + 8, r, g);
+    post_rows<D, DFF, NB>(yb, x1, Wol + z, Wgl + z, Wul + z, Wdl + z, D + 8, DFF + 8, r, g);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+    for (int rb = 0; rb < NB; ++rb) {
       const int64_t row = row0 + 16 * rb + r;
       if (row >= nrows) continue;
       bf16_t* orow = row_out<bf16_t>(Out, row);
@@ -944,7 +963,19 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
 #pragma unroll
       for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[rb][8 * p]);
     }
-  }
+  };
+  // whole rounds of RPW-row blocks over all the waves; after at least one
+  // such round a short remainder (its 16-row blocks fit one round) is taken
+  // as 16-row blocks by more waves, spread over the workgroups, so no wave
+  // runs a lone extra full block
+  const int64_t nblk = (nrows + RPW - 1) / RPW;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * NW;
+  int64_t nfull = nblk / nw * nw;
+  if (nfull == 0 || (RPW / 16) * (nblk - nfull) > nw) nfull = nblk;
+  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * NW + w; blk < nfull; blk += nw)
+    rows_block(std::integral_constant<int, RB>{}, blk * RPW);
+  for (int64_t hid = static_cast<int64_t>(w) * gridDim.x + blockIdx.x; nfull * RPW + 16 * hid < nrows; hid += nw)
+    rows_block(std::integral_constant<int, 1>{}, nfull * RPW + 16 * hid);
 }
 
 // ---------------------------------------------------------------------------
