@@ -494,6 +494,12 @@ __device__ __forceinline__ void with_phi(bool softmax, F&& f) {
     f(std::false_type{});
 }
 
+// The same for any runtime flag.
+template <typename F>
+__device__ __forceinline__ void with_flag(bool b, F&& f) {
+  with_phi(b, static_cast<F&&>(f));
+}
+
 // ---------------------------------------------------------------------------
 // Post-attention block on RB row blocks of 16 rows (lane (r, g) of block rb
 // carries one row, columns 32*p + 8*g .. +8 of every 32-column block):
@@ -696,42 +702,57 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g, qkl);
   LState<ELL> st;
   st.init();
+  // phi and the E-branch switch as compile-time flags: straight-line chunk
+  // loops with no conditional loads
   with_phi(softmax, [&](auto phi_tag) {
-    constexpr bool SM = decltype(phi_tag)::value;
-    int64_t c0 = lo & ~int64_t(7);
-    ChunkOps cur, nxt;
-    if (c0 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0, h, do_e, r, g, qkl);
-    if constexpr (NKW == 0) {
-      // chunk operands two chunks ahead of the one being computed, in three
-      // buffers that rotate by name
-      ChunkOps nxt2;
-      if (c0 + 32 < hi) load_chunk<D>(nxt, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
-      auto step = [&](const ChunkOps& ci, ChunkOps& ahead) {
-        if (c0 + 64 < hi) load_chunk<D>(ahead, QK, Vp, nlr, c0 + 64, h, do_e, r, g, qkl);
-        if (do_e) e_branch<ELL, D, SM>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
-        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
-        c0 += 32;
+    with_flag(do_e != 0, [&](auto e_tag) {
+      constexpr bool SM = decltype(phi_tag)::value, DO_E = decltype(e_tag)::value;
+      int64_t c0 = lo & ~int64_t(7);
+      if (c0 >= hi) return;
+      // chunk loads past the last chunk re-read the last one (never used),
+      // so every step issues the same loads and the waits on them are exact
+      const int64_t clast = c0 + ((hi - 1 - c0) >> 5) * 32;
+      auto ld = [&](ChunkOps& c, int64_t at) {
+        load_chunk<D>(c, QK, Vp, nlr, at < clast ? at : clast, h, DO_E, r, g, qkl);
       };
-      while (c0 < hi) {
-        step(cur, nxt2);
-        if (c0 >= hi) break;
-        step(nxt, cur);
-        if (c0 >= hi) break;
-        step(nxt2, nxt);
-      }
-    } else {
-      // the windowed form's own operands take the registers: one chunk at a time
-      for (; c0 < hi; c0 += 32) {
-        if (do_e) {
-          WinOps<NKW> wo;
-          load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, qkl);
-          const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
-          e_branch<ELL, D, SM, NKW>(o, cur, Y, nlr, c0, lo, hi, h, r, g, yl, &wo, &wa);
+      ChunkOps cur;
+      ld(cur, c0);
+      if constexpr (NKW == 0) {
+        // chunk operands two chunks ahead of the one being computed, in
+        // three buffers that rotate by name
+        ChunkOps nxt, nxt2;
+        ld(nxt, c0 + 32);
+        auto step = [&](const ChunkOps& ci, ChunkOps& ahead) {
+          ld(ahead, c0 + 64);
+          if constexpr (DO_E) e_branch<ELL, D, SM>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+          l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+          c0 += 32;
+        };
+        // whole rounds of three steps, then the remainder: a loop with one
+        // exit keeps the waits on the loads exact
+        const int nch = static_cast<int>((clast - c0) >> 5) + 1;
+        for (int k = 3; k <= nch; k += 3) {
+          step(cur, nxt2);
+          step(nxt, cur);
+          step(nxt2, nxt);
         }
-        l_branch<ELL, SM>(st, o, cur, c0, lo, hi, r, g);
-        if (c0 + 32 < hi) load_chunk<D>(cur, QK, Vp, nlr, c0 + 32, h, do_e, r, g, qkl);
+        if (nch % 3 >= 1) step(cur, nxt2);
+        if (nch % 3 == 2) step(nxt, cur);
+      } else {
+        // the windowed form's own operands take the registers: one chunk at
+        // a time
+        for (; c0 < hi; c0 += 32) {
+          if constexpr (DO_E) {
+            WinOps<NKW> wo;
+            load_window<NKW, D>(wo, QK, Vp, nlr, win_key0(c0, half), rmax, h, r, g, qkl);
+            const WinArgs wa{u0, u1, rmax, half, Vp, nlr};
+            e_branch<ELL, D, SM, NKW>(o, cur, Y, nlr, c0, lo, hi, h, r, g, yl, &wo, &wa);
+          }
+          l_branch<ELL, SM>(st, o, cur, c0, lo, hi, r, g);
+          if (c0 + 32 < hi) ld(cur, c0 + 32);
+        }
       }
-    }
+    });
   });
   float* p0 = part + ((x * H + h) * ELL) * PART_LD;
 #pragma unroll
