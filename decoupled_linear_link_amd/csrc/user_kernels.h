@@ -1366,14 +1366,19 @@ struct ResCfg {
 };
 
 // chunk e of a weight set -> (source pointer, LDS row) ; set 0 = w_qkv,
-// set 1 = w_o, w_gate, w_up, w_down stacked
-template <int D>
-__device__ __forceinline__ const bf16_t* wsrc(const LayerSet& w, int l, int set, int e, int* row_out) {
+// set 1 = w_o, w_gate, w_up, w_down stacked.  A thread's i-th chunk lies in
+// one matrix for all threads (the chunks per matrix are a multiple of the
+// threads), so the matrix index is a constant and its pointer is read once
+// per wave, not per lane.
+template <int D, int NT>
+__device__ __forceinline__ const bf16_t* wsrc(const LayerSet& w, int l, int set, int i, int e, int* row_out) {
+  constexpr int CPM = D * (D / 8);  // 16-byte chunks per matrix
+  static_assert(CPM % NT == 0, "weight chunks per matrix");
   const int row = e / (D / 8), c8 = e % (D / 8);
   *row_out = row;
   if (set == 0) return w.p[l][0] + static_cast<int64_t>(row) * D + 8 * c8;
-  const int m = 1 + row / D;
-  return w.p[l][m] + static_cast<int64_t>(row % D) * D + 8 * c8;
+  const int m = (i * NT) / CPM;  // 0..3: w_o, w_gate, w_up, w_down
+  return w.p[l][1 + m] + static_cast<int64_t>(row - m * D) * D + 8 * c8;
 }
 
 template <int ELL, int D, int NKW = 0>
@@ -1417,7 +1422,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
         const int e = tid + i * NT;
         int row;
         if (e < cnt) {
-          const bf16x8 v = ld16(wsrc<D>(w, l, set, e, &row));
+          const bf16x8 v = ld16(wsrc<D, NT>(w, l, set, i, e, &row));
           if (set == 0) pq[i] = v; else pp[i] = v;
         }
       }
@@ -1438,21 +1443,43 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     }
   };
 
-  load_set(0, 0);
-  load_set(0, 1);
-  // residual stream <- [L^C_b ; E_b], zero padding
-  for (int e = tid; e < RT * (D / 8); e += NT) {
-    const int row = e / (D / 8), c8 = e % (D / 8);
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const bf16_t* src = nullptr;
-    if (row < ELL) src = links_ctx + (static_cast<int64_t>(b) * ELL + row) * D + 8 * c8;
-    else if (row < rows) src = hist + (u0 + row - ELL) * D + 8 * c8;
-    if (src) {
-      const bf16x8 x = ld16(src);
+  // residual stream <- [L^C_b ; E_b], zero padding.  Every load is issued
+  // (padding rows read the user's first link row, then zeroed), the first
+  // batch before the weight loads, so converting it waits on it alone.
+  constexpr int XU = 4;  // chunks per thread and batch
+  auto x_load = [&](int e0, bf16x8 (&xv)[XU]) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = static_cast<float>(x[q]);
+    for (int u = 0; u < XU; ++u) {
+      const int e = e0 + u * NT, row = e / (D / 8), c8 = e % (D / 8);
+      const bool link = row < ELL, hrow = !link && row < rows;
+      const bf16_t* src = hrow ? hist + (u0 + row - ELL) * D + 8 * c8
+                               : links_ctx + (static_cast<int64_t>(b) * ELL + (link ? row : 0)) * D + 8 * c8;
+      xv[u] = ld16(src);
     }
-    lds_st8f(Xs + row * XS + 8 * c8, v);
+  };
+  auto x_store = [&](int e0, const bf16x8 (&xv)[XU]) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int e = e0 + u * NT, row = e / (D / 8), c8 = e % (D / 8);
+      if (row < RT) {
+        const bool real = row < rows;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = real ? static_cast<float>(xv[u][q]) : 0.f;
+        lds_st8f(Xs + row * XS + 8 * c8, v);
+      }
+    }
+  };
+  {
+    bf16x8 xv[XU];
+    x_load(tid, xv);
+    load_set(0, 0);
+    load_set(0, 1);
+    x_store(tid, xv);
+    for (int e0 = tid + XU * NT; e0 < RT * (D / 8); e0 += XU * NT) {
+      x_load(e0, xv);
+      x_store(e0, xv);
+    }
   }
   store_set(0);
   store_set(1);
