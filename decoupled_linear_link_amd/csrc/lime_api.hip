@@ -200,10 +200,14 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
   const int dh = d / heads;
   if (p.mfma) {
     // splits of equal row count over all histories (a user's last one
-    // shorter): about 2048 (split, head) waves, at least 64 rows each
+    // shorter): about 2048 (split, head) waves, i.e. one 8-wave workgroup
+    // per CU; at least 32 rows each where the history rows' projection is
+    // fused into the attention (d <= 128: a split then carries that
+    // projection too), 64 otherwise
     int64_t c = (total_N * heads + 2047) / 2048;
     c = (c + 31) / 32 * 32;
-    p.chunk = c < 64 ? 64 : c;
+    const int64_t cmin = d <= 128 ? 32 : 64;
+    p.chunk = c < cmin ? cmin : c;
     p.G = (total_N + p.chunk - 1) / p.chunk + B;  // >= sum over users of max(1, ceil(n_b / chunk))
   } else {
     int64_t S = (static_cast<int64_t>(max_N) + 511) / 512;
@@ -336,6 +340,9 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     // history rows need Q only for their own attention (the E-branch); the
     // links always need it
     const int64_t q_rows = full ? P.R_pad : nlr;
+    // d <= 128 without the window: the history rows' projection runs inside
+    // the attention kernel, so only the link rows are projected here
+    const bool fused = D <= 128 && !(va.half > 0 && full);
     if constexpr (D <= 128) {
       // weights staged in LDS, persistent workgroups (one per CU)
       auto k = mfma::qkv_proj_lds<D>;
@@ -345,12 +352,13 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                                                    static_cast<int>(lds)) == hipSuccess;
       (void)attr;
       static const int per_cu = blocks_per_cu_lds(k, 64 * mfma::QkvLds<D>::NW, lds);
-      const int64_t nblk = P.R_pad / 32;
+      const int64_t nproj = fused ? nlr : P.R_pad;  // nlr is a multiple of 32
+      const int64_t nblk = nproj / 32;
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
       if (grid > need) grid = need;
       hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
+                         P.R_pad, nproj, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
     } else {
       // weights streamed through LDS, persistent workgroups
       auto k = mfma::qkv_proj_stream<D>;
@@ -374,7 +382,21 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       // the windowed form runs at most 4 heads per workgroup (registers)
       constexpr int HBW = H > 4 ? 4 : H;
       const dim3 grid_w(static_cast<unsigned>(P.G * (H / HBW)));
-      if (va.half > 0 && full)
+      if (fused) {
+        if constexpr (D <= 128) {
+          using FC = mfma::FusedCfg<ELL, H>;
+          auto k = mfma::xor_attn_qkv<ELL, H>;
+          static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(FC::lds_bytes)) == hipSuccess;
+          (void)attr;
+          const dim3 grid_f(static_cast<unsigned>((P.G + FC::SPW - 1) / FC::SPW));
+          hipLaunchKernelGGL(k, grid_f, dim3(64 * FC::NW), FC::lds_bytes, st, Xin,
+                             static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, Y, part, off, soff, suser, B,
+                             static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, P.R_pad,
+                             qs);
+        }
+      } else if (va.half > 0 && full)
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
                            Vp, Y, part, off, soff, suser, B, P.chunk, total_N, static_cast<int>(phi), 1, va.half,
                            P.R_pad);

@@ -298,8 +298,10 @@ __device__ __forceinline__ bf16x8 window_v(const WinArgs& wa, int64_t key0, int 
 // score y is the logit x in log2 units.
 
 // E-branch: history rows c0 + [0, 32) attend to the ell links (and, with
-// NKW > 0, to their window); rows in [lo, hi) are written to Y.
-template <int ELL, int D, bool SM, int NKW = 0>
+// NKW > 0, to their window); rows in [lo, hi) are written to Y.  Row order
+// of the Q operands: qe[rb] lane r holds chunk row 16*rb + r, or with RHO
+// the projection's order 8*(r/4) + 4*rb + r%4.
+template <int ELL, int D, bool SM, int NKW = 0, bool RHO = false>
 __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& ci, bf16_t* Y,
                                          int64_t hrow, int64_t c0, int64_t lo, int64_t hi, int h,
                                          int r, int g, Lay yl,
@@ -308,7 +310,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
   constexpr int NWS = NKW > 0 ? NKW / 4 : 1;  // window scores per lane
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int64_t j = c0 + 16 * rb + r;
+    const int64_t j = c0 + (RHO ? 8 * (r >> 2) + 4 * rb + (r & 3) : 16 * rb + r);
     float v[4 * MB];
 #pragma unroll
     for (int c = 0; c < MB; ++c) {
@@ -432,6 +434,18 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
     const int64_t j = c0 + 8 * g + q;  // q = 4*c + jj
     valid[q] = !MASK || ((j >= lo) && (j < hi));
   }
+  // V of rows outside [lo, hi) (another user's, or past the history end) is
+  // zeroed, not only their weights: a non-finite value there must not reach
+  // this split through 0 * inf
+  bf16x8 ve[2] = {ci.ve[0], ci.ve[1]};
+  if constexpr (MASK) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (!valid[q]) {
+        ve[0][q] = static_cast<__bf16>(0.f);
+        ve[1][q] = static_cast<__bf16>(0.f);
+      }
+  }
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
     float p[8];
@@ -470,8 +484,8 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
     // (V^T P^T): P's lane layout (link r, rows 8g..8g+7) is the B operand as
     // it stands, and the product's columns are the links
     const bf16x8 pb = pack8(p);
-    st.acc[nb][0] = mma(ci.ve[0], pb, st.acc[nb][0]);
-    st.acc[nb][1] = mma(ci.ve[1], pb, st.acc[nb][1]);
+    st.acc[nb][0] = mma(ve[0], pb, st.acc[nb][0]);
+    st.acc[nb][1] = mma(ve[1], pb, st.acc[nb][1]);
   }
 }
 
@@ -718,26 +732,22 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
       ChunkOps cur;
       ld(cur, c0);
       if constexpr (NKW == 0) {
-        // chunk operands two chunks ahead of the one being computed, in
-        // three buffers that rotate by name
-        ChunkOps nxt, nxt2;
-        ld(nxt, c0 + 32);
+        // the next chunk's operands load while a chunk is computed; pairs
+        // of steps swap the two buffers by name, and the loop has a single
+        // exit, so the waits on the loads stay exact
+        const int nch = static_cast<int>((clast - c0) >> 5) + 1;
+        ChunkOps nxt;
         auto step = [&](const ChunkOps& ci, ChunkOps& ahead) {
-          ld(ahead, c0 + 64);
+          ld(ahead, c0 + 32);
           if constexpr (DO_E) e_branch<ELL, D, SM>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
           l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
           c0 += 32;
         };
-        // whole rounds of three steps, then the remainder: a loop with one
-        // exit keeps the waits on the loads exact
-        const int nch = static_cast<int>((clast - c0) >> 5) + 1;
-        for (int k = 3; k <= nch; k += 3) {
-          step(cur, nxt2);
+        for (int k = 2; k <= nch; k += 2) {
+          step(cur, nxt);
           step(nxt, cur);
-          step(nxt2, nxt);
         }
-        if (nch % 3 >= 1) step(cur, nxt2);
-        if (nch % 3 == 2) step(nxt, cur);
+        if (nch & 1) step(cur, nxt);
       } else {
         // the windowed form's own operands take the registers: one chunk at
         // a time
@@ -849,12 +859,27 @@ __global__ __launch_bounds__(256) void xor_combine(const float* __restrict__ par
 // distinct banks).  NW waves per workgroup; each wave walks 32-row blocks
 // strided by the whole grid.
 // ---------------------------------------------------------------------------
+// Copies rows x K bf16 from global memory into LDS rows padded by 16 bytes.
+// SU loads per thread are issued before their LDS stores (indexes past the
+// end re-read the last chunk and are not stored), so a thread waits on one
+// round trip per batch rather than one per chunk.
+constexpr int SU = 8;
 __device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict__ src, int rows, int K,
                                            int tid, int nthreads) {
-  const int c8n = K / 8;
-  for (int e = tid; e < rows * c8n; e += nthreads) {
-    const int row = e / c8n, c8 = e % c8n;
-    *reinterpret_cast<bf16x8*>(dst + row * (K + 8) + 8 * c8) = ld16(src + static_cast<int64_t>(row) * K + 8 * c8);
+  const int c8n = K / 8, total = rows * c8n;
+  for (int e0 = tid; e0 < total; e0 += SU * nthreads) {
+    bf16x8 v[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      int e = e0 + u * nthreads;
+      e = e < total ? e : total - 1;
+      v[u] = ld16(src + static_cast<int64_t>(e / c8n) * K + 8 * (e % c8n));
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = e0 + u * nthreads;
+      if (e < total) *reinterpret_cast<bf16x8*>(dst + (e / c8n) * (K + 8) + 8 * (e % c8n)) = v[u];
+    }
   }
 }
 
@@ -866,7 +891,7 @@ struct QkvLds {
 
 template <int D>
 __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64_t R, int64_t R_pad,
-                                                    const bf16_t* __restrict__ W,
+                                                    int64_t nproj, const bf16_t* __restrict__ W,
                                                     bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
                                                     float qs, int64_t q_rows) {
   constexpr int KB = D / 32, NW = QkvLds<D>::NW;
@@ -876,7 +901,7 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
   lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t nblk = R_pad / 32;
+  const int64_t nblk = nproj / 32;  // rows [0, nproj) are projected
   // whole rounds of 32-row blocks over all the waves; after at least one
   // such round a short remainder (its 16-row halves fit one round) is taken
   // as halves by twice as many waves, spread over the workgroups, so no wave
@@ -923,6 +948,165 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
       for (int j = 0; j < 8; ++j) x[0][8 * kb + j] = static_cast<float>(v[j]);
     }
     qkv_rows<D, 1>(x, Wl + opaque_zero(), D + 8, QK, Vp, row0, r, g, Lay{32, R_pad * 32}, qs, row0 < q_rows);
+  }
+}
+
+// XOR attention with the history rows' LN + QKV projection fused in, for
+// d <= 128 (w_qkv fits LDS).  A history row's Q, K and V feed only the
+// attention of its own chunk (there are no history-to-history terms), so
+// they stay in registers, already in the attention's operand layouts: the
+// kernel reads the residual rows X and writes Y, where a separate projection
+// would write Q|K and V to HBM and read them back.  The link rows' Q|K and V
+// come from a projection of the link rows alone.  A workgroup of 8 waves
+// holds w_qkv in LDS (rows padded by 16 bytes) and runs SPW = 8 / H splits
+// with one wave per (split, head); splits and partials as in xor_attn.
+template <int ELL, int H>
+struct FusedCfg {
+  static constexpr int D = 32 * H, NW = 8, SPW = NW / H;
+  static constexpr size_t lds_bytes = static_cast<size_t>(3) * D * (D + 8) * 2;
+};
+
+template <int ELL, int H>
+__global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __restrict__ W,
+                                                    const bf16_t* __restrict__ QK, const bf16_t* __restrict__ Vp,
+                                                    bf16_t* __restrict__ Y, float* __restrict__ part,
+                                                    const int64_t* __restrict__ off,
+                                                    const int32_t* __restrict__ split_off,
+                                                    const int32_t* __restrict__ split_user, int B, int G,
+                                                    int64_t chunk, int64_t total_N, int phi, int do_e,
+                                                    int64_t rmax, float qs) {
+  using C = FusedCfg<ELL, H>;
+  constexpr int D = C::D, KB = D / 32, MB = ELL / 16, LDW = D + 8;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
+  stage_rows(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
+  lds_barrier();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * C::SPW + w / H;  // split
+  const int h = w % H;
+  if (x >= G) return;
+  const int b = split_user[x];
+  if (b < 0) return;  // past the last split
+  const int64_t s = x - split_off[b];
+  const int64_t nlr = static_cast<int64_t>(B) * ELL;
+  const int64_t u0 = clamp64(off[b], 0, total_N);
+  const int64_t u1 = clamp64(off[b + 1], u0, total_N);
+  const int64_t n = u1 - u0;
+  const int64_t lo = u0 + clamp64(s * chunk, 0, n);
+  const int64_t hi = u0 + clamp64((s + 1) * chunk, 0, n);
+  const bool softmax = (phi == PHI_SOFTMAX);
+
+  HeadOps<ELL> o;
+  const Lay qkl{32, rmax * 32}, yl{32, (nlr + total_N) * 32};
+  load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g, qkl);
+  LState<ELL> st;
+  st.init();
+  // X rows of a chunk in the projection's row order: lane (r, g) of block
+  // rb holds chunk row 8*(r/4) + 4*rb + r%4, columns 32*kb + 8*g .. +8
+  struct XChunk {
+    bf16x8 v[2][KB];
+  };
+  with_phi(softmax, [&](auto phi_tag) {
+    with_flag(do_e != 0, [&](auto e_tag) {
+      constexpr bool SM = decltype(phi_tag)::value, DO_E = decltype(e_tag)::value;
+      int64_t c0 = lo & ~int64_t(7);
+      if (c0 >= hi) return;
+      const int64_t clast = c0 + ((hi - 1 - c0) >> 5) * 32;
+      // loads past the last chunk re-read it; rows past the history end
+      // read its last row (both unused), so every step issues the same loads
+      auto ld = [&](XChunk& xc, int64_t at) {
+        at = at < clast ? at : clast;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          int64_t j = at + 8 * (r >> 2) + 4 * rb + (r & 3);
+          j = j < total_N ? j : total_N - 1;
+          const bf16_t* xr = row_in<bf16_t>(X, nlr + j) + 8 * g;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) xc.v[rb][kb] = ld16(xr + kb * 32);
+        }
+      };
+      auto step = [&](const XChunk& xc, XChunk& ahead) {
+        ld(ahead, c0 + 32);
+        // LN, then this head's Q, K and V of the chunk: Q and K in the
+        // transposed form (16-byte row pieces, features in order), V with
+        // the operands swapped (8 consecutive rows of one column)
+        bf16x8 hb[2][KB];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float v[8 * KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) v[8 * kb + jj] = static_cast<float>(xc.v[rb][kb][jj]);
+          ln_rows<8 * KB>(v, D);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+        }
+        const bf16_t* Wb = Wl + opaque_zero();
+        ChunkOps ci;
+        auto proj_qk = [&](int p, float f, bf16x8(&out)[2]) {
+          floatx4 acc[2][2] = {};
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const bf16_t* wr = Wb + (32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * LDW + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 a = ld16(wr + kb * 32);
+              acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
+              acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
+            }
+          }
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                                acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
+            out[rb] = pack8(v);
+          }
+        };
+        if constexpr (DO_E) proj_qk(h, qs, ci.qe);  // Q carries the logit scale
+        proj_qk(H + h, 1.f, ci.ke);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const bf16_t* wr = Wb + (2 * D + 32 * h + 16 * c2 + r) * LDW + 8 * g;
+          floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 bq = ld16(wr + kb * 32);
+            a0 = mma(hb[0][kb], bq, a0);
+            a1 = mma(hb[1][kb], bq, a1);
+          }
+          const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          ci.ve[c2] = pack8(v);
+        }
+        if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+        c0 += 32;
+      };
+      const int nch = static_cast<int>((clast - c0) >> 5) + 1;
+      XChunk cur, nxt;
+      ld(cur, c0);
+      for (int k = 2; k <= nch; k += 2) {
+        step(cur, nxt);
+        step(nxt, cur);
+      }
+      if (nch & 1) step(cur, nxt);
+    });
+  });
+  float* p0 = part + ((x * H + h) * ELL) * PART_LD;
+#pragma unroll
+  for (int nb = 0; nb < MB; ++nb) {
+    // partials in natural units: max * ln 2; silu sums * ln 2
+    float* pl = p0 + (16 * nb + r) * PART_LD;
+    if (g == 0) {
+      pl[0] = softmax ? st.m[nb] * LN2 : 0.f;
+      pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
+    }
+    const float f = softmax ? 1.f : LN2;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      *reinterpret_cast<floatx4*>(pl + 4 + 16 * c2 + 4 * g) =
+          floatx4{st.acc[nb][c2][0] * f, st.acc[nb][c2][1] * f, st.acc[nb][c2][2] * f, st.acc[nb][c2][3] * f};
   }
 }
 
