@@ -340,41 +340,43 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     // history rows need Q only for their own attention (the E-branch); the
     // links always need it
     const int64_t q_rows = full ? P.R_pad : nlr;
-    // d <= 128 without the window: the history rows' projection runs inside
-    // the attention kernel, so only the link rows are projected here
+    // d <= 128 without the window: the projection runs inside the attention
+    // kernel
     const bool fused = D <= 128 && !(va.half > 0 && full);
-    if constexpr (D <= 128) {
-      // weights staged in LDS, persistent workgroups (one per CU)
-      auto k = mfma::qkv_proj_lds<D>;
-      constexpr size_t lds = mfma::QkvLds<D>::lds_bytes;
-      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   static_cast<int>(lds)) == hipSuccess;
-      (void)attr;
-      static const int per_cu = blocks_per_cu_lds(k, 64 * mfma::QkvLds<D>::NW, lds);
-      const int64_t nproj = fused ? nlr : P.R_pad;  // nlr is a multiple of 32
-      const int64_t nblk = nproj / 32;
-      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
-      const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
-      if (grid > need) grid = need;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
-                         P.R_pad, nproj, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
-    } else {
-      // weights streamed through LDS, persistent workgroups
-      auto k = mfma::qkv_proj_stream<D>;
-      constexpr size_t lds = mfma::StreamCfg<D>::lds_bytes;
-      static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   static_cast<int>(lds)) == hipSuccess;
-      (void)attr;
-      static const int per_cu = blocks_per_cu_lds(k, mfma::StreamCfg<D>::NT, lds);
-      const int64_t ntiles = (P.R_pad + 255) / 256;
-      int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
-      if (grid > ntiles) grid = ntiles;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
-                         P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
+    if (!fused) {
+      if constexpr (D <= 128) {
+        // weights staged in LDS, persistent workgroups (one per CU)
+        auto k = mfma::qkv_proj_lds<D>;
+        constexpr size_t lds = mfma::QkvLds<D>::lds_bytes;
+        static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(lds)) == hipSuccess;
+        (void)attr;
+        static const int per_cu = blocks_per_cu_lds(k, 64 * mfma::QkvLds<D>::NW, lds);
+        const int64_t nproj = P.R_pad;
+        const int64_t nblk = nproj / 32;
+        int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+        const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
+        if (grid > need) grid = need;
+        hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
+                           P.R_pad, nproj, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
+      } else {
+        // weights streamed through LDS, persistent workgroups
+        auto k = mfma::qkv_proj_stream<D>;
+        constexpr size_t lds = mfma::StreamCfg<D>::lds_bytes;
+        static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     static_cast<int>(lds)) == hipSuccess;
+        (void)attr;
+        static const int per_cu = blocks_per_cu_lds(k, mfma::StreamCfg<D>::NT, lds);
+        const int64_t ntiles = (P.R_pad + 255) / 256;
+        int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+        if (grid > ntiles) grid = ntiles;
+        hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
+                           P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
+      }
+      LIME_CHECK_LAUNCH("qkv projection (mfma)");
     }
-    LIME_CHECK_LAUNCH("qkv projection (mfma)");
     {
       // one workgroup per (split slot, head group); slots past the last
       // split return at once
@@ -392,9 +394,8 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
           (void)attr;
           const dim3 grid_f(static_cast<unsigned>((P.G + FC::SPW - 1) / FC::SPW));
           hipLaunchKernelGGL(k, grid_f, dim3(64 * FC::NW), FC::lds_bytes, st, Xin,
-                             static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, Y, part, off, soff, suser, B,
-                             static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, P.R_pad,
-                             qs);
+                             static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser, B,
+                             static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, qs);
         }
       } else if (va.half > 0 && full)
         hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
@@ -576,6 +577,12 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
   if (resident) {
     launches = 1;
     snprintf(line, sizeof(line), "user-resident: 1 launch for %d layers, one workgroup per user", layers);
+  } else if (P.mfma && d <= 128) {
+    launches = 3 * layers + 1;
+    snprintf(line, sizeof(line),
+             "streaming matrix-core: a split plan, then 3 launches per layer (qkv + xor_attn fused, "
+             "combine, post); splits of %lld history rows, at most %lld splits",
+             static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else if (P.mfma) {
     launches = 4 * layers + 1;
     snprintf(line, sizeof(line),

@@ -956,10 +956,110 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
 // attention of its own chunk (there are no history-to-history terms), so
 // they stay in registers, already in the attention's operand layouts: the
 // kernel reads the residual rows X and writes Y, where a separate projection
-// would write Q|K and V to HBM and read them back.  The link rows' Q|K and V
-// come from a projection of the link rows alone.  A workgroup of 8 waves
-// holds w_qkv in LDS (rows padded by 16 bytes) and runs SPW = 8 / H splits
-// with one wave per (split, head); splits and partials as in xor_attn.
+// would write Q|K and V to HBM and read them back.  Each wave also projects
+// its user's link rows for its head (K_L, V_L, Q_L: the HeadOps operands),
+// so a layer needs no projection launch.  A workgroup of 8 waves holds w_qkv
+// in LDS (rows padded by 16 bytes) and runs SPW = 8 / H splits with one wave
+// per (split, head); splits and partials as in xor_attn.
+// LN(X) operands of two 16-row blocks: lane (r, g) of block rb holds row
+// row_of(rb) of X, columns 32*kb + 8*g .. +8, as bf16 after the LN.
+template <int D, typename F>
+__device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf16x8 (&hb)[2][D / 32]) {
+  constexpr int KB = D / 32;
+  bf16x8 xv[2][KB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const bf16_t* xr = row_in<bf16_t>(X, row_of(rb)) + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) xv[rb][kb] = ld16(xr + kb * 32);
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float v[8 * KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) v[8 * kb + jj] = static_cast<float>(xv[rb][kb][jj]);
+    ln_rows<8 * KB>(v, D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+  }
+}
+
+// Q or K of head part p (p < H: Q, scaled by f; else K) for the two row
+// blocks of hb, in the transposed form: out[rb] lane (r, g) holds features
+// 8g .. 8g+7 of the row that hb[rb] lane r carries.  W: w_qkv rows in LDS
+// with row stride LDW.
+template <int D>
+__device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
+                                             float f, int r, int g, bf16x8 (&out)[2]) {
+  constexpr int KB = D / 32;
+  floatx4 acc[2][2] = {};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const bf16_t* wr = W + (32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 a = ld16(wr + kb * 32);
+      acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
+      acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                        acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
+    out[rb] = pack8(v);
+  }
+}
+
+// V of two 16-row blocks whose rows are in the projection order (block rb,
+// lane r: row 8*(r/4) + 4*rb + r%4), operands swapped: lane (r, g) ends with
+// V of rows 8g .. 8g+7 for column `col_of(r)` of w_qkv's V part.
+template <int D, typename F>
+__device__ __forceinline__ bf16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw,
+                                              F&& col_of, int r, int g) {
+  constexpr int KB = D / 32;
+  const bf16_t* wr = W + (2 * D + col_of(r)) * ldw + 8 * g;
+  floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const bf16x8 bq = ld16(wr + kb * 32);
+    a0 = mma(hb[0][kb], bq, a0);
+    a1 = mma(hb[1][kb], bq, a1);
+  }
+  const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  return pack8(v);
+}
+
+// The link operands of user b and head h (the HeadOps layouts) computed
+// from the link rows of X: K and V from rows in the projection order, Q
+// from rows in natural order.
+template <int ELL, int D>
+__device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const bf16_t* W, int ldw, int b, int h,
+                                         int r, int g, float qs) {
+  constexpr int H = D / 32;
+  const int64_t l0 = static_cast<int64_t>(b) * ELL;
+#pragma unroll
+  for (int kb2 = 0; kb2 < ELL / 32; ++kb2) {
+    bf16x8 hb[2][D / 32];
+    ln_operands<D>(X, [&](int rb) { return l0 + kb2 * 32 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
+    bf16x8 k2[2];
+    proj_qk_regs<D>(hb, W, ldw, H + h, 1.f, r, g, k2);
+    o.kl[2 * kb2] = k2[0];
+    o.kl[2 * kb2 + 1] = k2[1];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      o.vlt[c2][kb2] = proj_v_regs<D>(hb, W, ldw, [&](int rr) { return 32 * h + 8 * (rr >> 2) + 4 * c2 + (rr & 3); },
+                                      r, g);
+    ln_operands<D>(X, [&](int rb) { return l0 + kb2 * 32 + 16 * rb + r; }, g, hb);
+    bf16x8 q2[2];
+    proj_qk_regs<D>(hb, W, ldw, h, qs, r, g, q2);
+    o.qlt[2 * kb2] = q2[0];
+    o.qlt[2 * kb2 + 1] = q2[1];
+  }
+}
+
 template <int ELL, int H>
 struct FusedCfg {
   static constexpr int D = 32 * H, NW = 8, SPW = NW / H;
@@ -968,13 +1068,12 @@ struct FusedCfg {
 
 template <int ELL, int H>
 __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __restrict__ W,
-                                                    const bf16_t* __restrict__ QK, const bf16_t* __restrict__ Vp,
                                                     bf16_t* __restrict__ Y, float* __restrict__ part,
                                                     const int64_t* __restrict__ off,
                                                     const int32_t* __restrict__ split_off,
                                                     const int32_t* __restrict__ split_user, int B, int G,
                                                     int64_t chunk, int64_t total_N, int phi, int do_e,
-                                                    int64_t rmax, float qs) {
+                                                    float qs) {
   using C = FusedCfg<ELL, H>;
   constexpr int D = C::D, KB = D / 32, MB = ELL / 16, LDW = D + 8;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -998,8 +1097,8 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
   const bool softmax = (phi == PHI_SOFTMAX);
 
   HeadOps<ELL> o;
-  const Lay qkl{32, rmax * 32}, yl{32, (nlr + total_N) * 32};
-  load_head_ops<ELL, D>(o, QK, Vp, static_cast<int64_t>(b) * ELL, h, r, g, qkl);
+  const Lay yl{32, (nlr + total_N) * 32};
+  link_ops<ELL, D>(o, X, Wl + opaque_zero(), LDW, b, h, r, g, qs);
   LState<ELL> st;
   st.init();
   // X rows of a chunk in the projection's row order: lane (r, g) of block
@@ -1045,40 +1144,11 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
         }
         const bf16_t* Wb = Wl + opaque_zero();
         ChunkOps ci;
-        auto proj_qk = [&](int p, float f, bf16x8(&out)[2]) {
-          floatx4 acc[2][2] = {};
+        if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, qs, r, g, ci.qe);  // Q carries the logit scale
+        proj_qk_regs<D>(hb, Wb, LDW, H + h, 1.f, r, g, ci.ke);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const bf16_t* wr = Wb + (32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * LDW + 8 * g;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const bf16x8 a = ld16(wr + kb * 32);
-              acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
-              acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
-            }
-          }
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
-                                acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-            out[rb] = pack8(v);
-          }
-        };
-        if constexpr (DO_E) proj_qk(h, qs, ci.qe);  // Q carries the logit scale
-        proj_qk(H + h, 1.f, ci.ke);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16_t* wr = Wb + (2 * D + 32 * h + 16 * c2 + r) * LDW + 8 * g;
-          floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 bq = ld16(wr + kb * 32);
-            a0 = mma(hb[0][kb], bq, a0);
-            a1 = mma(hb[1][kb], bq, a1);
-          }
-          const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          ci.ve[c2] = pack8(v);
-        }
+        for (int c2 = 0; c2 < 2; ++c2)
+          ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * h + 16 * c2 + rr; }, r, g);
         if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
         l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
         c0 += 32;
