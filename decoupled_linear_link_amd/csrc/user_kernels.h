@@ -72,6 +72,42 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
   return o;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// LayerNorm (no affine, eps 1e-5) of the bf16 row a lane group holds
+// (x[kb]: this lane's values, the rest in lanes ^16, ^32), straight to bf16
+// operands.  The statistics come from bf16 pair dot products (sum and sum
+// of squares, one instruction per pair each, float32 accumulation), the
+// variance as E[x^2] - E[x]^2: the inputs are bf16, whose own rounding
+// dominates that formula's float32 cancellation error.
+template <int KB>
+__device__ __forceinline__ void ln_bf16(const bf16x8 (&x)[KB], int D, bf16x8 (&out)[KB]) {
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  float s[2] = {0.f, 0.f}, q[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const bf16x2 v = {x[kb][2 * pp], x[kb][2 * pp + 1]};
+      s[pp & 1] = __builtin_amdgcn_fdot2_f32_bf16(v, one, s[pp & 1], false);
+      q[pp & 1] = __builtin_amdgcn_fdot2_f32_bf16(v, v, q[pp & 1], false);
+    }
+  const float sum = rows_sum(s[0] + s[1]), sq = rows_sum(q[0] + q[1]);
+  const float inv_d = 1.f / static_cast<float>(D);
+  const float mu = sum * inv_d;
+  const float var = fmaxf(sq * inv_d - mu * mu, 0.f);
+  const float rs = rsqrtf(var + 1e-5f);
+  const float nb = -mu * rs;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = fmaf(static_cast<float>(x[kb][j]), rs, nb);
+    out[kb] = pack8(v);
+  }
+}
+
+
 // ---------------------------------------------------------------------------
 // QKV projection of one 32-row chunk.  hb[rb][kb] are LN(X) operands: lane
 // (r, g) of row block rb carries chunk row 8*(r/4) + 4*rb + r%4, columns
@@ -974,16 +1010,7 @@ __device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf
     for (int kb = 0; kb < KB; ++kb) xv[rb][kb] = ld16(xr + kb * 32);
   }
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    float v[8 * KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) v[8 * kb + jj] = static_cast<float>(xv[rb][kb][jj]);
-    ln_rows<8 * KB>(v, D);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
-  }
+  for (int rb = 0; rb < 2; ++rb) ln_bf16<KB>(xv[rb], D, hb[rb]);
 }
 
 // Q or K of head part p (p < H: Q, scaled by f; else K) for the two row
@@ -1132,16 +1159,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
         // the operands swapped (8 consecutive rows of one column)
         bf16x8 hb[2][KB];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          float v[8 * KB];
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) v[8 * kb + jj] = static_cast<float>(xc.v[rb][kb][jj]);
-          ln_rows<8 * KB>(v, D);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
-        }
+        for (int rb = 0; rb < 2; ++rb) ln_bf16<KB>(xc.v[rb], D, hb[rb]);
         const bf16_t* Wb = Wl + opaque_zero();
         ChunkOps ci;
         if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, qs, r, g, ci.qe);  // Q carries the logit scale
