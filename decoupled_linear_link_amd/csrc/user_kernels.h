@@ -987,16 +987,6 @@ __global__ __launch_bounds__(64 * QkvLds<D>::NW) void qkv_proj_lds(Rows X, int64
   }
 }
 
-// XOR attention with the history rows' LN + QKV projection fused in, for
-// d <= 128 (w_qkv fits LDS).  A history row's Q, K and V feed only the
-// attention of its own chunk (there are no history-to-history terms), so
-// they stay in registers, already in the attention's operand layouts: the
-// kernel reads the residual rows X and writes Y, where a separate projection
-// would write Q|K and V to HBM and read them back.  Each wave also projects
-// its user's link rows for its head (K_L, V_L, Q_L: the HeadOps operands),
-// so a layer needs no projection launch.  A workgroup of 8 waves holds w_qkv
-// in LDS (rows padded by 16 bytes) and runs SPW = 8 / H splits with one wave
-// per (split, head); splits and partials as in xor_attn.
 // LN(X) operands of two 16-row blocks: lane (r, g) of block rb holds row
 // row_of(rb) of X, columns 32*kb + 8*g .. +8, as bf16 after the LN.
 template <int D, typename F>
@@ -1087,11 +1077,43 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
   }
 }
 
+// XOR attention with the history rows' LN + QKV projection fused in, for
+// d <= 128 (w_qkv fits LDS).  A history row's Q, K and V feed only the
+// attention of its own chunk (there are no history-to-history terms), so
+// they stay in registers, already in the attention's operand layouts: the
+// kernel reads the residual rows X and writes Y, where a separate projection
+// would write Q|K and V to HBM and read them back.  Each wave also projects
+// its user's link rows for its head (K_L, V_L, Q_L: the HeadOps operands),
+// so a layer needs no projection launch.
+// A workgroup of 8 waves holds w_qkv in LDS (rows padded by 16 bytes) and
+// runs SPW = 8 / H splits with one wave per (split, head); splits and
+// partials as in xor_attn.  The H waves of a split share each chunk's LN:
+// every wave normalizes 32 / H of its rows into an LDS chunk buffer (two per
+// split, alternating), and after one workgroup barrier per chunk each wave
+// reads the rows it needs as projection operands.  The splits of a
+// workgroup run the same number of barrier steps (the most chunks of any of
+// them); a split out of chunks only joins the barriers.
 template <int ELL, int H>
 struct FusedCfg {
-  static constexpr int D = 32 * H, NW = 8, SPW = NW / H;
-  static constexpr size_t lds_bytes = static_cast<size_t>(3) * D * (D + 8) * 2;
+  static constexpr int D = 32 * H, NW = 8, SPW = NW / H, LDW = D + 8;
+  static constexpr int RPWV = 32 / H;  // chunk rows each wave normalizes
+  static constexpr size_t w_elems = static_cast<size_t>(3) * D * LDW;
+  static constexpr size_t buf_elems = static_cast<size_t>(32) * LDW;
+  static constexpr size_t lds_bytes = (w_elems + 2 * SPW * buf_elems) * 2 + 4 * SPW;
 };
+
+// Sum over the lanes of a wave that share lane % N (N = 8 or 16): xor
+// steps of N (a row rotation by 8 within 16 lanes when N = 8), 16 and 32.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group");
+  if constexpr (N == 8) {
+    // row_ror:8 within each 16-lane row: lane i reads lane i ^ 8
+    const int o = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false);
+    x += __int_as_float(o);
+  }
+  return rows_sum(x);
+}
 
 template <int ELL, int H>
 __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __restrict__ W,
@@ -1102,85 +1124,118 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
                                                     int64_t chunk, int64_t total_N, int phi, int do_e,
                                                     float qs) {
   using C = FusedCfg<ELL, H>;
-  constexpr int D = C::D, KB = D / 32, MB = ELL / 16, LDW = D + 8;
+  constexpr int D = C::D, KB = D / 32, MB = ELL / 16, LDW = C::LDW, RPWV = C::RPWV, SPW = C::SPW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* hbuf = Wl + C::w_elems;  // [SPW][2][32][LDW]
+  int* nchs = reinterpret_cast<int*>(hbuf + 2 * SPW * C::buf_elems);
   stage_rows(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
-  lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t x = static_cast<int64_t>(blockIdx.x) * C::SPW + w / H;  // split
-  const int h = w % H;
-  if (x >= G) return;
-  const int b = split_user[x];
-  if (b < 0) return;  // past the last split
-  const int64_t s = x - split_off[b];
+  const int sidx = w / H, h = w % H;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * SPW + sidx;  // split
+  const int b = x < G ? split_user[x] : -1;
+  const bool has = b >= 0;  // uniform over the split's waves
   const int64_t nlr = static_cast<int64_t>(B) * ELL;
-  const int64_t u0 = clamp64(off[b], 0, total_N);
-  const int64_t u1 = clamp64(off[b + 1], u0, total_N);
-  const int64_t n = u1 - u0;
-  const int64_t lo = u0 + clamp64(s * chunk, 0, n);
-  const int64_t hi = u0 + clamp64((s + 1) * chunk, 0, n);
+  int64_t lo = 0, hi = 0;
+  if (has) {
+    const int64_t sx = x - split_off[b];
+    const int64_t u0 = clamp64(off[b], 0, total_N);
+    const int64_t u1 = clamp64(off[b + 1], u0, total_N);
+    const int64_t n = u1 - u0;
+    lo = u0 + clamp64(sx * chunk, 0, n);
+    hi = u0 + clamp64((sx + 1) * chunk, 0, n);
+  }
+  const int64_t c0s = lo & ~int64_t(7);
+  const int nch = c0s < hi ? static_cast<int>((hi - 1 - c0s) >> 5) + 1 : 0;
+  if (h == 0 && lane == 0) nchs[sidx] = nch;
+  lds_barrier();
+  int nmax = 0;
+#pragma unroll
+  for (int q = 0; q < SPW; ++q) nmax = nchs[q] > nmax ? nchs[q] : nmax;
   const bool softmax = (phi == PHI_SOFTMAX);
 
   HeadOps<ELL> o;
   const Lay yl{32, (nlr + total_N) * 32};
-  link_ops<ELL, D>(o, X, Wl + opaque_zero(), LDW, b, h, r, g, qs);
+  if (has) link_ops<ELL, D>(o, X, Wl + opaque_zero(), LDW, b, h, r, g, qs);
   LState<ELL> st;
   st.init();
-  // X rows of a chunk in the projection's row order: lane (r, g) of block
-  // rb holds chunk row 8*(r/4) + 4*rb + r%4, columns 32*kb + 8*g .. +8
-  struct XChunk {
-    bf16x8 v[2][KB];
-  };
+  // LN lanes: chunk row crow = RPWV*h + lr, features 16*fg .. +16
+  const int lr = lane % RPWV, fg = lane / RPWV, crow = RPWV * h + lr;
   with_phi(softmax, [&](auto phi_tag) {
     with_flag(do_e != 0, [&](auto e_tag) {
       constexpr bool SM = decltype(phi_tag)::value, DO_E = decltype(e_tag)::value;
-      int64_t c0 = lo & ~int64_t(7);
-      if (c0 >= hi) return;
-      const int64_t clast = c0 + ((hi - 1 - c0) >> 5) * 32;
-      // loads past the last chunk re-read it; rows past the history end
-      // read its last row (both unused), so every step issues the same loads
-      auto ld = [&](XChunk& xc, int64_t at) {
-        at = at < clast ? at : clast;
+      // this lane's X row of chunk i (clamped: past the history end or past
+      // the split's chunks it is read but not used)
+      auto ldx = [&](bf16x8(&xv)[2], int i) {
+        int64_t j = c0s + 32 * i + crow;
+        j = j < total_N ? j : total_N - 1;
+        const bf16_t* p = row_in<bf16_t>(X, nlr + j) + 16 * fg;
+        xv[0] = ld16(p);
+        xv[1] = ld16(p + 8);
+      };
+      auto step = [&](const bf16x8(&xc)[2], bf16x8(&xn)[2], int i, int par) {
+        ldx(xn, i + 1);
+        const bool active = i < nch;
+        bf16_t* buf = hbuf + (sidx * 2 + par) * C::buf_elems;
+        if (active) {
+          // LN of this lane's 16 values of row crow; the row's other values
+          // are in the lanes with the same lr
+          const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+          float sm[2] = {0.f, 0.f}, sq[2] = {0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          int64_t j = at + 8 * (r >> 2) + 4 * rb + (r & 3);
-          j = j < total_N ? j : total_N - 1;
-          const bf16_t* xr = row_in<bf16_t>(X, nlr + j) + 8 * g;
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) xc.v[rb][kb] = ld16(xr + kb * 32);
+            for (int pp = 0; pp < 4; ++pp) {
+              const bf16x2 v = {xc[u][2 * pp], xc[u][2 * pp + 1]};
+              sm[u] = __builtin_amdgcn_fdot2_f32_bf16(v, one, sm[u], false);
+              sq[u] = __builtin_amdgcn_fdot2_f32_bf16(v, v, sq[u], false);
+            }
+          const float sum = group_sum<RPWV>(sm[0] + sm[1]), ssq = group_sum<RPWV>(sq[0] + sq[1]);
+          constexpr float inv_d = 1.f / static_cast<float>(D);
+          const float mu = sum * inv_d;
+          const float rs = rsqrtf(fmaxf(ssq * inv_d - mu * mu, 0.f) + 1e-5f);
+          const float nb = -mu * rs;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            float v[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) v[jj] = fmaf(static_cast<float>(xc[u][jj]), rs, nb);
+            *reinterpret_cast<bf16x8*>(buf + crow * LDW + 16 * fg + 8 * u) = pack8(v);
+          }
+        }
+        lds_barrier();
+        if (active) {
+          const int64_t c0 = c0s + 32 * i;
+          // the chunk's LN rows in the projection order
+          bf16x8 hb[2][KB];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+              hb[rb][kb] = *reinterpret_cast<const bf16x8*>(
+                  buf + (8 * (r >> 2) + 4 * rb + (r & 3)) * LDW + 32 * kb + 8 * g);
+          const bf16_t* Wb = Wl + opaque_zero();
+          ChunkOps ci;
+          if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, qs, r, g, ci.qe);  // Q carries the logit scale
+          proj_qk_regs<D>(hb, Wb, LDW, H + h, 1.f, r, g, ci.ke);
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2)
+            ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * h + 16 * c2 + rr; }, r, g);
+          if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+          l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
         }
       };
-      auto step = [&](const XChunk& xc, XChunk& ahead) {
-        ld(ahead, c0 + 32);
-        // LN, then this head's Q, K and V of the chunk: Q and K in the
-        // transposed form (16-byte row pieces, features in order), V with
-        // the operands swapped (8 consecutive rows of one column)
-        bf16x8 hb[2][KB];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) ln_bf16<KB>(xc.v[rb], D, hb[rb]);
-        const bf16_t* Wb = Wl + opaque_zero();
-        ChunkOps ci;
-        if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, qs, r, g, ci.qe);  // Q carries the logit scale
-        proj_qk_regs<D>(hb, Wb, LDW, H + h, 1.f, r, g, ci.ke);
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-          ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * h + 16 * c2 + rr; }, r, g);
-        if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
-        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
-        c0 += 32;
-      };
-      const int nch = static_cast<int>((clast - c0) >> 5) + 1;
-      XChunk cur, nxt;
-      ld(cur, c0);
-      for (int k = 2; k <= nch; k += 2) {
-        step(cur, nxt);
-        step(nxt, cur);
+      bf16x8 xa[2], xb[2];
+      ldx(xa, 0);
+      for (int i = 0; i + 2 <= nmax; i += 2) {
+        step(xa, xb, i, 0);
+        step(xb, xa, i + 1, 1);
       }
-      if (nch & 1) step(cur, nxt);
+      if (nmax & 1) step(xa, xb, nmax - 1, 0);
     });
   });
+  if (!has) return;
   float* p0 = part + ((x * H + h) * ELL) * PART_LD;
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
