@@ -1051,7 +1051,9 @@ __device__ __forceinline__ bf16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], con
 
 // The link operands of user b and head h (the HeadOps layouts) computed
 // from the link rows of X: K and V from rows in the projection order, Q
-// from rows in natural order.
+// from rows in natural order.  Both Q_L and K_L carry the logit scale qs:
+// each branch's scores then come out in log2 units with the history rows'
+// Q and K left unscaled.
 template <int ELL, int D>
 __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const bf16_t* W, int ldw, int b, int h,
                                          int r, int g, float qs) {
@@ -1062,7 +1064,7 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
     bf16x8 hb[2][D / 32];
     ln_operands<D>(X, [&](int rb) { return l0 + kb2 * 32 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
     bf16x8 k2[2];
-    proj_qk_regs<D>(hb, W, ldw, H + h, 1.f, r, g, k2);
+    proj_qk_regs<D>(hb, W, ldw, H + h, qs, r, g, k2);
     o.kl[2 * kb2] = k2[0];
     o.kl[2 * kb2 + 1] = k2[1];
 #pragma unroll
@@ -1217,7 +1219,8 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
                   buf + (8 * (r >> 2) + 4 * rb + (r & 3)) * LDW + 32 * kb + 8 * g);
           const bf16_t* Wb = Wl + opaque_zero();
           ChunkOps ci;
-          if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, qs, r, g, ci.qe);  // Q carries the logit scale
+          // (the logit scale is on the link side)
+          if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, h, 1.f, r, g, ci.qe);
           proj_qk_regs<D>(hb, Wb, LDW, H + h, 1.f, r, g, ci.ke);
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2)
