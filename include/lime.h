@@ -109,7 +109,9 @@ size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, i
  *   X += Y w_o^T;  X += SwiGLU-MLP(LayerNorm(X)).
  *
  *   links_ctx    [B, ell, d]          context links L^C (device)
- *   hist         [total_N, d]         packed histories E (device)
+ *   hist         [total_N, d]         packed histories E (device); users
+ *                                     stay independent even when one
+ *                                     user's rows hold inf or nan
  *   hist_offsets [B+1] int64 (device) exclusive prefix sum of history
  *                                     lengths: user b owns rows
  *                                     [off[b], off[b+1]); off[0] = 0 and
