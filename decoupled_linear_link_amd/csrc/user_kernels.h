@@ -554,14 +554,17 @@ __device__ __forceinline__ void with_flag(bool b, F&& f) {
 // Post-attention block on RB row blocks of 16 rows (lane (r, g) of block rb
 // carries one row, columns 32*p + 8*g .. +8 of every 32-column block):
 //   x1 += Y Wo^T ;  G = LN(x1) ;  M = SiLU(G Wg^T) * (G Wu^T) ;  x1 += M Wd^T
-// x1 holds the residual on entry and the layer output on exit (float32).
+// x1 holds the residual on entry and the layer output on exit (float32);
+// with xres the residual comes as bf16 from xres instead and is first read
+// in the W_o epilogue (so its loads can still be in flight through W_o).
 // Each product's output is the next product's B operand as it stands.
 // ---------------------------------------------------------------------------
-template <int D, int DFF, int RB>
+template <int D, int DFF, int RB, bool XB = false>
 __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float (&x1)[RB][D / 4],
                                           const bf16_t* __restrict__ Wo, const bf16_t* __restrict__ Wg,
                                           const bf16_t* __restrict__ Wu, const bf16_t* __restrict__ Wd,
-                                          int ldd, int ldf, int r, int g) {
+                                          int ldd, int ldf, int r, int g,
+                                          const bf16x8 (*xres)[D / 32] = nullptr) {
   constexpr int KB = D / 32, KF = DFF / 32;
 #pragma unroll
   for (int p = 0; p < KB; ++p) {
@@ -580,8 +583,10 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        x1[rb][8 * p + q] += acc[0][rb][q];
-        x1[rb][8 * p + 4 + q] += acc[1][rb][q];
+        const float r0 = XB ? static_cast<float>(xres[rb][p][q]) : x1[rb][8 * p + q];
+        const float r1 = XB ? static_cast<float>(xres[rb][p][4 + q]) : x1[rb][8 * p + 4 + q];
+        x1[rb][8 * p + q] = r0 + acc[0][rb][q];
+        x1[rb][8 * p + 4 + q] = r1 + acc[1][rb][q];
       }
     // keep the scheduler from hoisting every block's weight loads at once
     __builtin_amdgcn_sched_barrier(0);
@@ -1287,24 +1292,29 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
   // the post block of NB 16-row blocks from row0
   auto rows_block = [&](auto nb_tag, int64_t row0) {
     constexpr int NB = decltype(nb_tag)::value;
-    bf16x8 yb[NB][KB];
+    // every load is issued (rows past nrows read the last row and are not
+    // stored), Y's first: the W_o product waits on Y only, the residual is
+    // first read in its epilogue
+    bf16x8 yb[NB][KB], xb[NB][KB];
     float x1[NB][D / 4];
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
-      const int64_t row = row0 + 16 * rb + r;
-      const bool ok = row < nrows;
+      int64_t row = row0 + 16 * rb + r;
+      row = row < nrows ? row : nrows - 1;
       const bf16_t* yr = Y + row * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
-      const bf16_t* xr = ok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        yb[rb][kb] = ok ? ld16(yr + kb * yR * 32) : zero8();
-        const bf16x8 x = ok ? ld16(xr + kb * 32) : zero8();
+      for (int kb = 0; kb < KB; ++kb) yb[rb][kb] = ld16(yr + kb * yR * 32);
+    }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x1[rb][8 * kb + q] = static_cast<float>(x[q]);
-      }
+    for (int rb = 0; rb < NB; ++rb) {
+      int64_t row = row0 + 16 * rb + r;
+      row = row < nrows ? row : nrows - 1;
+      const bf16_t* xr = row_in<bf16_t>(Xres, row) + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) xb[rb][kb] = ld16(xr + kb * 32);
     }
     const int z = opaque_zero();
-    post_rows<D, DFF, NB>(yb, x1, Wol + z, Wgl + z, Wul + z, Wdl + z, D + 8, DFF + 8, r, g);
+    post_rows<D, DFF, NB, true>(yb, x1, Wol + z, Wgl + z, Wul + z, Wdl + z, D + 8, DFF + 8, r, g, xb);
 #pragma unroll
     for (int rb = 0; rb < NB; ++rb) {
       const int64_t row = row0 + 16 * rb + r;
