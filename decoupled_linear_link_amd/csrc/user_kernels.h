@@ -559,7 +559,7 @@ __device__ __forceinline__ void with_flag(bool b, F&& f) {
 // in the W_o epilogue (so its loads can still be in flight through W_o).
 // Each product's output is the next product's B operand as it stands.
 // ---------------------------------------------------------------------------
-template <int D, int DFF, int RB, bool XB = false>
+template <int D, int DFF, int RB, bool XB = false, bool SB = true>
 __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float (&x1)[RB][D / 4],
                                           const bf16_t* __restrict__ Wo, const bf16_t* __restrict__ Wg,
                                           const bf16_t* __restrict__ Wu, const bf16_t* __restrict__ Wd,
@@ -589,7 +589,7 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
         x1[rb][8 * p + 4 + q] = r1 + acc[1][rb][q];
       }
     // keep the scheduler from hoisting every block's weight loads at once
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
   }
   bf16x8 gb[RB][KB];
 #pragma unroll
@@ -631,7 +631,7 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
       }
       mb[rb][q2] = pack8(v);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int p = 0; p < KB; ++p) {
@@ -654,7 +654,7 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
         x1[rb][8 * p + 4 + q] += acc[1][rb][q];
       }
     // keep the scheduler from hoisting every block's weight loads at once
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -1938,7 +1938,7 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
           for (int kb = 0; kb < KB; ++kb) yb[rb][kb] = row < rows ? ld16(Ys + row * LY + kb * 32 + 8 * g) : zero8();
         }
         const int z = opaque_zero();
-        post_rows<D, D, PRB>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
+        post_rows<D, D, PRB, false, false>(yb, x1, lo_w + z, lg_w + z, lu_w + z, ld_w + z, ldd, ldd, r, g);
 #pragma unroll
         for (int rb = 0; rb < PRB; ++rb) {
           const bool real = row0 + 16 * rb + r < rows;
