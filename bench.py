@@ -197,6 +197,19 @@ def main():
                 "avg_launch_us": round(single[dom] * 1e3, 2),
                 "algorithmic_bytes_per_launch": int(a["bytes"]),
                 "algorithmic_flops_per_launch": float(a["flops"])}
+    # the user side against its roofline: algorithmic flops of the call, and
+    # the fused minimum of HBM bytes (every layer reads and writes each row of
+    # the residual stream once: 2 (B ell + N) d s per layer), at the peaks
+    t_user = call_ms["lime_xor_fwd"] * 1e-3
+    u_flops = xor_fwd_flops(w, np.diff(off))
+    u_bytes = 2.0 * w.layers * (w.B * w.ell + total_N) * w.d * es
+    u_roof = max(u_bytes / (HBM_PEAK_GBS * 1e9), u_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    user_side = {"us": round(t_user * 1e6, 2), "users_per_s": round(w.B / t_user, 1),
+                 "history_rows_per_s": round(total_N / t_user, 1),
+                 "TFLOP/s": round(u_flops / t_user / 1e12, 2),
+                 "fused_min_bytes": int(u_bytes), "fused_min_GB/s": round(u_bytes / t_user / 1e9, 1),
+                 "roofline_us": round(u_roof * 1e6, 2), "frac": round(u_roof / t_user, 4),
+                 "launches": launches}
     per_call = {}
     for k, v in algo.items():
         tk = call_ms[k] * 1e-3
@@ -352,6 +365,7 @@ def main():
         "users_per_s": w.B / (ms_step * 1e-3),
         "items_per_s": w.n_items / (ms_step * 1e-3),
         "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
+        "user_side": user_side,
         "per_call": per_call,
         "scoring": scoring,
         "variants": extras,
