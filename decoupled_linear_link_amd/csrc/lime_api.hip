@@ -208,7 +208,9 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
     c = (c + 31) / 32 * 32;
     const int64_t cmin = d <= 128 ? 32 : 64;
     p.chunk = c < cmin ? cmin : c;
-    p.G = (total_N + p.chunk - 1) / p.chunk + B;  // >= sum over users of max(1, ceil(n_b / chunk))
+    // >= sum over users of max(1, ceil((n_b + u0 % 8) / chunk)) (the split
+    // grid is anchored at the 8-aligned row below each user's first row)
+    p.G = (total_N + 7 * static_cast<int64_t>(B) + p.chunk - 1) / p.chunk + B;
   } else {
     int64_t S = (static_cast<int64_t>(max_N) + 511) / 512;
     if (S < 1) S = 1;

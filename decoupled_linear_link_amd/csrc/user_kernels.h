@@ -662,14 +662,32 @@ __device__ __forceinline__ void post_rows(const bf16x8 (&yb)[RB][D / 32], float 
 // Streaming kernels (any history length)
 // ===========================================================================
 
-// Splits of the streaming attention.  User b's history is cut into
-// S_b = max(1, ceil(n_b / chunk)) splits of chunk rows (its last one
-// shorter), so every split but the tails carries the same work however
-// ragged the histories are.  split_off[b] = sum of S_b' over b' < b
-// (split_off[B] = the number of splits) and split_user[x] = the user of split
-// x, -1 for x >= split_off[B] up to G.  One workgroup of 1024 threads.
+// Splits of the streaming attention.  User b's history rows [u0, u1) are
+// cut at a grid of chunk rows anchored at the 8-aligned row below u0
+// (a = u0 & ~7): split s is [max(u0, a + s chunk), min(u1, a + (s+1) chunk)),
+// S_b = max(1, ceil((u1 - a) / chunk)) of them.  Every split but the tails
+// then carries the same work however ragged the histories are, and, since
+// the attention walks 32-row chunks from the 8-aligned row at or below a
+// split's start, a chunk that is a multiple of 32 takes chunk / 32 steps for
+// every split (cut at u0 itself, a misaligned user would take one more).
+// split_off[b] = sum of S_b' over b' < b (split_off[B] = the number of
+// splits) and split_user[x] = the user of split x, -1 for x >= split_off[B]
+// up to G.  One workgroup of 1024 threads.
 constexpr int SPLIT_PLAN_NT = 1024;
 constexpr int PART_LD = 36;  // floats per partial row: m, l, 2 spare, acc[32]
+
+__device__ __forceinline__ int64_t split_count(int64_t u0, int64_t u1, int64_t chunk) {
+  const int64_t sb = (u1 - (u0 & ~int64_t(7)) + chunk - 1) / chunk;
+  return sb > 1 ? sb : 1;
+}
+
+// rows [lo, hi) of split s of the user owning [u0, u1)
+__device__ __forceinline__ void split_rows(int64_t u0, int64_t u1, int64_t s, int64_t chunk, int64_t* lo,
+                                           int64_t* hi) {
+  const int64_t a = u0 & ~int64_t(7);
+  *lo = clamp64(a + s * chunk, u0, u1);
+  *hi = clamp64(a + (s + 1) * chunk, *lo, u1);
+}
 
 __global__ __launch_bounds__(SPLIT_PLAN_NT) void split_plan(const int64_t* __restrict__ off, int B,
                                                             int64_t total_N, int64_t chunk,
@@ -689,8 +707,7 @@ __global__ __launch_bounds__(SPLIT_PLAN_NT) void split_plan(const int64_t* __res
     if (b < B) {
       const int64_t u0 = clamp64(off[b], 0, total_N);
       const int64_t u1 = clamp64(off[b + 1], u0, total_N);
-      const int64_t sb = (u1 - u0 + chunk - 1) / chunk;
-      cnt = sb > 1 ? static_cast<int32_t>(sb) : 1;
+      cnt = static_cast<int32_t>(split_count(u0, u1, chunk));
     }
     // inclusive scan: within the wave, then over the waves
     int32_t v = cnt;
@@ -745,9 +762,8 @@ __global__ __launch_bounds__(64 * HB) void xor_attn(const bf16_t* __restrict__ Q
   const int64_t nlr = static_cast<int64_t>(B) * ELL;
   const int64_t u0 = clamp64(off[b], 0, total_N);
   const int64_t u1 = clamp64(off[b + 1], u0, total_N);
-  const int64_t n = u1 - u0;
-  const int64_t lo = u0 + clamp64(s * chunk, 0, n);
-  const int64_t hi = u0 + clamp64((s + 1) * chunk, 0, n);
+  int64_t lo, hi;
+  split_rows(u0, u1, s, chunk, &lo, &hi);
   const bool softmax = (phi == PHI_SOFTMAX);
 
   HeadOps<ELL> o;
@@ -1149,9 +1165,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
     const int64_t sx = x - split_off[b];
     const int64_t u0 = clamp64(off[b], 0, total_N);
     const int64_t u1 = clamp64(off[b + 1], u0, total_N);
-    const int64_t n = u1 - u0;
-    lo = u0 + clamp64(sx * chunk, 0, n);
-    hi = u0 + clamp64((sx + 1) * chunk, 0, n);
+    split_rows(u0, u1, sx, chunk, &lo, &hi);
   }
   const int64_t c0s = lo & ~int64_t(7);
   const int nch = c0s < hi ? static_cast<int>((hi - 1 - c0s) >> 5) + 1 : 0;
