@@ -1148,6 +1148,13 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
                                                     float qs) {
   using C = FusedCfg<ELL, H>;
   constexpr int D = C::D, KB = D / 32, MB = ELL / 16, LDW = C::LDW, RPWV = C::RPWV, SPW = C::SPW;
+  // splits are numbered without gaps, so a workgroup whose first slot holds
+  // none has nothing to do (slots past the last split: the grid covers G,
+  // an upper bound); it leaves before staging the weights
+  {
+    const int64_t x0 = static_cast<int64_t>(blockIdx.x) * SPW;
+    if (x0 >= G || split_user[x0] < 0) return;
+  }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
   bf16_t* hbuf = Wl + C::w_elems;  // [SPW][2][32][LDW]
