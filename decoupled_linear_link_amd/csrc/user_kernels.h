@@ -45,6 +45,14 @@ __device__ __forceinline__ float tree_sum(const float* v) {
   }
 }
 
+// Sum over each group of N consecutive lanes (N a power of two up to 64).
+template <int N>
+__device__ __forceinline__ float span_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < N; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // LayerNorm (no affine, eps 1e-5) of the row a lane group holds: v[] are
 // this lane's values of the row; the other values are in lanes ^16, ^32.
 template <int N>
@@ -1024,10 +1032,10 @@ __device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf
   for (int rb = 0; rb < 2; ++rb) ln_bf16<KB>(xv[rb], D, hb[rb]);
 }
 
-// Q or K of head part p (p < H: Q, scaled by f; else K) for the two row
+// Q or K of head part p (p < H: Q, else K), multiplied by f, for the two row
 // blocks of hb, in the transposed form: out[rb] lane (r, g) holds features
 // 8g .. 8g+7 of the row that hb[rb] lane r carries.  W: w_qkv rows in LDS
-// with row stride LDW.
+// with row stride ldw.
 template <int D>
 __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
                                              float f, int r, int g, bf16x8 (&out)[2]) {
@@ -1818,16 +1826,30 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
       xv[u] = ld16(src);
     }
   };
+  // Each row's D/8 chunks sit in D/8 consecutive lanes, so the store also
+  // takes the row's LN (layer 0's pre-attention LN) and writes it as bf16
+  // into the Y rows, which hold nothing before the first attention.
   auto x_store = [&](int e0, const bf16x8 (&xv)[XU]) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int e = e0 + u * NT, row = e / (D / 8), c8 = e % (D / 8);
-      if (row < RT) {
-        const bool real = row < rows;
-        float v[8];
+      const bool real = row < rows;
+      float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = real ? static_cast<float>(xv[u][q]) : 0.f;
+      for (int q = 0; q < 8; ++q) v[q] = real ? static_cast<float>(xv[u][q]) : 0.f;
+      const float mu = span_sum<D / 8>(tree_sum<8>(v)) * (1.f / static_cast<float>(D));
+      float t[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float dv = v[q] - mu;
+        t[q] = dv * dv;
+      }
+      const float rs = rsqrtf(span_sum<D / 8>(tree_sum<8>(t)) * (1.f / static_cast<float>(D)) + 1e-5f);
+      if (row < RT) {
         lds_st8f(Xs + row * XS + 8 * c8, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t[q] = (v[q] - mu) * rs;
+        *reinterpret_cast<bf16x8*>(Ys + row * LY + 8 * c8) = pack8(t);
       }
     }
   };
@@ -1854,16 +1876,14 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     const bf16_t* lq = WL ? Wq : w.p[0][0];
     for (int it = wv; it < 2 * nchunks; it += NW) {
       const int row0 = (it >> 1) * 32;
+      // the LN rows the staging wrote into Y
       bf16x8 hb[2][KB];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-        float v[8 * KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) lds_ld8f(Xs + row * XS + kb * 32 + 8 * g, v + 8 * kb);
-        ln_rows<8 * KB>(v, D);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+        for (int kb = 0; kb < KB; ++kb)
+          hb[rb][kb] = *reinterpret_cast<const bf16x8*>(Ys + row * LY + kb * 32 + 8 * g);
       }
       if (it & 1) v_part<D>(hb, lq + opaque_zero(), ldd, Vps, row0, r, g);
       else qk_part<D>(hb, lq + opaque_zero(), ldd, QKs, row0, r, g, qs, qkl);
