@@ -77,7 +77,7 @@ int blocks_per_cu(K kernel, int threads) {
 template <int ELL, int D, int H, bool I8>
 lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, float* qscale,
                              int64_t n_items, float scale, int phi, hipStream_t st) {
-  using C = mfma::QkCfg<ELL, D, H>;
+  using C = mfma::QkCfg<ELL, D, H, I8>;
   auto k = mfma::qk_cache<ELL, D, H, I8>;
   static const int per_cu = blocks_per_cu(k, C::NT);
   const int64_t ntiles = (n_items + C::TI - 1) / C::TI;

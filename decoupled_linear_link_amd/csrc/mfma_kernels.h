@@ -132,14 +132,17 @@ __device__ __forceinline__ void st8(bf16_t* p, const float* v) {
 // in registers for the whole kernel.  The next tile's rows are prefetched
 // into registers while the current tile is computed.
 // ---------------------------------------------------------------------------
-template <int ELL, int D, int H>
+template <int ELL, int D, int H, bool I8 = false>
 struct QkCfg {
   static constexpr int NW = H >= 8 ? 8 : 4;               // waves per workgroup
   static constexpr int HPW = H > NW ? H / NW : 1;         // heads per wave
   static constexpr int WPH = NW > H ? NW / H : 1;         // waves per head
   static constexpr int MB = ELL / 16;                     // M-blocks per head
   static constexpr int KB = D / 32;                       // K-blocks
-  static constexpr int TI = 64;                           // items per tile
+  // items per tile: at d = 64 a bf16 tile of 128 items (16 KB of item rows
+  // per 4-wave workgroup) beats 64 (a catalogue of 100k items: 7.7 against
+  // 8.2 us); the int8 form, with its quantisation epilogue, stays at 64
+  static constexpr int TI = (D <= 64 && !I8) ? 128 : 64;
   static constexpr int NB = TI / 16;                      // 16-item blocks per tile
   static constexpr int NBW = NB / WPH;                    // item blocks per wave
   static constexpr int STRIDE = D * 2 + 16;               // LDS bytes per item row
@@ -233,10 +236,10 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
 }
 
 template <int ELL, int D, int H, bool I8 = false>
-__global__ __launch_bounds__((QkCfg<ELL, D, H>::NT)) void qk_cache(
+__global__ __launch_bounds__((QkCfg<ELL, D, H, I8>::NT)) void qk_cache(
     const bf16_t* __restrict__ items, const bf16_t* __restrict__ keys, void* __restrict__ cache_out,
     float* __restrict__ qscale, int64_t n_items, float scale, int phi, int64_t ntiles) {
-  using C = QkCfg<ELL, D, H>;
+  using C = QkCfg<ELL, D, H, I8>;
   __shared__ __attribute__((aligned(16))) char lds[C::TI * C::STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
