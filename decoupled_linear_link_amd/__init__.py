@@ -42,7 +42,8 @@ STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
           3: "LIME_ERR_WORKSPACE", 4: "LIME_ERR_HIP"}
 
 # every symbol include/lime.h declares
-EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_variant", "lime_xor_fwd_workspace_size", "lime_xor_fwd_plan",
+EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_variant", "lime_xor_fwd_score", "lime_xor_fwd_workspace_size",
+            "lime_xor_fwd_plan",
             "lime_qk_cache_build", "lime_qk_cache_build_i8", "lime_cand_score", "lime_cand_score_i8",
             "lime_cand_score_uncached", "lime_status_string", "lime_last_error")
 
@@ -69,6 +70,8 @@ lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32,
                              _vp, ctypes.c_size_t, _vp]
 lib.lime_xor_fwd_variant.restype = ctypes.c_int
 lib.lime_xor_fwd_variant.argtypes = [ctypes.c_int, _i32] + lib.lime_xor_fwd.argtypes
+lib.lime_xor_fwd_score.restype = ctypes.c_int
+lib.lime_xor_fwd_score.argtypes = lib.lime_xor_fwd.argtypes[:-1] + [_vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp]
 lib.lime_qk_cache_build.restype = ctypes.c_int
 lib.lime_qk_cache_build.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i64, _i32, _i32, _i32,
                                     _vp, _vp, _vp, _vp]
@@ -140,18 +143,11 @@ def xor_fwd_plan(dtype, B, ell, d, heads, layers, d_ff, total_N, max_N, with_his
     return int(n), buf.value.decode()
 
 
-def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
-            scale: float | None = None, max_N: int | None = None, want_hist: bool = False,
-            links_pers=None, hist_out=None, workspace=None, stream=None,
-            variant: str = "xor", window: int | None = None):
-    """Stacked LIME-XOR layers.  links_ctx [B, ell, d], hist [total_N, d],
-    hist_offsets [B+1] int64 (device), weights: list of per-layer dicts with
-    w_qkv [3d, d], w_o [d, d], w_gate/w_up [d_ff, d], w_down [d, d_ff].
-    variant "mha" (LIME-MHA, links -> history only) or "xor_window"
-    (LIME-XOR+Window, window neighbours on each side, default ell // 2).
-    Returns (links_pers [B, ell, d], hist_out [total_N, d] or None)."""
-    if variant not in VARIANT:
-        raise ValueError(f"variant must be one of {sorted(VARIANT)}")
+def _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale, max_N, want_hist, links_pers,
+              hist_out, workspace):
+    """Checks and marshals the user-side arguments: (argument tuple without
+    the stream, links_pers, hist_out, what must stay alive until the call:
+    the layer array and the workspace)."""
     _want(links_ctx, "links_ctx", dims=3)
     dt = links_ctx.dtype
     _want(hist, "hist", dt, 2)
@@ -181,7 +177,26 @@ def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=links_ctx.device)
     args = (DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
             _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
-            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel(), _stream(stream))
+            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel())
+    return args, links_pers, hist_out, (arr, workspace)
+
+
+def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
+            scale: float | None = None, max_N: int | None = None, want_hist: bool = False,
+            links_pers=None, hist_out=None, workspace=None, stream=None,
+            variant: str = "xor", window: int | None = None):
+    """Stacked LIME-XOR layers.  links_ctx [B, ell, d], hist [total_N, d],
+    hist_offsets [B+1] int64 (device), weights: list of per-layer dicts with
+    w_qkv [3d, d], w_o [d, d], w_gate/w_up [d_ff, d], w_down [d, d_ff].
+    variant "mha" (LIME-MHA, links -> history only) or "xor_window"
+    (LIME-XOR+Window, window neighbours on each side, default ell // 2).
+    Returns (links_pers [B, ell, d], hist_out [total_N, d] or None)."""
+    if variant not in VARIANT:
+        raise ValueError(f"variant must be one of {sorted(VARIANT)}")
+    args, links_pers, hist_out, keep = _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale,
+                                                max_N, want_hist, links_pers, hist_out, workspace)
+    args = args + (_stream(stream),)
+    ell = links_ctx.shape[1]
     if variant == "xor" and window is None:
         _check(lib.lime_xor_fwd(*args), "lime_xor_fwd")
     else:
@@ -189,6 +204,32 @@ def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu
             window = max(1, ell // 2) if variant == "xor_window" else 0
         _check(lib.lime_xor_fwd_variant(VARIANT[variant], int(window), *args), "lime_xor_fwd_variant")
     return links_pers, hist_out
+
+
+def xor_fwd_score(links_ctx, hist, hist_offsets, weights, heads: int, cache, cand_ids, cand_offsets,
+                  phi: str = "silu_mean", scale: float | None = None, max_N: int | None = None,
+                  want_hist: bool = False, links_pers=None, hist_out=None, workspace=None, out=None,
+                  bad_id_count=None, stream=None):
+    """xor_fwd (the XOR variant) followed by cand_score of every user's
+    candidates with the links it produced, as one call.  Returns
+    (links_pers, hist_out or None, scores [total_M, d])."""
+    args, links_pers, hist_out, keep = _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale,
+                                                max_N, want_hist, links_pers, hist_out, workspace)
+    _want(cache, "cache", links_ctx.dtype, 3)
+    _want(cand_ids, "cand_ids", torch.int64, 1)
+    _want(cand_offsets, "cand_offsets", torch.int64, 1)
+    n_items, H, ell = cache.shape
+    B, ell2, d = links_ctx.shape
+    if ell2 != ell or H != heads or cand_offsets.shape[0] != B + 1:
+        raise ValueError("shape mismatch between cache, links_ctx, heads and cand_offsets")
+    M = cand_ids.shape[0]
+    if out is None:
+        out = torch.empty((M, d), dtype=cache.dtype, device=cache.device)
+    if bad_id_count is not None:
+        _want(bad_id_count, "bad_id_count", torch.int32)
+    _check(lib.lime_xor_fwd_score(*args, _ptr(cache), n_items, _ptr(cand_ids), _ptr(cand_offsets), M,
+                                  _ptr(out), _ptr(bad_id_count), _stream(stream)), "lime_xor_fwd_score")
+    return links_pers, hist_out, out
 
 
 def qk_cache_build(items, link_keys, phi: str = "silu_mean", scale: float | None = None,

@@ -179,6 +179,10 @@ bool xor_mfma_ok(lime_dtype_t dtype, int ell, int d, int heads, int d_ff) {
 struct VariantArgs {
   bool links_only = false;  // LIME-MHA: history rows are never updated
   int half = 0;             // LIME-XOR+Window: neighbours on each side (0: none)
+  // candidate scoring inside the user-resident kernel (score.ids == nullptr:
+  // none); *scored is set when the launch took it
+  mfma::ScoreArgs score;
+  bool* scored = nullptr;
 };
 
 // widest window the matrix-core kernels serve for this ell
@@ -248,11 +252,11 @@ int max_dynamic_lds() {
   return v;
 }
 
-template <int ELL, int D, int NKW>
+template <int ELL, int D, int NKW, bool SC = false>
 void launch_resident(int B, size_t lds, hipStream_t st, const void* links_ctx, const void* hist,
                      const int64_t* off, int64_t total_N, int RT, int layers, const mfma::LayerSet& ls,
                      float scale, lime_phi_t phi, void* links_pers, void* hist_out, const VariantArgs& va) {
-  auto k = mfma::xor_fwd_resident<ELL, D, NKW>;
+  auto k = mfma::xor_fwd_resident<ELL, D, NKW, SC>;
   static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                160 * 1024) == hipSuccess;
@@ -260,7 +264,7 @@ void launch_resident(int B, size_t lds, hipStream_t st, const void* links_ctx, c
   hipLaunchKernelGGL(k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
                      static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
                      static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
-                     static_cast<bf16_t*>(hist_out), va.links_only ? 1 : 0, va.half);
+                     static_cast<bf16_t*>(hist_out), va.links_only ? 1 : 0, va.half, va.score);
 }
 
 // user-resident kernel: one workgroup per user, all layers, when the rows fit
@@ -285,14 +289,19 @@ bool run_xor_resident(const XorPlan& P, lime_phi_t phi, float scale, int B, int 
     ls.p[l][3] = static_cast<const bf16_t*>(w[l].w_up);
     ls.p[l][4] = static_cast<const bf16_t*>(w[l].w_down);
   }
+  const bool score = va.score.ids != nullptr && va.half == 0 && !va.links_only;
   if (va.half > 0)
     launch_resident<ELL, D, mfma::win_nkw(ELL)>(B, lds, st, links_ctx, hist, off, total_N, RT, layers, ls, scale,
                                                  phi, links_pers, hist_out, va);
+  else if (score)
+    launch_resident<ELL, D, 0, true>(B, lds, st, links_ctx, hist, off, total_N, RT, layers, ls, scale, phi,
+                                     links_pers, hist_out, va);
   else
     launch_resident<ELL, D, 0>(B, lds, st, links_ctx, hist, off, total_N, RT, layers, ls, scale, phi,
                                links_pers, hist_out, va);
   hipError_t e = hipGetLastError();
   *status = (e == hipSuccess) ? ok() : fail(LIME_ERR_HIP, "user-resident xor: %s", hipGetErrorString(e));
+  if (va.scored != nullptr && score) *va.scored = true;
   (void)P;
   return true;
   }
@@ -613,17 +622,23 @@ lime_status_t lime_xor_fwd(lime_dtype_t dtype, lime_phi_t phi, float scale, int3
                               workspace, workspace_bytes, stream);
 }
 
-lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_dtype_t dtype,
-                                   lime_phi_t phi, float scale, int32_t B, int32_t ell, int32_t d,
-                                   int32_t heads, int32_t layers, int32_t d_ff,
-                                   const void* links_ctx, const void* hist,
-                                   const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
-                                   const lime_layer_weights_t* w, void* links_pers,
-                                   void* hist_out, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+// score != nullptr: also score the candidates inside the user-resident
+// kernel when that path runs (*scored tells whether it did)
+static lime_status_t xor_fwd_impl(lime_variant_t variant, int32_t window, lime_dtype_t dtype,
+                                  lime_phi_t phi, float scale, int32_t B, int32_t ell, int32_t d,
+                                  int32_t heads, int32_t layers, int32_t d_ff,
+                                  const void* links_ctx, const void* hist,
+                                  const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
+                                  const lime_layer_weights_t* w, void* links_pers,
+                                  void* hist_out, void* workspace, size_t workspace_bytes,
+                                  void* stream, const mfma::ScoreArgs* score, bool* scored) {
   lime_status_t st = check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N);
   if (st != LIME_OK) return st;
   VariantArgs va;
+  if (score != nullptr) {
+    va.score = *score;
+    va.scored = scored;
+  }
   switch (variant) {
     case LIME_VARIANT_XOR:
       if (window != 0) return fail(LIME_ERR_INVALID_ARG, "window must be 0 for LIME_VARIANT_XOR");
@@ -679,6 +694,19 @@ lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_
                                       hist, hist_offsets, total_N, w, links_pers, hist_out, va, ws, s);
 }
 
+lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_dtype_t dtype,
+                                   lime_phi_t phi, float scale, int32_t B, int32_t ell, int32_t d,
+                                   int32_t heads, int32_t layers, int32_t d_ff,
+                                   const void* links_ctx, const void* hist,
+                                   const int64_t* hist_offsets, int64_t total_N, int32_t max_N,
+                                   const lime_layer_weights_t* w, void* links_pers,
+                                   void* hist_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return xor_fwd_impl(variant, window, dtype, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx, hist,
+                      hist_offsets, total_N, max_N, w, links_pers, hist_out, workspace, workspace_bytes, stream,
+                      nullptr, nullptr);
+}
+
 static lime_status_t qk_cache_impl(bool i8, lime_dtype_t dtype, lime_phi_t phi, float scale,
                                    int64_t n_items, int32_t d, int32_t heads, int32_t ell,
                                    const void* items, const void* link_keys, void* cache,
@@ -722,11 +750,11 @@ static lime_status_t qk_cache_impl(bool i8, lime_dtype_t dtype, lime_phi_t phi, 
   return ok();
 }
 
-static lime_status_t cand_score_impl(bool i8, lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
-                                     int32_t heads, const void* cache, const float* qscale,
-                                     int64_t n_items, const void* links_pers, const int64_t* cand_ids,
-                                     const int64_t* cand_offsets, int64_t total_M, void* out,
-                                     int32_t* bad_id_count, void* stream) {
+static lime_status_t check_score(bool i8, lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                 int32_t heads, const void* cache, const float* qscale, int64_t n_items,
+                                 const void* links_pers, const int64_t* cand_ids,
+                                 const int64_t* cand_offsets, int64_t total_M, void* out,
+                                 int32_t* bad_id_count) {
   if (dtype != LIME_F32 && dtype != LIME_BF16) return fail(LIME_ERR_INVALID_ARG, "bad dtype %d", (int)dtype);
   if (B < 1 || ell < 1 || d < 1 || heads < 1 || n_items < 0 || total_M < 0)
     return fail(LIME_ERR_INVALID_ARG, "sizes must be positive");
@@ -742,6 +770,17 @@ static lime_status_t cand_score_impl(bool i8, lime_dtype_t dtype, int32_t B, int
     return fail(LIME_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(bad_id_count) & 3u) != 0 || (reinterpret_cast<uintptr_t>(qscale) & 3u) != 0)
     return fail(LIME_ERR_INVALID_ARG, "bad_id_count and qscale must be 4-byte aligned");
+  return ok();
+}
+
+static lime_status_t cand_score_impl(bool i8, lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
+                                     int32_t heads, const void* cache, const float* qscale,
+                                     int64_t n_items, const void* links_pers, const int64_t* cand_ids,
+                                     const int64_t* cand_offsets, int64_t total_M, void* out,
+                                     int32_t* bad_id_count, void* stream) {
+  const lime_status_t cs = check_score(i8, dtype, B, ell, d, heads, cache, qscale, n_items, links_pers,
+                                       cand_ids, cand_offsets, total_M, out, bad_id_count);
+  if (cs != LIME_OK) return cs;
   if (total_M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == LIME_BF16) {
@@ -789,6 +828,37 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
                               const void* links_pers, const int64_t* cand_ids,
                               const int64_t* cand_offsets, int64_t total_M, void* out,
                               int32_t* bad_id_count, void* stream) {
+  return cand_score_impl(false, dtype, B, ell, d, heads, cache, nullptr, n_items, links_pers, cand_ids,
+                         cand_offsets, total_M, out, bad_id_count, stream);
+}
+
+lime_status_t lime_xor_fwd_score(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                 int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
+                                 const void* links_ctx, const void* hist, const int64_t* hist_offsets,
+                                 int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                                 void* links_pers, void* hist_out, void* workspace,
+                                 size_t workspace_bytes, const void* cache, int64_t n_items,
+                                 const int64_t* cand_ids, const int64_t* cand_offsets, int64_t total_M,
+                                 void* out, int32_t* bad_id_count, void* stream) {
+  // every argument of the scoring half is checked before anything launches
+  const lime_status_t cs = check_score(false, dtype, B, ell, d, heads, cache, nullptr, n_items, links_pers,
+                                       cand_ids, cand_offsets, total_M, out, bad_id_count);
+  if (cs != LIME_OK) return cs;
+  mfma::ScoreArgs sa;
+  if (dtype == LIME_BF16 && total_M > 0) {
+    sa.cache = static_cast<const bf16_t*>(cache);
+    sa.n_items = n_items;
+    sa.ids = cand_ids;
+    sa.coff = cand_offsets;
+    sa.total_M = total_M;
+    sa.out = static_cast<bf16_t*>(out);
+    sa.bad = bad_id_count;
+  }
+  bool scored = false;
+  const lime_status_t xs = xor_fwd_impl(LIME_VARIANT_XOR, 0, dtype, phi, scale, B, ell, d, heads, layers, d_ff,
+                                        links_ctx, hist, hist_offsets, total_N, max_N, w, links_pers, hist_out,
+                                        workspace, workspace_bytes, stream, &sa, &scored);
+  if (xs != LIME_OK || scored) return xs;
   return cand_score_impl(false, dtype, B, ell, d, heads, cache, nullptr, n_items, links_pers, cand_ids,
                          cand_offsets, total_M, out, bad_id_count, stream);
 }

@@ -1699,6 +1699,19 @@ struct LayerSet {
   const bf16_t* p[RES_MAX_LAYERS][5];
 };
 
+// Candidate scoring inside the user-resident kernel (its SC form): the
+// same operands and products as cand_score, for the candidates of the
+// workgroup's own user.
+struct ScoreArgs {
+  const bf16_t* cache = nullptr;  // [n_items, H, ELL]
+  int64_t n_items = 0;
+  const int64_t* ids = nullptr;   // [total_M]
+  const int64_t* coff = nullptr;  // [B + 1]
+  int64_t total_M = 0;
+  bf16_t* out = nullptr;          // [total_M, D]
+  int* bad = nullptr;
+};
+
 // 8 consecutive floats of an LDS row as two 16-byte accesses (the row
 // strides keep every such piece 16-byte aligned)
 __device__ __forceinline__ void lds_ld8f(const float* p, float* v) {
@@ -1750,11 +1763,11 @@ __device__ __forceinline__ const bf16_t* wsrc(const LayerSet& w, int l, int set,
   return w.p[l][1 + m] + static_cast<int64_t>(row - m * D) * D + 8 * c8;
 }
 
-template <int ELL, int D, int NKW = 0>
+template <int ELL, int D, int NKW = 0, bool SC = false>
 __global__ __launch_bounds__(512) void xor_fwd_resident(
     const bf16_t* __restrict__ links_ctx, const bf16_t* __restrict__ hist,
     const int64_t* __restrict__ off, int64_t total_N, int RT, int layers, LayerSet w, float scale, int phi,
-    bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out, int links_only, int half) {
+    bf16_t* __restrict__ links_pers, bf16_t* __restrict__ hist_out, int links_only, int half, ScoreArgs sa) {
   using C = ResCfg<ELL, D>;
   constexpr int H = D / 32, KB = D / 32, XS = C::XS, NW = C::NW, NT = C::NT;
   constexpr bool WL = C::WL;
@@ -1891,6 +1904,37 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     lds_barrier();
   }
 
+  // scoring form: this user's candidate range; waves idle in the last post
+  // phase take the first tiles and gather them during that phase (PF)
+  constexpr int KBL = ELL / 32;
+  constexpr bool PF = SC && D <= 64;
+  int64_t m0 = 0, m1 = 0, ntile = 0;
+  int sw = wv;  // this wave's first scoring tile
+  bf16x8 bw_pf[H][KBL];
+  int64_t i_pf = 0;
+  bool ok_pf = false, have_pf = false;
+  if constexpr (SC) {
+    m0 = clamp64(sa.coff[b], 0, sa.total_M);
+    m1 = clamp64(sa.coff[b + 1], m0, sa.total_M);
+    ntile = (m1 - m0 + 15) >> 4;
+    const bool full_last = !links_only && hist_out != nullptr;
+    const int pl = ((full_last ? rows : ELL) + 15) / 16;  // items of the last post phase
+    sw = (wv + NW - pl % NW) % NW;
+  }
+  auto gather_tile = [&](int64_t t, int64_t& i, bool& okid, bf16x8 (&bw)[H][KBL]) {
+    i = m0 + 16 * t + r;
+    const bool valid = i < m1;
+    const int64_t id = valid ? sa.ids[i] : int64_t(-1);
+    okid = id >= 0 && id < sa.n_items;
+    if (valid && !okid && g == 0 && sa.bad != nullptr) atomicAdd(sa.bad, 1);
+    const int64_t idc = okid ? id : 0;
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+      for (int kb = 0; kb < KBL; ++kb)
+        bw[hh][kb] = okid ? ld16(sa.cache + (idc * H + hh) * ELL + 8 * g + kb * 32) : zero8();
+  };
+
   for (int l = 0; l < layers; ++l) {
     const bool last = (l == layers - 1);
     // history rows get attention and the post block unless nothing can
@@ -1961,6 +2005,12 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
     constexpr int PR = 16 * PRB;
     const int prow_end = full ? rows : ELL;  // a multiple of PR when not every row
     const int pitems = ((last ? prow_end : rows) + PR - 1) / PR;
+    if constexpr (PF) {
+      if (last && wv >= pitems && sw < ntile) {
+        gather_tile(sw, i_pf, ok_pf, bw_pf);
+        have_pf = true;
+      }
+    }
     for (int it = wv; it < pitems; it += NW) {
       const int row0 = it * PR;
       const bool do_post = row0 < prow_end;
@@ -2008,11 +2058,64 @@ __global__ __launch_bounds__(512) void xor_fwd_resident(
             if (dst)
 #pragma unroll
               for (int kb = 0; kb < KB; ++kb) st8(dst + kb * 32 + 8 * g, &x1[rb][8 * kb]);
+            // scoring reads the user's L^P from the Y rows (this item has
+            // already read its own)
+            if (SC && row < ELL)
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb) st8(Ys + row * LY + kb * 32 + 8 * g, &x1[rb][8 * kb]);
           }
         }
       }
     }
     lds_barrier();
+  }
+
+  // ---- candidate scoring of this user's candidates: 16-candidate tiles
+  // round-robin over the waves; per head O^T = L^P_h^T (cache rows)^T, the
+  // operand layout, products and output rounding of cand_score
+  if constexpr (SC) {
+    if (sw < ntile) {
+      bf16x8 a[H][2][KBL];
+#pragma unroll
+      for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int col = hh * 32 + 8 * (r >> 2) + 4 * c + (r & 3);
+#pragma unroll
+          for (int kb = 0; kb < KBL; ++kb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[hh][c][kb][j] = __builtin_bit_cast(__bf16, Ys[(kb * 32 + 8 * g + j) * LY + col]);
+        }
+      for (int64_t t = sw; t < ntile; t += NW) {
+        int64_t i;
+        bool okid;
+        bf16x8 bw[H][KBL];
+        if (PF && have_pf && t == sw) {
+          i = i_pf;
+          okid = ok_pf;
+#pragma unroll
+          for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+            for (int kb = 0; kb < KBL; ++kb) bw[hh][kb] = bw_pf[hh][kb];
+        } else {
+          gather_tile(t, i, okid, bw);
+        }
+        const bool valid = i < m1;
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+          floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KBL; ++kb) {
+            acc0 = mma(a[hh][0][kb], bw[hh][kb], acc0);
+            acc1 = mma(a[hh][1][kb], bw[hh][kb], acc1);
+          }
+          if (valid) {
+            const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+            st8_stream(sa.out + i * D + hh * 32 + 8 * g, v);
+          }
+        }
+      }
+    }
   }
 }
 

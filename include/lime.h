@@ -3,7 +3,8 @@
  * (gfx950).
  *
  * Three operations, following the LIME pages (plus the int8, uncached and
- * user-side variant forms declared further down):
+ * user-side variant forms and a combined user-side + scoring call declared
+ * further down):
  *
  *   lime_xor_fwd        user side: stacked LIME-XOR layers over the context
  *                       links L^C and the user history E, giving the
@@ -212,6 +213,27 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
                               const void* links_pers, const int64_t* cand_ids,
                               const int64_t* cand_offsets, int64_t total_M, void* out,
                               int32_t* bad_id_count, void* stream);
+
+/* User side and candidate scoring in one call: the online stage run for a
+ * batch of requests, each user's personalised links followed at once by the
+ * scoring of that user's candidates (LIME notes, framework flowchart, online
+ * stage; "complete example", steps 2 and 3).  Arguments, results, errors and
+ * limits are those of lime_xor_fwd followed by lime_cand_score on the same
+ * stream (links_pers is written as there and is the scoring's input); for
+ * offsets that meet their preconditions the outputs and bad_id_count are
+ * bit-identical to that pair of calls.  On the user-resident
+ * path (short histories, bf16) each user's workgroup scores its own
+ * candidates from the links it holds on chip, so the pair costs one launch;
+ * elsewhere the call makes the two launches.  Every argument of both halves
+ * is checked before anything is enqueued.                                  */
+lime_status_t lime_xor_fwd_score(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                 int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
+                                 const void* links_ctx, const void* hist, const int64_t* hist_offsets,
+                                 int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                                 void* links_pers, void* hist_out, void* workspace,
+                                 size_t workspace_bytes, const void* cache, int64_t n_items,
+                                 const int64_t* cand_ids, const int64_t* cand_offsets, int64_t total_M,
+                                 void* out, int32_t* bad_id_count, void* stream);
 
 /* Int8 QK cache (LIME summary page, Tables 10 and 12: int8 lookup with
  * dequantisation, int8 cache sizes; the scheme is not given there).  Same
