@@ -1,6 +1,7 @@
 """The hot path captured in a HIP graph: every replay must reproduce the
 eager result, with eager work and synchronisations between the replays.
-Both user-side paths are covered (user-resident and streaming)."""
+Both user-side paths are covered (user-resident and streaming), as three
+calls and as the bench's step (cache build, then lime_xor_fwd_score)."""
 import numpy as np
 import pytest
 import torch
@@ -19,8 +20,9 @@ def L():
     return lib
 
 
+@pytest.mark.parametrize("combined", [False, True])
 @pytest.mark.parametrize("max_n_hint", [None, 4096])
-def test_graph_replays_match_eager(L, max_n_hint):
+def test_graph_replays_match_eager(L, max_n_hint, combined):
     w = W.workload("ctr")
     ui, ci = user_inputs("ctr"), cache_inputs("ctr")
     off = ui["hist_offsets"]
@@ -37,10 +39,16 @@ def test_graph_replays_match_eager(L, max_n_hint):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
 
     def step():
+        if combined:
+            L.qk_cache_build(items, keys, phi=w.phi, cache=cache)
+            L.xor_fwd_score(lc, hs, ho, wts, heads=w.heads, cache=cache, cand_ids=ids, cand_offsets=coff,
+                            phi=w.phi, max_N=max_n, links_pers=lp, workspace=ws, out=out)
+            return
         L.xor_fwd(lc, hs, ho, wts, heads=w.heads, phi=w.phi, max_N=max_n, links_pers=lp, workspace=ws)
         L.qk_cache_build(items, keys, phi=w.phi, cache=cache)
         L.cand_score(cache, lp, ids, coff, out=out)
 
+    print(f"graph replays max_N hint={max_n_hint} combined={combined}", flush=True)
     step()
     torch.cuda.synchronize()
     ref = (lp.clone(), cache.clone(), out.clone())
