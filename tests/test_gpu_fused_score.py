@@ -104,3 +104,34 @@ def test_fused_without_candidates_and_twice_in_a_row(L):
         assert torch.equal(_bits(lp1), _bits(lp2)), f"links_pers, call {k}"
         assert out2.shape[0] == sum(counts)
         assert torch.equal(_bits(out1), _bits(out2)), f"scores, call {k}"
+
+
+@pytest.mark.parametrize("name", ["ctr", "large_m"])
+def test_fused_equals_the_two_calls_at_workload_size(L, name):
+    """The bench's configuration (ctr: 256 users, 8,192 candidates, the
+    user-resident path) and a streaming one (large-M users with a sample of
+    their candidates): bit-identical to the two calls."""
+    from parity_utils import cache_inputs, ids_for, user_inputs
+    w = W.workload(name)
+    ui, ci = user_inputs(name), cache_inputs(name)
+    off = ui["hist_offsets"]
+    scale = W.scale_for(w)
+    ids, coff = ids_for(name), W.candidate_offsets(w)
+    if name == "large_m":  # the first 4,096 candidates of every user
+        per = np.minimum(np.diff(coff), 4096)
+        ids = np.concatenate([ids[coff[b]:coff[b] + per[b]] for b in range(w.B)])
+        coff = W.offsets_from_lengths(per)
+    print(f"fused score at {name} size: B={w.B} candidates={len(ids)}", flush=True)
+    cache = torch.empty((min(w.n_items, 1 << 20), w.heads, w.ell), dtype=torch.bfloat16, device="cuda")
+    n_items = cache.shape[0]
+    L.qk_cache_build(dev(ci["items"][:n_items]), dev(ci["link_keys"]), phi=w.phi, scale=scale, cache=cache)
+    ids = np.where(ids < n_items, ids, ids % n_items)
+    args = (dev(ui["links_ctx"]), dev(ui["hist"]), dev(off), dev_weights(ui["weights"]))
+    max_n = int(np.diff(off).max())
+    lp1, _ = L.xor_fwd(*args, heads=w.heads, phi=w.phi, scale=scale, max_N=max_n)
+    out1 = L.cand_score(cache, lp1, dev(ids), dev(coff))
+    lp2, _, out2 = L.xor_fwd_score(*args, heads=w.heads, cache=cache, cand_ids=dev(ids), cand_offsets=dev(coff),
+                                   phi=w.phi, scale=scale, max_N=max_n)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(lp1), _bits(lp2)), "links_pers"
+    assert torch.equal(_bits(out1), _bits(out2)), "scores"
