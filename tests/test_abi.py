@@ -169,3 +169,26 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.replace("oracle is", ""), f
+
+
+@pytest.mark.parametrize("kw,skw,code", [
+    ({}, dict(ids=None), 1), ({}, dict(cache=None), 1), ({}, dict(out=None), 1), ({}, dict(out=PM), 1),
+    ({}, dict(bad=P + 2), 1), ({}, dict(M=-1), 1), ({}, dict(coff=None), 1),
+    (dict(phi=5), {}, 1), (dict(layers=0), {}, 1), (dict(lp=None), {}, 1), (dict(ell=300), {}, 2),
+    (dict(ws=None), {}, 3), (dict(ws_bytes=1024), {}, 3),
+])
+def test_xor_fwd_score_rejects(L, kw, skw, code):
+    """Errors of either half (the user side or the scoring) return before
+    anything is enqueued."""
+    a = _xor_args(**kw)
+    s = dict(cache=P, n=100, ids=P, coff=P, M=10, out=P, bad=None)
+    s.update(skw)
+    arr = (L.LayerWeights * max(1, a["layers"]))()
+    for i in range(max(1, a["layers"])):
+        arr[i] = L.LayerWeights(P, P, P, P, P)
+    st = L.lib.lime_xor_fwd_score(a["dtype"], a["phi"], a["scale"], a["B"], a["ell"], a["d"], a["heads"],
+                                  a["layers"], a["d_ff"], a["links_ctx"], a["hist"], a["off"], a["total_N"],
+                                  a["max_N"], arr, a["lp"], a["ho"], a["ws"], a["ws_bytes"], s["cache"], s["n"],
+                                  s["ids"], s["coff"], s["M"], s["out"], s["bad"], None)
+    assert st == code
+    assert L.lib.lime_last_error().decode() != ""
