@@ -1699,8 +1699,10 @@ struct LayerSet {
   const bf16_t* p[RES_MAX_LAYERS][5];
 };
 
-// Candidate scoring inside the user-resident kernel (its SC form): the
-// same operands and products as cand_score, for the candidates of the
+// Candidate scoring inside the user-resident kernel (its SC form; LIME
+// notes, "complete example", step 3: the cached weights of a candidate,
+// looked up by id, weight the user's personalised links): the same
+// operands and products as cand_score, for the candidates of the
 // workgroup's own user.
 struct ScoreArgs {
   const bf16_t* cache = nullptr;  // [n_items, H, ELL]
