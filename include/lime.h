@@ -224,8 +224,9 @@ lime_status_t lime_cand_score(lime_dtype_t dtype, int32_t B, int32_t ell, int32_
  * bit-identical to that pair of calls.  On the user-resident
  * path (short histories, bf16) each user's workgroup scores its own
  * candidates from the links it holds on chip, so the pair costs one launch;
- * elsewhere the call makes the two launches.  Every argument of both halves
- * is checked before anything is enqueued.                                  */
+ * elsewhere the call enqueues lime_xor_fwd's kernels and then the scoring
+ * kernel.  Every argument of both halves is checked before anything is
+ * enqueued.                                                                */
 lime_status_t lime_xor_fwd_score(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
                                  int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
                                  const void* links_ctx, const void* hist, const int64_t* hist_offsets,

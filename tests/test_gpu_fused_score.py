@@ -3,7 +3,8 @@ candidates in one call) against lime_xor_fwd followed by lime_cand_score:
 links, scores, history rows and the bad-id count must be bit-identical.
 Covers the user-resident path, where the scoring runs inside the user-side
 kernel (ell = 32 with d = 64, ell = 64 with d = 128), the streaming path and
-the float32 generic path, where the call makes the two launches; ragged and
+the float32 generic path, where the call runs the user side's kernels and
+then the scoring kernel; ragged and
 empty candidate lists, out-of-range ids, both phi.  One case is also checked
 against the oracle."""
 import numpy as np
