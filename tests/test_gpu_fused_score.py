@@ -2,7 +2,7 @@
 candidates in one call) against lime_xor_fwd followed by lime_cand_score:
 links, scores, history rows and the bad-id count must be bit-identical.
 Covers the user-resident path, where the scoring runs inside the user-side
-kernel (ell = 32 with d = 64, ell = 64 with d = 128), the streaming path and
+kernel (ell = 32 and 64 with d = 64, ell = 64 with d = 128), the streaming path and
 the float32 generic path, where the call runs the user side's kernels and
 then the scoring kernel; ragged and
 empty candidate lists, out-of-range ids, both phi.  One case is also checked
@@ -30,10 +30,14 @@ def L():
 CASES = [
     ("bf16", 32, 64, 2, 2, [50, 0, 17, 64, 3], [0, 1, 17, 40, 16], None),     # user-resident
     ("bf16", 64, 128, 4, 2, [32, 5, 0], [33, 0, 16], None),                   # user-resident, ell = 64
+    ("bf16", 64, 64, 2, 3, [30, 1, 0, 32], [40, 17, 0, 100], None),           # user-resident, ell = 64, d = 64
     ("bf16", 32, 128, 4, 1, [300, 40, 0, 9], [7, 0, 50, 1], None),            # streaming
     ("bf16", 32, 64, 2, 2, [50, 3, 20], [20, 20, 5], 4096),                   # streaming (max_N hint)
     ("f32", 8, 32, 1, 1, [10, 0, 7], [3, 5, 0], None),                        # generic
 ]
+
+
+RESIDENT = {0, 1, 2}  # cases planned on the user-resident path (scored inside the kernel)
 
 
 def _bits(t):
@@ -68,6 +72,9 @@ def test_fused_equals_the_two_calls(L, case, phi):
     scale = (d // H) ** -0.5
     max_n = hint if hint is not None else max(lens)
     print(f"fused score case {case} {phi}: {dt} ell={ell} d={d} lens={lens} counts={counts}", flush=True)
+    launches, plan = L.xor_fwd_plan(torch.bfloat16 if dt == "bf16" else torch.float32, len(lens), ell, d, H,
+                                    layers, d, int(off[-1]), max_n)
+    assert (launches == 1 and "user-resident" in plan) == (case in RESIDENT), plan
     cache = L.qk_cache_build(dev(items), dev(keys), phi=phi, scale=scale)
     args = (dev(lc), dev(hs) if hs.shape[0] else torch.empty((0, d), dtype=cache.dtype, device="cuda"),
             dev(off), dev_weights(ws))
