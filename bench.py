@@ -1,31 +1,39 @@
 """Benchmark of the LIME inference hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-  lime_qk_cache_build (QK cache over the whole catalogue), then
-  lime_xor_fwd_score  (user encoder over all B users and all layers, and the
-                       scoring of all B*M candidates: lime_xor_fwd followed
-                       by lime_cand_score in one call, one launch on the
-                       user-resident path)
-Inputs are resident in HBM before the timed region starts.  The step made of
-the three separate calls is timed alongside (`ms_per_step_separate_calls`).
+  lime_qk_cache_build (the QK cache over the whole catalogue: the offline
+                       stage), then
+  lime_xor_fwd_score  (the online stage: user encoder over all B users and
+                       all layers, and the scoring of all B*M candidates;
+                       lime_xor_fwd followed by lime_cand_score in one call)
+Inputs are resident in HBM before the timed region starts.  The default
+workload is the largest one that fits one GPU (lifelong: 8 users with
+8,192-16,384 history rows, ell = 64, d = 256, 8 heads, 4 layers, a 4M-item
+catalogue, 65,536 candidates).
 
-    python bench.py [--steps K] [--warmup W] [--workload ctr] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload lifelong] [--no-cpu-baseline]
 
 Prints ONE JSON line.  `value` = candidates scored per second of whole-step
-time; users encoded/s and items cached/s are reported alongside.  The K
-timed steps are captured in one HIP graph and replayed once (every kernel
-of every step is a graph node; --no-graph launches them eagerly instead).  The `roofline` object is
-for the kernel with the largest share of step time, its duration measured
-with HIP events on the launch stream around a graph of K back-to-back calls
-(per-call times are the median of 5 such graphs, the minimum alongside);
-`scoring` has candidate scoring cold (each call after a 512 MiB write and a
-512 MiB read that evict L2 and the Infinity Cache) and warm, for the
-workload's ids and for a uniform-id control with no reuse; `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same workload.
+time; `online` has the rate of the online call alone (lime_xor_fwd_score),
+without the catalogue rebuild.  The K timed steps are captured in one HIP
+graph and replayed once.  Per-call times are HIP events on the launch
+stream around a graph of K back-to-back calls (median of 5, minimum
+alongside).  Per-kernel times come from a kernel trace of the library
+(lime_trace_begin / lime_trace_end: every launch stamped with its own start
+and end by the runtime), taken over eager calls after the timed region.
+
+`rooflines` puts each kernel against max(algorithmic bytes / 8 TB/s,
+algorithmic flops / peak); `roofline` is the kernel with the largest share
+of the step's kernel time.  `scoring` has candidate scoring cold (each call
+after a 512 MiB write and a 512 MiB read that evict L2 and the Infinity
+Cache) and warm, for the workload's ids and for a uniform-id control with
+no reuse; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,25 +45,147 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_PEAK_TFLOPS = 2500.0
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA bf16; fp32 vector
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ctr")
+    ap.add_argument("--workload", default="lifelong")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
     ap.add_argument("--no-graph", action="store_true",
-                    help="launch the timed steps eagerly instead of replaying a HIP graph of one step")
+                    help="launch the timed steps eagerly instead of replaying a HIP graph of them")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip timing the int8 and uncached candidate-side variants")
+                    help="skip the cold-scoring, int8, uncached and user-side variant timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter scaling)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# algorithmic work per launch (bytes each kernel must move, flops it must do)
+# --------------------------------------------------------------------------
+
+def xor_fwd_flops(w, lens):
+    """Algorithmic flops of one lime_xor_fwd call without hist_out: every
+    layer projects all rows (QKV 6d^2, W_o 2d^2, gated MLP 6 d d_ff per row)
+    and runs both XOR branches (8 ell N d per user); the last layer needs
+    only the K,V projection of history rows (4d^2) and the link-side branch
+    (4 ell N d)."""
+    d, f, ell, L = w.d, w.dff, w.ell, w.layers
+    N = float(np.sum(lens))
+    rows_link = w.B * ell
+    full = (rows_link + N) * (8 * d * d + 6 * d * f) + 8 * ell * N * d
+    last = rows_link * (8 * d * d + 6 * d * f) + N * 4 * d * d + 4 * ell * N * d
+    return (L - 1) * full + last
+
+
+def kernel_work(w, es, total_N, n_cand):
+    """name -> f(full) = (bytes, flops) of one launch of that kernel, where
+    `full` says whether the layer also updates history rows (every layer but
+    the last when hist_out is not requested).  Bytes are what the method
+    must move (inputs read once, outputs written once), not what a kernel
+    happens to move."""
+    d, f, ell, H = w.d, w.dff, w.ell, w.heads
+    N, nlr = float(total_N), float(w.B * ell)
+    R = N + nlr
+
+    def qkv(full):
+        # read X; write Q (all rows, or links only), K and V
+        q_rows = R if full else nlr
+        return (R + q_rows + 2 * R) * d * es, 2.0 * d * d * (q_rows + 2 * R)
+
+    def attn(full):
+        # per user-layer 4 (N + ell) d s: read Q, K, V, write Y; the links-only
+        # last layer reads K_E, V_E and the links' Q, K, V, writes Y_L
+        if full:
+            return 4 * R * d * es, 8.0 * ell * N * d
+        return (2 * N + 4 * nlr) * d * es, 4.0 * ell * N * d
+
+    def attn_fused(full):
+        # the history rows' LN + QKV inside the attention: read X, write Y_E
+        # (the links' Y comes from the split combine)
+        if full:
+            return (R + N) * d * es, 2.0 * d * 3 * d * R + 8.0 * ell * N * d
+        return R * d * es, 2.0 * d * 2 * d * N + 2.0 * d * 3 * d * nlr + 4.0 * ell * N * d
+
+    def post(full):
+        rows = R if full else nlr
+        return 3 * rows * d * es, rows * (2.0 * d * d + 6.0 * d * f)
+
+    def combine(full):
+        return nlr * d * es, 0.0
+
+    user_bytes = (2 * nlr + N) * d * es
+
+    def resident(full):
+        return user_bytes, xor_fwd_flops(w, [total_N])
+
+    def resident_score(full):
+        cb, cf = cand(full)
+        return user_bytes + cb, xor_fwd_flops(w, [total_N]) + cf
+
+    def cache(full):
+        return w.n_items * (d + H * ell) * es, 2.0 * w.n_items * d * H * ell
+
+    def cand(full):
+        return n_cand * (H * ell * es + d * es + 8), 2.0 * n_cand * ell * d
+
+    return {"qkv_proj_stream": qkv, "qkv_proj_lds": qkv, "xor_attn": attn, "xor_attn_qkv": attn_fused,
+            "xor_combine": combine, "post_block_stream": post, "post_block_lds": post,
+            "xor_fwd_resident": resident, "xor_fwd_resident_score": resident_score,
+            "qk_cache": cache, "cand_score": cand}
+
+
+def against_roof(bytes_, flops, seconds, peak_tflops):
+    """bound, roofline time and fraction: t_roof = max(bytes/BW, flops/peak)."""
+    t_b = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_f = flops / (peak_tflops * 1e12)
+    t_roof = max(t_b, t_f)
+    return {"bound": "hbm" if t_b >= t_f else ("mfma" if peak_tflops == PEAK_TFLOPS["bf16"] else "alu"),
+            "roofline_us": round(t_roof * 1e6, 3),
+            "frac": round(t_roof / seconds, 4),
+            "GB/s": round(bytes_ / seconds / 1e9, 1), "frac_of_hbm_peak": round(t_b / seconds, 4),
+            "TFLOP/s": round(flops / seconds / 1e12, 2), "frac_of_flops_peak": round(t_f / seconds, 4),
+            "algorithmic_bytes": int(bytes_), "algorithmic_flops": float(flops)}
+
+
+def traffic_from_profiles(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE in
+    KiB per dispatch, scaled by the copy-kernel factors recorded there), or
+    None if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("sources_sha256") != sources_sha256():
+            return None
+        return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])
+                   + float(kv["write_kib"]) * 1024 * float(kv["write_factor"]))
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decoupled_linear_link_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def main():
@@ -73,6 +203,7 @@ def main():
     w = W.workload(args.workload)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16}[w.dtype]
     es = 4 if w.dtype == "f32" else 2
+    peak_tf = PEAK_TFLOPS[w.dtype]
     scale = W.scale_for(w)
 
     def dev(a):
@@ -82,13 +213,16 @@ def main():
         return torch.from_numpy(a).cuda()
 
     # ---- inputs, resident in HBM
+    log(f"generating the {w.name} inputs")
+    t_gen = time.perf_counter()
     ui = W.user_inputs(w)
     ci = W.cache_inputs(w)
     ids = W.candidate_ids(w)
     coff = W.candidate_offsets(w)
     off = ui["hist_offsets"]
+    lens = np.diff(off)
     total_N = int(off[-1])
-    max_N = int(np.diff(off).max())
+    max_N = int(lens.max())
     lc, hs, hoff = dev(ui["links_ctx"]), dev(ui["hist"]), dev(off)
     wts = [{k: dev(v) for k, v in lw.items()} for lw in ui["weights"]]
     items, keys = dev(ci["items"]), dev(ci["link_keys"])
@@ -98,6 +232,7 @@ def main():
     out = torch.empty((len(ids), w.d), dtype=dt, device="cuda")
     ws_bytes = L.xor_fwd_workspace_size(dt, w.B, w.ell, w.d, w.heads, w.dff, total_N, max_N)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    log(f"inputs on the device ({time.perf_counter() - t_gen:.1f} s)")
 
     def user(stream=None):
         L.xor_fwd(lc, hs, hoff, wts, heads=w.heads, phi=w.phi, scale=scale, max_N=max_N,
@@ -145,6 +280,7 @@ def main():
         torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps
+    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     if graph is not None:
         graph.replay()
@@ -154,6 +290,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    del graph
 
     def time_calls(fn, reps, repeats=5):
         """Per-call milliseconds (median, min over `repeats`) from HIP events
@@ -172,8 +309,8 @@ def main():
         del g
         return float(np.median(ts)), float(min(ts))
 
-    # ---- the step made of the three separate calls, and the per-call
-    # durations
+    # ---- per-call durations, and the step as three separate calls
+    log("timing the calls")
     ms_sep = time_calls(step_separate, args.steps)[0]
     calls = {"lime_xor_fwd": user, "lime_qk_cache_build": build, "lime_cand_score": score,
              "lime_xor_fwd_score": user_score}
@@ -181,64 +318,91 @@ def main():
     for k, fn in calls.items():
         call_ms[k], call_min_ms[k] = time_calls(fn, args.steps)
 
-    # roofline of the kernel with the largest share of step time among the
-    # calls that are one kernel launch (lime_xor_fwd is one launch on the
-    # user-resident path)
+    # ---- per-kernel durations: a trace of eager steps (each launch stamped
+    # with its own start and end on the GPU)
+    log("tracing the kernels of the step")
     n_cand = len(ids)
     launches, plan = L.xor_fwd_plan(dt, w.B, w.ell, w.d, w.heads, w.layers, w.dff, total_N, max_N)
-    algo = {
-        "lime_qk_cache_build": dict(kernel="qk_cache", bound="hbm",
-                                    bytes=w.n_items * (w.d + w.heads * w.ell) * es,
-                                    flops=2.0 * w.n_items * w.d * w.heads * w.ell),
-        "lime_cand_score": dict(kernel="cand_score", bound="hbm",
-                                bytes=n_cand * (w.heads * w.ell * es + w.d * es + 8),
-                                flops=2.0 * n_cand * w.ell * w.d),
-    }
-    # the step's single-launch calls: the cache build, and either the
-    # user-resident kernel in its scoring form (lime_xor_fwd_score is one
-    # launch) or the scoring kernel the call launches after the user side
-    in_step = ["lime_qk_cache_build"]
-    if launches == 1:
-        cs = algo["lime_cand_score"]
-        algo["lime_xor_fwd_score"] = dict(kernel="xor_fwd_resident_score", bound="mfma",
-                                          bytes=(w.B * w.ell * 2 + total_N) * w.d * es + cs["bytes"],
-                                          flops=xor_fwd_flops(w, np.diff(off)) + cs["flops"])
-        in_step.append("lime_xor_fwd_score")
+    work = kernel_work(w, es, total_N, n_cand)
+    trace_steps = 5
+    L.trace_begin(4096)
+    for _ in range(trace_steps):
+        step()
+    torch.cuda.synchronize()
+    recs, dropped = L.trace_end(4096)
+    if dropped:
+        log(f"trace dropped {dropped} launches")
+    # each record: (name, ms, full) where full = the layer updates history
+    # rows; layers are counted by the launch that opens each of them
+    opens = ("qkv_proj_stream", "qkv_proj_lds", "xor_attn_qkv")
+    per_layer = ("xor_attn", "xor_attn_qkv", "qkv_proj_stream", "qkv_proj_lds", "post_block_stream",
+                 "post_block_lds")
+    per = {}
+    layer = -1
+    for name, ms in recs:
+        if name == "split_plan":
+            layer = -1  # a streaming user side starts
+        elif name in opens:
+            layer += 1
+        full = layer < w.layers - 1
+        key = f"{name}[{'full' if full else 'last'}]" if name in per_layer else name
+        per.setdefault(key, {"name": name, "full": full, "ms": []})["ms"].append(ms)
+    step_kernel_ms = sum(ms for _, ms in recs) / trace_steps
+    rooflines = {}
+    for key, v in per.items():
+        t_mean = float(np.mean(v["ms"])) * 1e-3
+        share = sum(v["ms"]) / trace_steps / step_kernel_ms
+        entry = {"us": round(t_mean * 1e6, 2), "launches_per_step": len(v["ms"]) // trace_steps,
+                 "share_of_step_kernel_time": round(share, 4)}
+        if v["name"] in work:
+            b, f = work[v["name"]](v["full"])
+            entry.update(against_roof(b, f, t_mean, peak_tf))
+        rooflines[key] = entry
+    # the MFMA ceiling of the cache build: its intensity over the MFMA ridge
+    if "qk_cache" in rooflines:
+        r = rooflines["qk_cache"]
+        ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+        r["mfma_ceiling_at_hbm_peak"] = round(min(1.0, r["algorithmic_flops"] / r["algorithmic_bytes"] / ridge), 4)
+
+    # ---- the headline roofline: the kernel with the largest share of the
+    # step's kernel time.  A kernel that is a whole call (the cache build,
+    # scoring) is timed by events around K back-to-back calls; the others by
+    # their traced mean.
+    dom = max((k for k in rooflines if "algorithmic_bytes" in rooflines[k]),
+              key=lambda k: rooflines[k]["share_of_step_kernel_time"])
+    whole_call = {"qk_cache": "lime_qk_cache_build", "cand_score": "lime_cand_score",
+                  "xor_fwd_resident_score": "lime_xor_fwd_score"}
+    dname = per[dom]["name"]
+    t_dom = (call_ms[whole_call[dname]] * 1e-3) if dname in whole_call else rooflines[dom]["us"] * 1e-6
+    b, f = work[dname](per[dom]["full"])
+    rr = against_roof(b, f, t_dom, peak_tf)
+    if rr["bound"] == "hbm":
+        achieved, peak, unit = b / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
-        in_step.append("lime_cand_score")
-    single = {k: v for k, v in call_ms.items() if k in in_step}
-    dom = max(single, key=single.get)
-    a = algo[dom]
-    t = single[dom] * 1e-3
-    if a["bound"] == "hbm":
-        achieved, peak, unit = a["bytes"] / t / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved, peak, unit = a["flops"] / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    roofline = {"kernel": a["kernel"], "bound": a["bound"], "achieved": round(achieved, 2),
-                "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic_from_profiles(w.name, a["kernel"]),
-                "avg_launch_us": round(single[dom] * 1e3, 2),
-                "algorithmic_bytes_per_launch": int(a["bytes"]),
-                "algorithmic_flops_per_launch": float(a["flops"])}
-    # the user side against its roofline: algorithmic flops of the call, and
-    # the fused minimum of HBM bytes (every layer reads and writes each row of
-    # the residual stream once: 2 (B ell + N) d s per layer), at the peaks
+        achieved, peak, unit = f / t_dom / 1e12, peak_tf, "TFLOP/s"
+    roofline = {"kernel": dname, "bound": rr["bound"], "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic_from_profiles(w.name, dname),
+                "avg_launch_us": round(t_dom * 1e6, 2), "traced_launch_us": rooflines[dom]["us"],
+                "algorithmic_bytes_per_launch": int(b), "algorithmic_flops_per_launch": float(f),
+                "other_bound_frac": rr["frac_of_flops_peak"] if rr["bound"] == "hbm" else rr["frac_of_hbm_peak"]}
+
+    # ---- the user side against its roofline: algorithmic flops of the call
+    # and the fused minimum of HBM bytes (every layer reads and writes each
+    # row of the residual stream once: 2 (B ell + N) d s per layer)
     t_user = call_ms["lime_xor_fwd"] * 1e-3
-    u_flops = xor_fwd_flops(w, np.diff(off))
+    u_flops = xor_fwd_flops(w, lens)
     u_bytes = 2.0 * w.layers * (w.B * w.ell + total_N) * w.d * es
-    u_roof = max(u_bytes / (HBM_PEAK_GBS * 1e9), u_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    u_roof = max(u_bytes / (HBM_PEAK_GBS * 1e9), u_flops / (peak_tf * 1e12))
     user_side = {"us": round(t_user * 1e6, 2), "users_per_s": round(w.B / t_user, 1),
                  "history_rows_per_s": round(total_N / t_user, 1),
                  "TFLOP/s": round(u_flops / t_user / 1e12, 2),
                  "fused_min_bytes": int(u_bytes), "fused_min_GB/s": round(u_bytes / t_user / 1e9, 1),
                  "roofline_us": round(u_roof * 1e6, 2), "frac": round(u_roof / t_user, 4),
                  "launches": launches}
-    per_call = {}
-    for k, v in algo.items():
-        tk = call_ms[k] * 1e-3
-        per_call[k] = {"us": round(call_ms[k] * 1e3, 2), "us_min": round(call_min_ms[k] * 1e3, 2),
-                       "GB/s": round(v["bytes"] / tk / 1e9, 1),
-                       "TFLOP/s": round(v["flops"] / tk / 1e12, 2)}
+    t_online = call_ms["lime_xor_fwd_score"] * 1e-3
+    online = {"call": "lime_xor_fwd_score", "us": round(t_online * 1e6, 2),
+              "candidates_per_s": round(n_cand / t_online, 1), "users_per_s": round(w.B / t_online, 1)}
 
     # ---- scoring cold and with no id reuse.  Cold: every timed call follows
     # a 512 MiB write and then a 512 MiB read of another buffer, which evict
@@ -249,7 +413,9 @@ def main():
     # draws the same number of candidates uniformly over the catalogue
     # (seeded), so nearly every gathered cache row is distinct and crosses HBM.
     scoring = None
+    cs_bytes, cs_flops = work["cand_score"](True)
     if not args.no_extras:
+        log("timing cold and warm scoring")
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         rbuf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         sink = []
@@ -272,19 +438,21 @@ def main():
         def score_uniform():
             L.cand_score(cache, lp, ids_u, coff_d, out=out)
 
-        cs_bytes = algo["lime_cand_score"]["bytes"]
-
         def entry(med, mn):
-            return {"us": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
-                    "candidates_per_s": round(n_cand / (med * 1e-3), 1),
-                    "GB/s": round(cs_bytes / (med * 1e-3) / 1e9, 1),
-                    "frac_of_hbm_peak": round(cs_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            e = {"us": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                 "candidates_per_s": round(n_cand / (med * 1e-3), 1)}
+            e.update(against_roof(cs_bytes, cs_flops, med * 1e-3, peak_tf))
+            return e
 
         scoring = {"zipf_cold": entry(*cold_calls(score)),
                    "uniform_cold": entry(*cold_calls(score_uniform)),
                    "uniform_warm": entry(*time_calls(score_uniform, args.steps)),
                    "zipf_warm": entry(call_ms["lime_cand_score"], call_min_ms["lime_cand_score"])}
         del scratch, rbuf, sink
+        if "cand_score" in rooflines:
+            rooflines["cand_score"]["cold_zipf"] = {k: scoring["zipf_cold"][k] for k in ("us", "frac", "GB/s")}
+            rooflines["cand_score"]["cold_uniform"] = {k: scoring["uniform_cold"][k]
+                                                       for k in ("us", "frac", "GB/s")}
 
     # ---- the pages' other variants (not part of the step): the user-side
     # LIME-MHA and LIME-XOR+Window; int8 cache build and scoring, uncached
@@ -292,6 +460,7 @@ def main():
     # calls above
     extras = {}
     if not args.no_extras:
+        log("timing the variants")
         codes = torch.empty((w.n_items, w.heads, w.ell), dtype=torch.int8, device="cuda")
         qsc = torch.empty((w.n_items, w.heads), dtype=torch.float32, device="cuda")
         out2 = torch.empty_like(out)
@@ -336,6 +505,7 @@ def main():
             extras[k] = {"us": round(t_ms * 1e3, 2), "us_min": round(t_min * 1e3, 2),
                          "GB/s": round(ex_bytes[k] / (t_ms * 1e-3) / 1e9, 1),
                          "per_s": round((w.n_items if "build" in k else n_cand) / (t_ms * 1e-3), 1)}
+        del codes, qsc, out2, lp2
 
     # achievable HBM bandwidth next to the 8 TB/s peak: a plain 1 GiB
     # device-to-device copy (read + write bytes counted), timed like the calls
@@ -355,7 +525,7 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
-    if a["bound"] == "hbm" and copy_gbs:
+    if roofline["bound"] == "hbm" and copy_gbs:
         roofline["achievable_copy_GBs"] = round(copy_gbs, 1)
         roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
@@ -380,7 +550,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded; shapes and id law of the workload)",
+        "data": "synthetic (seeded; shapes, length law and id law of the workload)",
         "config": {"workload": f"{w.name}: B={w.B} users, N={w.N}, ell={w.ell}, d={w.d}, "
                                f"heads={w.heads}, layers={w.layers}, catalogue={w.n_items}, "
                                f"M={w.M}/user, zipf={w.zipf}, phi={w.phi}",
@@ -388,61 +558,23 @@ def main():
                    "candidates": n_cand},
         "users_per_s": w.B / (ms_step * 1e-3),
         "items_per_s": w.n_items / (ms_step * 1e-3),
+        "online": online,
         "call_ms": {k: round(v, 4) for k, v in call_ms.items()},
         "user_side": user_side,
-        "per_call": per_call,
+        "roofline": roofline,
+        "rooflines": rooflines,
+        "step_kernel_ms_traced": round(step_kernel_ms, 4),
         "scoring": scoring,
         "variants": extras,
         "xor_fwd_plan": plan,
         "launch": "eager" if args.no_graph else "one hip-graph replay of the K captured steps",
-        "roofline": roofline,
         "hbm_copy_GBs": round(copy_gbs, 1) if copy_gbs else None,
     }
 
     if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(w, ui, ci, ids, coff, scale, args.cpu_seconds)
     print(json.dumps(res), flush=True)
-
-
-def xor_fwd_flops(w, lens):
-    """Algorithmic flops of one lime_xor_fwd call without hist_out: every
-    layer projects all rows (QKV 6d^2, W_o 2d^2, gated MLP 6 d d_ff per row)
-    and runs both XOR branches (8 ell N d per user); the last layer needs
-    only the K,V projection of history rows (4d^2) and the link-side branch
-    (4 ell N d)."""
-    d, f, ell, L = w.d, w.dff, w.ell, w.layers
-    N = float(np.sum(lens))
-    rows_link = w.B * ell
-    full = (rows_link + N) * (8 * d * d + 6 * d * f) + 8 * ell * N * d
-    last = rows_link * (8 * d * d + 6 * d * f) + N * 4 * d * d + 4 * ell * N * d
-    return (L - 1) * full + last
-
-
-def traffic_from_profiles(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE in
-    KiB per dispatch, scaled by the copy-kernel factors recorded there), or
-    None if there is none or the kernel sources changed since it was taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    try:
-        h = hashlib.sha256()
-        csrc = os.path.join(ROOT, "decoupled_linear_link_amd", "csrc")
-        for f in sorted(os.listdir(csrc)):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-        if kv.get("sources_sha256") != h.hexdigest():
-            return None
-        return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])
-                   + float(kv["write_kib"]) * 1024 * float(kv["write_factor"]))
-    except (KeyError, ValueError, OSError):
-        return None
 
 
 def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
@@ -471,7 +603,7 @@ def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
     off = ui["hist_offsets"]
     frac = 1.0 / 3.0
     # users: a prefix of users
-    nu = max(1, min(w.B, 8))
+    nu = 1
     t0 = time.perf_counter()
     O.xor_fwd(ui["links_ctx"], ui["hist"], off, ui["weights"], w.heads, scale, w.phi, users=range(nu))
     t_user = (time.perf_counter() - t0) / nu
@@ -504,8 +636,8 @@ def cpu_baseline(w, ui, ci, ids, coff, scale, budget_s):
     t_step = t_user * w.B + t_item * w.n_items + t_cand * n_cand
     return {"value": n_cand / t_step, "unit": "candidates/s", "cores": int(cores), "kind": "oracle",
             "cpu_model": cpu_model, "blas": blas,
-            "sample": f"{nu} users, {ni} catalogue items, {int(coff[nc_users])} candidates; "
-                      "per-part times scaled to one whole step",
+            "sample": f"{nu} of {w.B} users, {ni} of {w.n_items} catalogue items, {int(coff[nc_users])} of "
+                      f"{n_cand} candidates; per-part times scaled to one whole step",
             "users_per_s": 1.0 / t_user, "items_per_s": 1.0 / t_item,
             "candidates_per_s": 1.0 / t_cand}
 

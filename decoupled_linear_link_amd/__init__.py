@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "xor_fwd_plan", "qk_cache_build",
     "qk_cache_build_i8", "cand_score", "cand_score_i8", "cand_score_uncached", "PHI", "DTYPE", "VARIANT", "EXPORTED",
+    "trace_begin", "trace_end",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +46,8 @@ STATUS = {0: "LIME_OK", 1: "LIME_ERR_INVALID_ARG", 2: "LIME_ERR_UNSUPPORTED",
 EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_variant", "lime_xor_fwd_score", "lime_xor_fwd_workspace_size",
             "lime_xor_fwd_plan",
             "lime_qk_cache_build", "lime_qk_cache_build_i8", "lime_cand_score", "lime_cand_score_i8",
-            "lime_cand_score_uncached", "lime_status_string", "lime_last_error")
+            "lime_cand_score_uncached", "lime_status_string", "lime_last_error",
+            "lime_trace_begin", "lime_trace_end")
 
 
 class LayerWeights(ctypes.Structure):
@@ -87,6 +89,13 @@ lib.lime_cand_score_uncached.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32,
 lib.lime_cand_score.restype = ctypes.c_int
 lib.lime_cand_score.argtypes = [ctypes.c_int, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp,
                                 _i64, _vp, _vp, _vp]
+
+
+lib.lime_trace_begin.restype = ctypes.c_int
+lib.lime_trace_begin.argtypes = [_i32]
+lib.lime_trace_end.restype = ctypes.c_int32
+lib.lime_trace_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), _i32,
+                               ctypes.POINTER(_i32)]
 
 
 class LimeError(RuntimeError):
@@ -131,6 +140,65 @@ def _want(t, name, dtype=None, dims=None):
         raise ValueError(f"{name} must have {dims} dims, got {t.dim()}")
 
 
+def _want_shape(t, name, dtype, shape, device):
+    """A tensor the kernels index with sizes taken from the other arguments:
+    a contiguous device tensor of exactly this dtype and shape, on the same
+    device (the C ABI sees only its pointer)."""
+    _want(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+
+
+def _want_workspace(ws, need, device):
+    _want(ws, "workspace", torch.uint8, 1)
+    if ws.device != device:
+        raise ValueError(f"workspace is on {ws.device}, the other arguments on {device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, the call needs {need}")
+
+
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _out_rows(out, M, d, dtype, device):
+    """The [M, d] score rows: allocated here, or checked when the caller
+    passes them (the kernels write M*d elements)."""
+    if out is None:
+        return torch.empty((M, d), dtype=dtype, device=device)
+    _want_shape(out, "out", dtype, (M, d), device)
+    return out
+
+
+def _want_bad(bad, device):
+    if bad is not None:
+        _want_shape(bad, "bad_id_count", torch.int32, tuple(bad.shape), device)
+        if bad.numel() < 1:
+            raise ValueError("bad_id_count must hold at least one int32")
+
+
+def trace_begin(capacity: int = 4096):
+    """Open a kernel trace (lime_trace_begin): every launch the library
+    makes until trace_end() records its own start and end on the GPU."""
+    _check(lib.lime_trace_begin(int(capacity)), "lime_trace_begin")
+
+
+def trace_end(capacity: int = 4096):
+    """Close the trace: [(kernel name, milliseconds)] in launch order, and
+    the number of launches past the capacity."""
+    names = (ctypes.c_char_p * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    dropped = _i32(0)
+    n = lib.lime_trace_end(names, ms, capacity, ctypes.byref(dropped))
+    if n < 0:
+        raise RuntimeError(f"lime_trace_end: {lib.lime_last_error().decode()}")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, capacity))], int(dropped.value)
+
+
 def xor_fwd_workspace_size(dtype, B, ell, d, heads, d_ff, total_N, max_N) -> int:
     return int(lib.lime_xor_fwd_workspace_size(DTYPE[dtype], B, ell, d, heads, d_ff, total_N, max_N))
 
@@ -159,22 +227,38 @@ def _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale, max_N, 
     if max_N is None:
         lens = hist_offsets.diff()
         max_N = int(lens.max().item()) if B > 0 else 0
+    dev = links_ctx.device
+    for t, name in ((hist, "hist"), (hist_offsets, "hist_offsets")):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, links_ctx on {dev}")
     layers = len(weights)
-    d_ff = weights[0]["w_gate"].shape[0] if layers else d
-    arr = (LayerWeights * max(1, layers))()
+    if layers < 1:
+        raise ValueError("weights must hold at least one layer")
+    _want(weights[0]["w_gate"], "weights[0].w_gate", dt, 2)
+    d_ff = weights[0]["w_gate"].shape[0]
+    # the kernels read every weight with the sizes d and d_ff: each must have
+    # exactly its [out, in] shape
+    shapes = {"w_qkv": (3 * d, d), "w_o": (d, d), "w_gate": (d_ff, d), "w_up": (d_ff, d), "w_down": (d, d_ff)}
+    arr = (LayerWeights * layers)()
     for i, lw in enumerate(weights):
-        for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
-            _want(lw[k], f"weights[{i}].{k}", dt, 2)
+        for k, shp in shapes.items():
+            _want_shape(lw[k], f"weights[{i}].{k}", dt, shp, dev)
         arr[i] = LayerWeights(*(lw[k].data_ptr() for k in ("w_qkv", "w_o", "w_gate", "w_up", "w_down")))
     if scale is None:
         scale = (d // heads) ** -0.5
     if links_pers is None:
         links_pers = torch.empty_like(links_ctx)
+    else:
+        _want_shape(links_pers, "links_pers", dt, (B, ell, d), dev)
     if want_hist and hist_out is None:
         hist_out = torch.empty_like(hist)
+    elif hist_out is not None:
+        _want_shape(hist_out, "hist_out", dt, (total_N, d), dev)
     need = xor_fwd_workspace_size(dt, B, ell, d, heads, d_ff, total_N, max_N)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=links_ctx.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _want_workspace(workspace, need, dev)
     args = (DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
             _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
             _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel())
@@ -222,11 +306,10 @@ def xor_fwd_score(links_ctx, hist, hist_offsets, weights, heads: int, cache, can
     B, ell2, d = links_ctx.shape
     if ell2 != ell or H != heads or cand_offsets.shape[0] != B + 1:
         raise ValueError("shape mismatch between cache, links_ctx, heads and cand_offsets")
+    _same_device(links_ctx.device, cache=cache, cand_ids=cand_ids, cand_offsets=cand_offsets)
     M = cand_ids.shape[0]
-    if out is None:
-        out = torch.empty((M, d), dtype=cache.dtype, device=cache.device)
-    if bad_id_count is not None:
-        _want(bad_id_count, "bad_id_count", torch.int32)
+    out = _out_rows(out, M, d, cache.dtype, links_ctx.device)
+    _want_bad(bad_id_count, links_ctx.device)
     _check(lib.lime_xor_fwd_score(*args, _ptr(cache), n_items, _ptr(cand_ids), _ptr(cand_offsets), M,
                                   _ptr(out), _ptr(bad_id_count), _stream(stream)), "lime_xor_fwd_score")
     return links_pers, hist_out, out
@@ -242,10 +325,13 @@ def qk_cache_build(items, link_keys, phi: str = "silu_mean", scale: float | None
     H, ell, d2 = link_keys.shape
     if d2 != d:
         raise ValueError("items and link_keys disagree on d")
+    _same_device(items.device, link_keys=link_keys)
     if scale is None:
         scale = (d // H) ** -0.5 if d % H == 0 else d ** -0.5
     if cache is None:
         cache = torch.empty((n, H, ell), dtype=items.dtype, device=items.device)
+    else:
+        _want_shape(cache, "cache", items.dtype, (n, H, ell), items.device)
     _check(lib.lime_qk_cache_build(_dtype(items), PHI[phi], scale, n, d, H, ell, _ptr(items),
                                    _ptr(link_keys), _ptr(cache), _stream(stream)),
            "lime_qk_cache_build")
@@ -264,11 +350,10 @@ def cand_score(cache, links_pers, cand_ids, cand_offsets, out=None, bad_id_count
     B, ell2, d = links_pers.shape
     if ell2 != ell or cand_offsets.shape[0] != B + 1:
         raise ValueError("shape mismatch between cache, links_pers and cand_offsets")
+    _same_device(cache.device, links_pers=links_pers, cand_ids=cand_ids, cand_offsets=cand_offsets)
     M = cand_ids.shape[0]
-    if out is None:
-        out = torch.empty((M, d), dtype=cache.dtype, device=cache.device)
-    if bad_id_count is not None:
-        _want(bad_id_count, "bad_id_count", torch.int32)
+    out = _out_rows(out, M, d, cache.dtype, cache.device)
+    _want_bad(bad_id_count, cache.device)
     _check(lib.lime_cand_score(_dtype(cache), B, ell, d, H, _ptr(cache), n_items, _ptr(links_pers),
                                _ptr(cand_ids), _ptr(cand_offsets), M, _ptr(out),
                                _ptr(bad_id_count), _stream(stream)), "lime_cand_score")
@@ -287,10 +372,15 @@ def qk_cache_build_i8(items, link_keys, phi: str = "silu_mean", scale: float | N
         raise ValueError("items and link_keys disagree on d")
     if scale is None:
         scale = (d // H) ** -0.5 if d % H == 0 else d ** -0.5
+    _same_device(items.device, link_keys=link_keys)
     if codes is None:
         codes = torch.empty((n, H, ell), dtype=torch.int8, device=items.device)
+    else:
+        _want_shape(codes, "codes", torch.int8, (n, H, ell), items.device)
     if qscale is None:
         qscale = torch.empty((n, H), dtype=torch.float32, device=items.device)
+    else:
+        _want_shape(qscale, "qscale", torch.float32, (n, H), items.device)
     _check(lib.lime_qk_cache_build_i8(_dtype(items), PHI[phi], scale, n, d, H, ell, _ptr(items),
                                       _ptr(link_keys), _ptr(codes), _ptr(qscale), _stream(stream)),
            "lime_qk_cache_build_i8")
@@ -309,11 +399,10 @@ def cand_score_i8(codes, qscale, links_pers, cand_ids, cand_offsets, out=None, b
     B, ell2, d = links_pers.shape
     if ell2 != ell or cand_offsets.shape[0] != B + 1 or tuple(qscale.shape) != (n_items, H):
         raise ValueError("shape mismatch between codes, qscale, links_pers and cand_offsets")
+    _same_device(codes.device, qscale=qscale, links_pers=links_pers, cand_ids=cand_ids, cand_offsets=cand_offsets)
     M = cand_ids.shape[0]
-    if out is None:
-        out = torch.empty((M, d), dtype=links_pers.dtype, device=links_pers.device)
-    if bad_id_count is not None:
-        _want(bad_id_count, "bad_id_count", torch.int32)
+    out = _out_rows(out, M, d, links_pers.dtype, links_pers.device)
+    _want_bad(bad_id_count, links_pers.device)
     _check(lib.lime_cand_score_i8(_dtype(links_pers), B, ell, d, H, _ptr(codes), _ptr(qscale), n_items,
                                   _ptr(links_pers), _ptr(cand_ids), _ptr(cand_offsets), M, _ptr(out),
                                   _ptr(bad_id_count), _stream(stream)), "lime_cand_score_i8")
@@ -333,13 +422,13 @@ def cand_score_uncached(items, link_keys, links_pers, cand_ids, cand_offsets, ph
     B, ell2, d3 = links_pers.shape
     if d2 != d or d3 != d or ell2 != ell or cand_offsets.shape[0] != B + 1:
         raise ValueError("shape mismatch between items, link_keys, links_pers and cand_offsets")
+    _same_device(items.device, link_keys=link_keys, links_pers=links_pers, cand_ids=cand_ids,
+                 cand_offsets=cand_offsets)
     if scale is None:
         scale = (d // H) ** -0.5
     M = cand_ids.shape[0]
-    if out is None:
-        out = torch.empty((M, d), dtype=items.dtype, device=items.device)
-    if bad_id_count is not None:
-        _want(bad_id_count, "bad_id_count", torch.int32)
+    out = _out_rows(out, M, d, items.dtype, items.device)
+    _want_bad(bad_id_count, items.device)
     _check(lib.lime_cand_score_uncached(_dtype(items), PHI[phi], scale, B, ell, d, H, _ptr(items), n_items,
                                         _ptr(link_keys), _ptr(links_pers), _ptr(cand_ids), _ptr(cand_offsets),
                                         M, _ptr(out), _ptr(bad_id_count), _stream(stream)),

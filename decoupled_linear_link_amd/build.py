@@ -21,7 +21,6 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "liblime.so")
 SOURCES = ["lime_api.hip"]
-HEADERS = ["common.h", "generic_kernels.h", "mfma_kernels.h"]
 ARCH = "gfx950"
 
 

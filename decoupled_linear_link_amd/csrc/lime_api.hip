@@ -2,11 +2,15 @@
 // kernel launches.  Every check that the host can make happens before the
 // first launch, so a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "lime.h"
 #include "common.h"
@@ -37,6 +41,46 @@ lime_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Kernel timing for measurement tools (lime_trace_begin / lime_trace_end).
+// While a trace is open, each launch takes a pair of events that the
+// runtime stamps with the dispatch's own start and end times
+// (hipExtLaunchKernelGGL); otherwise launches are plain.
+struct Trace {
+  std::mutex m;
+  std::atomic<bool> on{false};
+  std::vector<hipEvent_t> ev;  // start, end per slot
+  std::vector<const char*> name;
+  int n = 0, dropped = 0;
+};
+Trace g_trace;
+
+// the event pair of the next launch, or nulls when no trace is open or it is
+// full
+void trace_slot(const char* name, hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
+  if (!g_trace.on.load(std::memory_order_acquire)) return;
+  std::lock_guard<std::mutex> lk(g_trace.m);
+  if (!g_trace.on.load(std::memory_order_relaxed)) return;
+  if (static_cast<size_t>(g_trace.n) >= g_trace.name.size()) {
+    ++g_trace.dropped;
+    return;
+  }
+  *e0 = g_trace.ev[2 * g_trace.n];
+  *e1 = g_trace.ev[2 * g_trace.n + 1];
+  g_trace.name[g_trace.n++] = name;
+}
+
+// a kernel launch under a trace name (the kernel's name in the source)
+#define LIME_LAUNCH(NAME, KERNEL, GRID, BLOCK, LDS, STREAM, ...)                          \
+  do {                                                                                   \
+    hipEvent_t e0_, e1_;                                                                 \
+    trace_slot(NAME, &e0_, &e1_);                                                        \
+    if (e0_ != nullptr)                                                                  \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, e0_, e1_, 0, __VA_ARGS__); \
+    else                                                                                 \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                 \
+  } while (0)
 
 #define LIME_CHECK_LAUNCH(what)                                                          \
   do {                                                                                   \
@@ -83,7 +127,7 @@ lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, f
   const int64_t ntiles = (n_items + C::TI - 1) / C::TI;
   int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
   if (grid > ntiles) grid = ntiles;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, st,
+  LIME_LAUNCH(I8 ? "qk_cache_i8" : "qk_cache", k, dim3(static_cast<unsigned>(grid)), dim3(C::NT), 0, st,
                      static_cast<const bf16_t*>(items), static_cast<const bf16_t*>(keys), cache, qscale,
                      n_items, scale, phi, ntiles);
   LIME_CHECK_LAUNCH("qk cache build (mfma)");
@@ -119,7 +163,7 @@ lime_status_t launch_cs_mfma(const void* cache, const float* qscale, int64_t n_i
   if (tpw < 1) tpw = 1;
   const int64_t waves = (ntiles + tpw - 1) / tpw * NG;
   const int64_t grid = (waves + 3) / 4;
-  hipLaunchKernelGGL((mfma::cand_score<ELL, H, I8>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+  LIME_LAUNCH(I8 ? "cand_score_i8" : "cand_score", (mfma::cand_score<ELL, H, I8>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
                      cache, qscale, n_items, static_cast<const bf16_t*>(lp), ids, off, B, total_M,
                      static_cast<bf16_t*>(out), bad, tpw);
   LIME_CHECK_LAUNCH("candidate scoring (mfma)");
@@ -261,7 +305,7 @@ void launch_resident(int B, size_t lds, hipStream_t st, const void* links_ctx, c
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                160 * 1024) == hipSuccess;
   (void)attr;
-  hipLaunchKernelGGL(k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
+  LIME_LAUNCH(SC ? "xor_fwd_resident_score" : NKW ? "xor_fwd_resident_window" : "xor_fwd_resident", k, dim3(B), dim3(mfma::ResCfg<ELL, D>::NT), lds, st, static_cast<const bf16_t*>(links_ctx),
                      static_cast<const bf16_t*>(hist), off, total_N, RT, layers, ls, scale,
                      static_cast<int>(phi), static_cast<bf16_t*>(links_pers),
                      static_cast<bf16_t*>(hist_out), va.links_only ? 1 : 0, va.half, va.score);
@@ -333,7 +377,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
   // the splits of every layer's attention
-  hipLaunchKernelGGL(mfma::split_plan, dim3(1), dim3(mfma::SPLIT_PLAN_NT), 0, st, off, B, total_N, P.chunk,
+  LIME_LAUNCH("split_plan", mfma::split_plan, dim3(1), dim3(mfma::SPLIT_PLAN_NT), 0, st, off, B, total_N, P.chunk,
                      soff, suser, static_cast<int>(P.G));
   LIME_CHECK_LAUNCH("split plan");
   // Q|K and Y are head-planar in the workspace (see the kernels' Lay)
@@ -369,7 +413,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
         int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
         const int64_t need = (nblk + mfma::QkvLds<D>::NW - 1) / mfma::QkvLds<D>::NW;
         if (grid > need) grid = need;
-        hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
+        LIME_LAUNCH("qkv_proj_lds", k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::QkvLds<D>::NW), lds, st, Xin, R,
                            P.R_pad, nproj, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
       } else {
         // weights streamed through LDS, persistent workgroups
@@ -383,7 +427,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
         const int64_t ntiles = (P.R_pad + 255) / 256;
         int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
         if (grid > ntiles) grid = ntiles;
-        hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
+        LIME_LAUNCH("qkv_proj_stream", k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,
                            P.R_pad, static_cast<const bf16_t*>(w[l].w_qkv), QK, Vp, qs, q_rows);
       }
       LIME_CHECK_LAUNCH("qkv projection (mfma)");
@@ -404,22 +448,22 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                                                        static_cast<int>(FC::lds_bytes)) == hipSuccess;
           (void)attr;
           const dim3 grid_f(static_cast<unsigned>((P.G + FC::SPW - 1) / FC::SPW));
-          hipLaunchKernelGGL(k, grid_f, dim3(64 * FC::NW), FC::lds_bytes, st, Xin,
+          LIME_LAUNCH("xor_attn_qkv", k, grid_f, dim3(64 * FC::NW), FC::lds_bytes, st, Xin,
                              static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser, B,
                              static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, qs);
         }
       } else if (va.half > 0 && full)
-        hipLaunchKernelGGL((mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
+        LIME_LAUNCH("xor_attn_window", (mfma::xor_attn<ELL, H, mfma::win_nkw(ELL), HBW>), grid_w, dim3(64 * HBW), 0, st, QK,
                            Vp, Y, part, off, soff, suser, B, P.chunk, total_N, static_cast<int>(phi), 1, va.half,
                            P.R_pad);
       else
-        hipLaunchKernelGGL((mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, soff, suser,
+        LIME_LAUNCH("xor_attn", (mfma::xor_attn<ELL, H>), grid, dim3(64 * H), 0, st, QK, Vp, Y, part, off, soff, suser,
                            B, P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, 0, P.R_pad);
     }
     LIME_CHECK_LAUNCH("xor attention (mfma)");
     {
       const int64_t n = static_cast<int64_t>(B) * H * ELL * 4 * mfma::CSG;
-      hipLaunchKernelGGL((mfma::xor_combine<ELL>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+      LIME_LAUNCH("xor_combine", (mfma::xor_combine<ELL>), dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                          part, soff, Y, B, H, R * 32);
       LIME_CHECK_LAUNCH("xor combine");
     }
@@ -435,7 +479,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       const int64_t need = (pw + mfma::PostLds<D, D>::NW - 1) / mfma::PostLds<D, D>::NW;
       if (grid > need) grid = need;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::PostLds<D, D>::NW), lds, st, Y, R,
+      LIME_LAUNCH("post_block_lds", k, dim3(static_cast<unsigned>(grid)), dim3(64 * mfma::PostLds<D, D>::NW), lds, st, Y, R,
                          Xin, Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
@@ -452,7 +496,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const int64_t ntiles = (rows_post + 16 * PC::NW - 1) / (16 * PC::NW);
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       if (grid > ntiles) grid = ntiles;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, static_cast<const bf16_t*>(Y), R, Xin,
+      LIME_LAUNCH("post_block_stream", k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, static_cast<const bf16_t*>(Y), R, Xin,
                          Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
                          static_cast<const bf16_t*>(w[l].w_down));
@@ -507,27 +551,27 @@ lime_status_t run_xor_generic(const XorPlan& P, lime_phi_t phi, float scale, int
     const Rows Xfinal = last ? Rows{links_pers, hist_out, nlr, d} : Xws;
     const T* Wqkv = static_cast<const T*>(w[l].w_qkv);
 
-    hipLaunchKernelGGL((gemm_rows<T, true, EPI_STORE>), dim3(gx(R), gy(3 * d)), blk, 0, st, Xin,
+    LIME_LAUNCH("gen::qkv_proj", (gemm_rows<T, true, EPI_STORE>), dim3(gx(R), gy(3 * d)), blk, 0, st, Xin,
                        int64_t(0), R, d, Wqkv, nullptr, 3 * d, none, QKVr);
     LIME_CHECK_LAUNCH("qkv projection");
-    hipLaunchKernelGGL((xor_attn<T, DH>), dim3(B, H, P.S), blk, 0, st, QKV, Y, part, off, B, ell,
+    LIME_LAUNCH("gen::xor_attn", (xor_attn<T, DH>), dim3(B, H, P.S), blk, 0, st, QKV, Y, part, off, B, ell,
                        d, H, P.S, P.chunk, total_N, scale, static_cast<int>(phi), full ? 1 : 0, va.half);
     LIME_CHECK_LAUNCH("xor attention");
     {
       const int64_t n = static_cast<int64_t>(B) * H * ell * DH;
-      hipLaunchKernelGGL((xor_combine<T, DH>), dim3(static_cast<unsigned>((n + 255) / 256)), blk, 0,
+      LIME_LAUNCH("gen::xor_combine", (xor_combine<T, DH>), dim3(static_cast<unsigned>((n + 255) / 256)), blk, 0,
                          st, part, Y, B, ell, d, H, P.S, static_cast<int64_t>(d), static_cast<int64_t>(DH));
       LIME_CHECK_LAUNCH("xor combine");
     }
-    hipLaunchKernelGGL((gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
+    LIME_LAUNCH("gen::out_proj", (gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
                        Yr, int64_t(0), rows_post, d, static_cast<const T*>(w[l].w_o), nullptr, d,
                        Xin, Xws);
     LIME_CHECK_LAUNCH("output projection");
-    hipLaunchKernelGGL((gemm_rows<T, true, EPI_SWIGLU>), dim3(gx(rows_post), gy(d_ff)), blk, 0,
+    LIME_LAUNCH("gen::mlp_up", (gemm_rows<T, true, EPI_SWIGLU>), dim3(gx(rows_post), gy(d_ff)), blk, 0,
                        st, Xws, int64_t(0), rows_post, d, static_cast<const T*>(w[l].w_gate),
                        static_cast<const T*>(w[l].w_up), d_ff, none, Hr);
     LIME_CHECK_LAUNCH("gated mlp up");
-    hipLaunchKernelGGL((gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
+    LIME_LAUNCH("gen::mlp_down", (gemm_rows<T, false, EPI_RESID>), dim3(gx(rows_post), gy(d)), blk, 0, st,
                        Hr, int64_t(0), rows_post, d_ff, static_cast<const T*>(w[l].w_down),
                        nullptr, d, Xws, Xfinal);
     LIME_CHECK_LAUNCH("gated mlp down");
@@ -567,6 +611,57 @@ const char* lime_status_string(lime_status_t s) {
 }
 
 const char* lime_last_error(void) { return g_err.c_str(); }
+
+lime_status_t lime_trace_begin(int32_t capacity) {
+  if (capacity < 1) return fail(LIME_ERR_INVALID_ARG, "trace capacity must be >= 1 (got %d)", capacity);
+  std::lock_guard<std::mutex> lk(g_trace.m);
+  if (g_trace.on.load(std::memory_order_relaxed)) return fail(LIME_ERR_INVALID_ARG, "a trace is already open");
+  std::vector<hipEvent_t> ev(2 * static_cast<size_t>(capacity), nullptr);
+  for (size_t i = 0; i < ev.size(); ++i) {
+    if (hipEventCreate(&ev[i]) != hipSuccess) {
+      for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return fail(LIME_ERR_HIP, "trace: hipEventCreate failed");
+    }
+  }
+  g_trace.ev.swap(ev);
+  g_trace.name.assign(static_cast<size_t>(capacity), nullptr);
+  g_trace.n = 0;
+  g_trace.dropped = 0;
+  g_trace.on.store(true, std::memory_order_release);
+  return ok();
+}
+
+int32_t lime_trace_end(const char** names, float* ms, int32_t cap, int32_t* dropped) {
+  std::lock_guard<std::mutex> lk(g_trace.m);
+  if (!g_trace.on.load(std::memory_order_relaxed)) {
+    fail(LIME_ERR_INVALID_ARG, "no trace is open");
+    return -1;
+  }
+  g_trace.on.store(false, std::memory_order_release);
+  int32_t n = g_trace.n;
+  bool waited = true;
+  for (int32_t i = 0; i < n; ++i) {
+    float t = 0.f;
+    if (hipEventSynchronize(g_trace.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&t, g_trace.ev[2 * i], g_trace.ev[2 * i + 1]) != hipSuccess)
+      waited = false;
+    if (i < cap) {
+      if (names) names[i] = g_trace.name[i];
+      if (ms) ms[i] = t;
+    }
+  }
+  if (dropped) *dropped = g_trace.dropped;
+  for (hipEvent_t e : g_trace.ev) (void)hipEventDestroy(e);
+  g_trace.ev.clear();
+  g_trace.name.clear();
+  g_trace.n = 0;
+  if (!waited) {
+    fail(LIME_ERR_HIP, "trace: waiting for a traced launch failed");
+    return -1;
+  }
+  ok();
+  return n;
+}
 
 size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
                                    int32_t heads, int32_t d_ff, int64_t total_N, int32_t max_N) {
@@ -737,7 +832,7 @@ static lime_status_t qk_cache_impl(bool i8, lime_dtype_t dtype, lime_phi_t phi, 
   const dim3 grid(static_cast<unsigned>((n_items + 63) / 64), heads);
   const size_t lds = 64 * static_cast<size_t>(ell) * 4;
 #define LIME_QKG(T, I) \
-  hipLaunchKernelGGL((gen::qk_cache<T, I>), grid, dim3(64), lds, s, static_cast<const T*>(items), \
+  LIME_LAUNCH("gen::qk_cache", (gen::qk_cache<T, I>), grid, dim3(64), lds, s, static_cast<const T*>(items), \
                      static_cast<const T*>(link_keys), cache, qscale, n_items, d, heads, ell, scale, \
                      static_cast<int>(phi))
   if (dtype == LIME_F32) {
@@ -794,7 +889,7 @@ static lime_status_t cand_score_impl(bool i8, lime_dtype_t dtype, int32_t B, int
   const int64_t n = total_M * d;
   const dim3 grid(static_cast<unsigned>((n + 255) / 256));
 #define LIME_CSG(T, I) \
-  hipLaunchKernelGGL((gen::cand_score<T, I>), grid, dim3(256), 0, s, cache, qscale, n_items, \
+  LIME_LAUNCH("gen::cand_score", (gen::cand_score<T, I>), grid, dim3(256), 0, s, cache, qscale, n_items, \
                      static_cast<const T*>(links_pers), cand_ids, cand_offsets, B, ell, d, heads, total_M, \
                      static_cast<T*>(out), bad_id_count)
   if (dtype == LIME_F32) {
@@ -906,7 +1001,7 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
 #define LIME_UC(E, DD, HH)                                                                             \
     if (ell == E && d == DD && heads == HH) {                                                          \
       constexpr size_t lds = mfma::UcCfg<E, DD, HH>::lds_bytes;                                        \
-      hipLaunchKernelGGL((mfma::cand_score_uncached<E, DD, HH>), dim3(grid), dim3(256), lds, s,        \
+      LIME_LAUNCH("cand_score_uncached", (mfma::cand_score_uncached<E, DD, HH>), dim3(grid), dim3(256), lds, s,        \
                          static_cast<const bf16_t*>(items), n_items, static_cast<const bf16_t*>(link_keys), \
                          static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B, total_M,   \
                          static_cast<bf16_t*>(out), bad_id_count, scale, static_cast<int>(phi), tpw);  \
@@ -919,12 +1014,12 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
   const dim3 grid(static_cast<unsigned>((total_M + 63) / 64), heads);
   const size_t lds = 64 * static_cast<size_t>(ell) * 4;
   if (dtype == LIME_F32)
-    hipLaunchKernelGGL(gen::cand_score_uncached<float>, grid, dim3(64), lds, s, static_cast<const float*>(items),
+    LIME_LAUNCH("gen::cand_score_uncached", gen::cand_score_uncached<float>, grid, dim3(64), lds, s, static_cast<const float*>(items),
                        n_items, static_cast<const float*>(link_keys), static_cast<const float*>(links_pers),
                        cand_ids, cand_offsets, B, ell, d, heads, total_M, static_cast<float*>(out), bad_id_count,
                        scale, static_cast<int>(phi));
   else
-    hipLaunchKernelGGL(gen::cand_score_uncached<bf16_t>, grid, dim3(64), lds, s, static_cast<const bf16_t*>(items),
+    LIME_LAUNCH("gen::cand_score_uncached", gen::cand_score_uncached<bf16_t>, grid, dim3(64), lds, s, static_cast<const bf16_t*>(items),
                        n_items, static_cast<const bf16_t*>(link_keys), static_cast<const bf16_t*>(links_pers),
                        cand_ids, cand_offsets, B, ell, d, heads, total_M, static_cast<bf16_t*>(out), bad_id_count,
                        scale, static_cast<int>(phi));

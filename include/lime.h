@@ -276,6 +276,30 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
                                        const int64_t* cand_ids, const int64_t* cand_offsets,
                                        int64_t total_M, void* out, int32_t* bad_id_count, void* stream);
 
+/* Kernel timing for measurement tools (profiling of the calls above; the
+ * pages time their stages the same way, per stage, LIME summary page,
+ * Table 10).  lime_trace_begin opens a trace: until lime_trace_end, every
+ * kernel the library launches, from any thread and on any stream, carries a
+ * pair of HIP events that the runtime stamps with that dispatch's own start
+ * and end, for up to `capacity` launches (later ones run untraced and are
+ * counted as dropped).  No device memory is allocated; the events are
+ * created here and destroyed by lime_trace_end.  Tracing changes no result.
+ * Do not open a trace while a stream that calls the library is being
+ * captured into a graph.
+ * Errors: LIME_ERR_INVALID_ARG if capacity < 1 or a trace is already open;
+ * LIME_ERR_HIP if an event cannot be created (no trace is then open).      */
+lime_status_t lime_trace_begin(int32_t capacity);
+
+/* Closes the open trace: waits for every traced launch to finish, then
+ * writes, for the first min(count, cap) traced launches in launch order,
+ * names[i] = the kernel's name (a static string: "qk_cache", "cand_score",
+ * "xor_attn", "post_block_stream", ...) and ms[i] = its duration in
+ * milliseconds (names and ms are HOST arrays of `cap` entries, either may be
+ * NULL).  *dropped (host, nullable) receives the launches past the capacity.
+ * Returns the number of traced launches, or -1 if no trace is open or a wait
+ * failed (lime_last_error tells which).                                    */
+int32_t lime_trace_end(const char** names, float* ms, int32_t cap, int32_t* dropped);
+
 /* Static string naming a status code. */
 const char* lime_status_string(lime_status_t status);
 

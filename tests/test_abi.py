@@ -192,3 +192,19 @@ def test_xor_fwd_score_rejects(L, kw, skw, code):
                                   s["ids"], s["coff"], s["M"], s["out"], s["bad"], None)
     assert st == code
     assert L.lib.lime_last_error().decode() != ""
+
+
+def test_binding_rejects_host_tensors(L):
+    """Host tensors never reach the C ABI (their pointers are not device
+    addresses)."""
+    import torch
+    bf = torch.bfloat16
+    lp = torch.zeros((2, 32, 64), dtype=bf)
+    ids = torch.zeros(4, dtype=torch.int64)
+    coff = torch.tensor([0, 2, 4], dtype=torch.int64)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.cand_score(torch.zeros((10, 2, 32), dtype=bf), lp, ids, coff)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.qk_cache_build(torch.zeros((10, 64), dtype=bf), torch.zeros((2, 32, 64), dtype=bf))
+    with pytest.raises(ValueError, match="device tensor"):
+        L.xor_fwd(lp, torch.zeros((4, 64), dtype=bf), coff, [], heads=2)

@@ -358,6 +358,71 @@ def pin_cand_brute_force(seed=8):
     return float(np.abs(a - b).max()) + abs(ba - bb)
 
 
+def _torch_bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns decoded by torch's own bfloat16 -> float64 cast."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def pin_bf16_decode():
+    """The oracle's decode of bf16 storage (the bits both sides read) against
+    torch's bfloat16 -> float64 conversion, over all 65,536 bit patterns:
+    normals, subnormals, both zeros, both infinities and every NaN.  Returns
+    the largest difference of finite values plus the number of patterns
+    whose class (NaN, infinity, sign of zero) disagrees."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a = O._f64(bits)
+    b = _torch_bf16_to_f64(bits)
+    if a.dtype != np.float64 or a.shape != b.shape:
+        return float("inf")
+    fin = np.isfinite(b)
+    err = float(np.abs(a[fin] - b[fin]).max()) if fin.any() else 0.0
+    bad = int(np.count_nonzero(np.isnan(a) != np.isnan(b)))
+    bad += int(np.count_nonzero(np.isinf(a) != np.isinf(b)))
+    inf = np.isinf(b)
+    bad += int(np.count_nonzero(np.sign(a[inf]) != np.sign(b[inf])))
+    zero = b == 0
+    bad += int(np.count_nonzero(np.signbit(a[zero]) != np.signbit(b[zero])))
+    return err + bad
+
+
+def pin_bf16_inputs_decode_through_calls(seed=21):
+    """The whole calls on bf16 storage arrays (uint16 bits, as the kernels
+    read them) against the same calls on those inputs decoded by torch: the
+    oracle must compute on exactly the values the bits stand for."""
+    rng = _rng(seed)
+    B, ell, d, H, n_items = 2, 4, 8, 2, 11
+    lens = np.array([5, 3])
+    off = np.concatenate([[0], np.cumsum(lens)])
+
+    def bits(shape, std):
+        x = (rng.standard_normal(shape) * std).astype(np.float32)
+        u = x.view(np.uint32)
+        return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+    lc, hs = bits((B, ell, d), 1.0), bits((int(off[-1]), d), 1.0)
+    W = [{k: bits(s, d ** -0.5) for k, s in (("w_qkv", (3 * d, d)), ("w_o", (d, d)), ("w_gate", (d, d)),
+                                              ("w_up", (d, d)), ("w_down", (d, d)))}]
+    T, K = bits((n_items, d), 1.0), bits((H, ell, d), 1.0)
+    ids = rng.integers(0, n_items, size=7)
+    coff = np.array([0, 4, 7])
+    dec = _torch_bf16_to_f64
+    err = 0.0
+    for phi in ("softmax", "silu_mean"):
+        lp_a, h_a = O.xor_fwd(lc, hs, off, W, H, 0.5, phi)
+        lp_b, h_b = O.xor_fwd(dec(lc), dec(hs), off, [{k: dec(v) for k, v in W[0].items()}], H, 0.5, phi)
+        c_a = O.qk_cache_build(T, K, 0.5, phi)
+        c_b = O.qk_cache_build(dec(T), dec(K), 0.5, phi)
+        err = max(err, float(np.abs(lp_a - lp_b).max()),
+                  float(np.abs(np.concatenate(h_a) - np.concatenate(h_b)).max()),
+                  float(np.abs(c_a - c_b).max()))
+    cb = bits((n_items, H, ell), 1.0)
+    lpb = bits((B, ell, d), 1.0)
+    s_a, _ = O.cand_score(cb, lpb, ids, coff)
+    s_b, _ = O.cand_score(dec(cb), dec(lpb), ids, coff)
+    return max(err, float(np.abs(s_a - s_b).max()))
+
+
 ALL_PINS = {
     "dense_equals_decoupled": (pin_dense_equals_decoupled, 1e-12),
     "stack_dense_equals_decoupled": (pin_stack_dense_equals_decoupled, 1e-11),
@@ -371,6 +436,8 @@ ALL_PINS = {
     "variant_layer_brute_force": (pin_variant_layer_brute_force, 1e-11),
     "variants_dense_equals_decoupled": (pin_variants_dense_equals_decoupled, 1e-11),
     "window_softmax_vs_sdpa": (pin_window_softmax_vs_sdpa, 1e-12),
+    "bf16_decode": (pin_bf16_decode, 0.0),
+    "bf16_inputs_decode_through_calls": (pin_bf16_inputs_decode_through_calls, 0.0),
 }
 
 
@@ -678,7 +745,21 @@ def _mutations():
     def window_one_sided(p, n, window):
         return np.arange(max(0, p - window), p)
 
+    def bf16_wrong_shift(a):
+        a = np.asarray(a)
+        if a.dtype == np.uint16:
+            return (a.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+
+    def bf16_read_as_half(a):
+        a = np.asarray(a)
+        if a.dtype == np.uint16:
+            return a.view(np.float16).astype(np.float64)
+        return a.astype(np.float64)
+
     return {
+        "bf16 decode shifted by 15 bits": ("_f64", bf16_wrong_shift),
+        "bf16 bits read as float16": ("_f64", bf16_read_as_half),
         "window includes the row itself": ("window_neighbours", window_with_self),
         "window reaches only backwards": ("window_neighbours", window_one_sided),
         "silu normaliser off by one": ("phi_weights", silu_norm_off),
