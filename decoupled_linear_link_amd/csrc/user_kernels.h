@@ -82,12 +82,23 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// The one-pass variance E[x^2] - E[x]^2 cancels float32 bits in proportion
+// to mean^2 / variance.  While mean^2 <= 64 variance its error stays below
+// about 3e-4 of the variance (E[x^2] <= 65 variance, summed in float32); a
+// row past that bound is a row whose values sit far from zero relative to
+// their spread.  If any row of the wave is past it, the whole wave (so that
+// the cross-lane sums see only active lanes) recomputes the variance from
+// centred values, which has no cancellation.
+__device__ __forceinline__ bool wave_needs_centred_var(float mu, float var) {
+  return __builtin_amdgcn_ballot_w64(mu * mu > 64.f * var) != 0;
+}
+
 // LayerNorm (no affine, eps 1e-5) of the bf16 row a lane group holds
 // (x[kb]: this lane's values, the rest in lanes ^16, ^32), straight to bf16
 // operands.  The statistics come from bf16 pair dot products (sum and sum
 // of squares, one instruction per pair each, float32 accumulation), the
-// variance as E[x^2] - E[x]^2: the inputs are bf16, whose own rounding
-// dominates that formula's float32 cancellation error.
+// variance as E[x^2] - E[x]^2, recomputed from centred values when the
+// mean dwarfs the spread (wave_needs_centred_var).
 template <int KB>
 __device__ __forceinline__ void ln_bf16(const bf16x8 (&x)[KB], int D, bf16x8 (&out)[KB]) {
   const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
@@ -103,8 +114,19 @@ __device__ __forceinline__ void ln_bf16(const bf16x8 (&x)[KB], int D, bf16x8 (&o
   const float sum = rows_sum(s[0] + s[1]), sq = rows_sum(q[0] + q[1]);
   const float inv_d = 1.f / static_cast<float>(D);
   const float mu = sum * inv_d;
-  const float var = fmaxf(sq * inv_d - mu * mu, 0.f);
-  const float rs = rsqrtf(var + 1e-5f);
+  float var = sq * inv_d - mu * mu;
+  if (wave_needs_centred_var(mu, var)) {
+    float c[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = static_cast<float>(x[kb][j]) - mu;
+        c[j & 1] = fmaf(u, u, c[j & 1]);
+      }
+    var = rows_sum(c[0] + c[1]) * inv_d;
+  }
+  const float rs = rsqrtf(fmaxf(var, 0.f) + 1e-5f);
   const float nb = -mu * rs;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -1230,7 +1252,19 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
           const float sum = group_sum<RPWV>(sm[0] + sm[1]), ssq = group_sum<RPWV>(sq[0] + sq[1]);
           constexpr float inv_d = 1.f / static_cast<float>(D);
           const float mu = sum * inv_d;
-          const float rs = rsqrtf(fmaxf(ssq * inv_d - mu * mu, 0.f) + 1e-5f);
+          float var = ssq * inv_d - mu * mu;
+          if (wave_needs_centred_var(mu, var)) {
+            float c[2] = {0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const float dv = static_cast<float>(xc[u][jj]) - mu;
+                c[u] = fmaf(dv, dv, c[u]);
+              }
+            var = group_sum<RPWV>(c[0] + c[1]) * inv_d;
+          }
+          const float rs = rsqrtf(fmaxf(var, 0.f) + 1e-5f);
           const float nb = -mu * rs;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {

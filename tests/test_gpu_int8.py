@@ -37,9 +37,10 @@ def _check_codes(codes_gpu, scale_gpu, ref_cache):
     assert np.all(diff[~near_tie] == 0), f"{int((diff[~near_tie] > 0).sum())} codes differ away from ties"
 
 
-@pytest.mark.parametrize("name", ["tiny", "ctr", "long", "lifelong"])
+@pytest.mark.parametrize("name", ["tiny", "ctr", "long", "large_m", "lifelong"])
 def test_int8_cache_build(L, name):
     w = W.workload(name)
+    print(f"int8 cache build {name}: {w.n_items} items", flush=True)
     ci = cache_inputs(name, stress=True)
     sc = W.scale_for(w)
     codes, qs = L.qk_cache_build_i8(dev(ci["items"]), dev(ci["link_keys"]), phi=w.phi, scale=sc)

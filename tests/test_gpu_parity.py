@@ -176,6 +176,48 @@ def test_xor_fwd(L, name):
     assert_close(host_f64(lp)[users], ref, w.dtype, f"L^P[{name}]")
 
 
+@pytest.mark.parametrize("case", ["streaming_d128", "streaming_d64", "resident_d64"])
+def test_xor_fwd_rows_far_from_zero_mean(L, case):
+    """Rows whose values sit far from zero relative to their spread (a
+    per-row offset of 30-100 times the spread, on the context links and the
+    history): the LayerNorm statistics must not lose the spread to
+    cancellation.  Covers the LN of the fused attention kernel and of its
+    link projection (streaming, d <= 128) and the user-resident kernel.  One
+    layer: between layers the streaming path keeps the residual stream in
+    bf16, whose rounding of rows this far from zero is not what is tested."""
+    rng = np.random.default_rng(77)
+    if case == "streaming_d128":
+        B, ell, d, H, lens, max_n = 4, 32, 128, 4, [600, 0, 1500, 77], None
+    elif case == "streaming_d64":
+        B, ell, d, H, lens, max_n = 3, 32, 64, 2, [900, 31, 2], 4096
+    else:
+        B, ell, d, H, lens, max_n = 5, 32, 64, 2, [50, 0, 13, 1, 40], None
+    off = W.offsets_from_lengths(lens)
+    spread = 0.05
+
+    def rows(n):
+        mag = rng.uniform(30, 100, size=(n, 1)) * spread
+        sign = np.where(rng.random((n, 1)) < 0.5, -1.0, 1.0)
+        return (sign * mag + spread * rng.standard_normal((n, d))).astype(np.float32)
+
+    lc = W.as_storage(rows(B * ell).reshape(B, ell, d), "bf16")
+    hs = W.as_storage(rows(int(off[-1])), "bf16")
+    ws = [{k: W.as_storage((rng.standard_normal(sh) * sh[1] ** -0.5).astype(np.float32), "bf16")
+           for k, sh in (("w_qkv", (3 * d, d)), ("w_o", (d, d)), ("w_gate", (d, d)), ("w_up", (d, d)),
+                         ("w_down", (d, d)))}]
+    scale = (d // H) ** -0.5
+    n_launch, plan = L.xor_fwd_plan(torch.bfloat16, B, ell, d, H, 1, d, int(off[-1]),
+                                    max_n or int(max(lens)))
+    assert (n_launch == 1) == (case == "resident_d64"), plan
+    for phi in ("softmax", "silu_mean"):
+        lp, ho = L.xor_fwd(dev(lc), dev(hs), dev(off), dev_weights(ws), heads=H, phi=phi, scale=scale,
+                           max_N=max_n, want_hist=True)
+        torch.cuda.synchronize()
+        ref, href = O.xor_fwd(lc, hs, off, ws, H, scale, phi)
+        assert_close(host_f64(lp), ref, "bf16", f"L^P far-from-zero rows {case} {phi}")
+        assert_close(host_f64(ho), np.concatenate(href), "bf16", f"hist_out far-from-zero rows {case} {phi}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "ctr"])
 @pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
 def test_xor_fwd_both_phis_with_history_out(L, name, phi):

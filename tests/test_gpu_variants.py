@@ -27,13 +27,16 @@ def L():
 
 def _users(name, variant, off):
     """Users the oracle checks: all of them for the small workloads; for the
-    large ones the longest and one other (LIME-MHA), or the shortest
-    (LIME-XOR+Window, whose oracle walks history rows one by one)."""
+    large ones the longest and one other (LIME-MHA), or, for LIME-XOR+Window
+    (whose oracle walks history rows one by one), the shortest and a second
+    user: the last one in the packed history at long (equal lengths) and the
+    longest at lifelong."""
     lens = np.diff(off)
     if name in ("tiny", "ctr"):
         return list(range(len(lens)))
     if variant == "xor_window":
-        return [int(np.argmin(lens))]
+        second = len(lens) - 1 if name == "long" else int(np.argmax(lens))
+        return sorted({int(np.argmin(lens)), second})
     return sorted({int(np.argmax(lens)), int(np.random.default_rng(1).integers(0, len(lens)))})
 
 
