@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "LimeError", "lib", "lib_path", "xor_fwd", "xor_fwd_workspace_size", "xor_fwd_plan", "qk_cache_build",
     "qk_cache_build_i8", "cand_score", "cand_score_i8", "cand_score_uncached", "PHI", "DTYPE", "VARIANT", "EXPORTED",
-    "trace_begin", "trace_end",
+    "trace_begin", "trace_end", "xor_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,7 +47,10 @@ EXPORTED = ("lime_xor_fwd", "lime_xor_fwd_variant", "lime_xor_fwd_score", "lime_
             "lime_xor_fwd_plan",
             "lime_qk_cache_build", "lime_qk_cache_build_i8", "lime_cand_score", "lime_cand_score_i8",
             "lime_cand_score_uncached", "lime_status_string", "lime_last_error",
-            "lime_trace_begin", "lime_trace_end")
+            "lime_trace_begin", "lime_trace_end", "lime_xor_fwd_noalloc")
+
+# bytes of the library's scratch array (LIME_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LayerWeights(ctypes.Structure):
@@ -70,6 +73,8 @@ lib.lime_xor_fwd.restype = ctypes.c_int
 lib.lime_xor_fwd.argtypes = [ctypes.c_int, ctypes.c_int, _f32, _i32, _i32, _i32, _i32, _i32, _i32,
                              _vp, _vp, _vp, _i64, _i32, ctypes.POINTER(LayerWeights), _vp, _vp,
                              _vp, ctypes.c_size_t, _vp]
+lib.lime_xor_fwd_noalloc.restype = ctypes.c_int
+lib.lime_xor_fwd_noalloc.argtypes = lib.lime_xor_fwd.argtypes[:-3] + [_vp]
 lib.lime_xor_fwd_variant.restype = ctypes.c_int
 lib.lime_xor_fwd_variant.argtypes = [ctypes.c_int, _i32] + lib.lime_xor_fwd.argtypes
 lib.lime_xor_fwd_score.restype = ctypes.c_int
@@ -212,10 +217,11 @@ def xor_fwd_plan(dtype, B, ell, d, heads, layers, d_ff, total_N, max_N, with_his
 
 
 def _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale, max_N, want_hist, links_pers,
-              hist_out, workspace):
+              hist_out, workspace, with_workspace=True):
     """Checks and marshals the user-side arguments: (argument tuple without
     the stream, links_pers, hist_out, what must stay alive until the call:
-    the layer array and the workspace)."""
+    the layer array and the workspace).  with_workspace=False leaves the
+    workspace and its size out of the tuple (lime_xor_fwd_noalloc)."""
     _want(links_ctx, "links_ctx", dims=3)
     dt = links_ctx.dtype
     _want(hist, "hist", dt, 2)
@@ -254,15 +260,17 @@ def _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale, max_N, 
         hist_out = torch.empty_like(hist)
     elif hist_out is not None:
         _want_shape(hist_out, "hist_out", dt, (total_N, d), dev)
+    args = (DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
+            _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
+            _ptr(links_pers), _ptr(hist_out))
+    if not with_workspace:
+        return args, links_pers, hist_out, (arr,)
     need = xor_fwd_workspace_size(dt, B, ell, d, heads, d_ff, total_N, max_N)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _want_workspace(workspace, need, dev)
-    args = (DTYPE[dt], PHI[phi], scale, B, ell, d, heads, layers, d_ff,
-            _ptr(links_ctx), _ptr(hist), _ptr(hist_offsets), total_N, max_N, arr,
-            _ptr(links_pers), _ptr(hist_out), _ptr(workspace), workspace.numel())
-    return args, links_pers, hist_out, (arr, workspace)
+    return args + (_ptr(workspace), workspace.numel()), links_pers, hist_out, (arr, workspace)
 
 
 def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
@@ -287,6 +295,21 @@ def xor_fwd(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu
         if window is None:
             window = max(1, ell // 2) if variant == "xor_window" else 0
         _check(lib.lime_xor_fwd_variant(VARIANT[variant], int(window), *args), "lime_xor_fwd_variant")
+    return links_pers, hist_out
+
+
+def xor_fwd_noalloc(links_ctx, hist, hist_offsets, weights, heads: int, phi: str = "silu_mean",
+                    scale: float | None = None, max_N: int | None = None, want_hist: bool = False,
+                    links_pers=None, hist_out=None, stream=None):
+    """xor_fwd (the XOR variant) through lime_xor_fwd_noalloc: the library
+    allocates nothing and uses its fixed per-GPU scratch array as the
+    workspace (calls that need more than NOALLOC_SCRATCH_BYTES of it are
+    rejected).  Pass links_pers (and hist_out) to allocate nothing here
+    either.  Returns (links_pers, hist_out or None)."""
+    args, links_pers, hist_out, keep = _xor_args(links_ctx, hist, hist_offsets, weights, heads, phi, scale,
+                                                max_N, want_hist, links_pers, hist_out, None,
+                                                with_workspace=False)
+    _check(lib.lime_xor_fwd_noalloc(*args, _stream(stream)), "lime_xor_fwd_noalloc")
     return links_pers, hist_out
 
 

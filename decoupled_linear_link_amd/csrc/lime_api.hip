@@ -595,6 +595,34 @@ lime_status_t dispatch_xor_generic(int dh, const XorPlan& P, lime_phi_t phi, flo
   return fail(LIME_ERR_UNSUPPORTED, "d_h %d", dh);
 }
 
+// The workspace of lime_xor_fwd_noalloc: a fixed device array, one copy per
+// GPU, held until the process ends.  Host code must never pass `scratch`
+// itself to a kernel or a runtime call (in host code the name is a host-side
+// stand-in, not a device address): its address on each device comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[LIME_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address, looked up on its first use
+lime_status_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LIME_ERR_HIP, "noalloc: hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LIME_ERR_UNSUPPORTED, "noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LIME_ERR_HIP, "noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LIME_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -799,6 +827,27 @@ lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_
                                    void* stream) {
   return xor_fwd_impl(variant, window, dtype, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx, hist,
                       hist_offsets, total_N, max_N, w, links_pers, hist_out, workspace, workspace_bytes, stream,
+                      nullptr, nullptr);
+}
+
+lime_status_t lime_xor_fwd_noalloc(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                   int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
+                                   const void* links_ctx, const void* hist, const int64_t* hist_offsets,
+                                   int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                                   void* links_pers, void* hist_out, void* stream) {
+  lime_status_t st = check_sizes(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  if (st != LIME_OK) return st;
+  // the size check comes before the device lookup, so an oversized call
+  // touches no GPU state
+  const size_t need = lime_xor_fwd_workspace_size(dtype, B, ell, d, heads, d_ff, total_N, max_N);
+  if (need > LIME_NOALLOC_SCRATCH_BYTES)
+    return fail(LIME_ERR_WORKSPACE, "noalloc: the call needs %zu bytes of workspace, more than the %llu of the "
+                "library's scratch array", need, static_cast<unsigned long long>(LIME_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != LIME_OK) return st;
+  return xor_fwd_impl(LIME_VARIANT_XOR, 0, dtype, phi, scale, B, ell, d, heads, layers, d_ff, links_ctx, hist,
+                      hist_offsets, total_N, max_N, w, links_pers, hist_out, ws, LIME_NOALLOC_SCRATCH_BYTES, stream,
                       nullptr, nullptr);
 }
 

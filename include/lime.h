@@ -170,6 +170,30 @@ lime_status_t lime_xor_fwd_variant(lime_variant_t variant, int32_t window, lime_
                                    void* hist_out, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Size of the scratch array lime_xor_fwd_noalloc uses as its workspace. */
+#define LIME_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* lime_xor_fwd with no workspace argument and no allocation of any kind, for
+ * callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a fixed device array inside the library of
+ * LIME_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU, held from the library's
+ * load until the process ends; its device address is looked up once per
+ * device, on the first call made with that device current.
+ * Arguments, results and errors are those of lime_xor_fwd (same kernels,
+ * bit-identical outputs), without workspace/workspace_bytes.  A call whose
+ * lime_xor_fwd_workspace_size(...) exceeds LIME_NOALLOC_SCRATCH_BYTES
+ * returns LIME_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array, and the array keeps what
+ * the last call left in it (no call depends on its contents on entry).
+ * Calls that may overlap on one GPU (different streams, or different host
+ * threads without ordering) race on it: the caller must order them.       */
+lime_status_t lime_xor_fwd_noalloc(lime_dtype_t dtype, lime_phi_t phi, float scale, int32_t B,
+                                   int32_t ell, int32_t d, int32_t heads, int32_t layers, int32_t d_ff,
+                                   const void* links_ctx, const void* hist, const int64_t* hist_offsets,
+                                   int64_t total_N, int32_t max_N, const lime_layer_weights_t* w,
+                                   void* links_pers, void* hist_out, void* stream);
+
 /* Launch plan lime_xor_fwd would use for these sizes (host only, no GPU
  * work): returns the number of kernel launches of one call (0 on invalid
  * sizes) and, if buf is not NULL, writes a one-line description (path name,
