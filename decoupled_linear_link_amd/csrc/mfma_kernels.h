@@ -65,6 +65,41 @@ __device__ __forceinline__ bf16x8 ld16(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Operands of the XOR attention's products (Q, K, V and the probabilities)
+// are float16: the same matrix-core rate as bf16 with three more mantissa
+// bits.  Their ranges are bounded (projections of LayerNorm rows, weights
+// in [0, 1] or about the size of the logits), far inside float16's.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4 mma(const f16x8& a, const f16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes of float16 held in a 16-bit buffer
+__device__ __forceinline__ f16x8 ldh16(const bf16_t* p) {
+  return *reinterpret_cast<const f16x8*>(p);
+}
+
+__device__ __forceinline__ f16x8 packh8(const float* v) {
+  f16x8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = static_cast<_Float16>(v[j]);
+  return o;
+}
+
+__device__ __forceinline__ void st8h(bf16_t* p, const float* v) {
+  *reinterpret_cast<f16x8*>(p) = packh8(v);
+}
+
+// 4 floats as float16 (8 bytes)
+__device__ __forceinline__ void st4h(bf16_t* p, const floatx4& v) {
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  f16x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = static_cast<_Float16>(v[j]);
+  *reinterpret_cast<f16x4*>(p) = o;
+}
+
 // 4 floats as bf16 (8 bytes)
 __device__ __forceinline__ void st4(bf16_t* p, const floatx4& v) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -169,7 +169,7 @@ __device__ __forceinline__ void qk_part(const bf16x8 (&hb)[2][D / 32], const bf1
       const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
       const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                           acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-      st8(QK + p * L.ps + row * L.rs + 8 * g, v);
+      st8h(QK + p * L.ps + row * L.rs + 8 * g, v);
     }
   }
 }
@@ -189,7 +189,7 @@ __device__ __forceinline__ void v_part(const bf16x8 (&hb)[2][D / 32], const bf16
       acc1 = mma(hb[1][kb], b, acc1);
     }
     const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-    st8(Vp + vp_index(row0 + 8 * g, 16 * n + r, D), v);
+    st8h(Vp + vp_index(row0 + 8 * g, 16 * n + r, D), v);
   }
 }
 
@@ -238,7 +238,7 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
     for (int rb = 0; rb < RB; ++rb) {
       const float o[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                           acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-      st8(QK + p * L.ps + (row0 + 16 * rb + r) * L.rs + 8 * g, o);
+      st8h(QK + p * L.ps + (row0 + 16 * rb + r) * L.rs + 8 * g, o);
     }
   }
 #pragma unroll 2
@@ -252,7 +252,7 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
       for (int rb = 0; rb < RB; ++rb) acc[rb] = mma(hb[rb][kb], b, acc[rb]);
     }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) st4(Vp + vp_index(row0 + 16 * rb + 4 * g, 16 * nn + r, D), acc[rb]);
+    for (int rb = 0; rb < RB; ++rb) st4h(Vp + vp_index(row0 + 16 * rb + 4 * g, 16 * nn + r, D), acc[rb]);
   }
 }
 
@@ -266,9 +266,9 @@ __device__ __forceinline__ void qkv_rows(const float (&x)[RB][D / 4], const bf16
 template <int ELL>
 struct HeadOps {
   static constexpr int MB = ELL / 16, KBL = ELL / 32;
-  bf16x8 kl[MB];       // A: K_L, rows = links (ordered as above), k = d_h
-  bf16x8 qlt[MB];      // B: Q_L^T, cols = links 16*c + r, k = d_h
-  bf16x8 vlt[2][KBL];  // A: V_L^T, rows = 8*(r/4) + 4*c2 + r%4, k = links
+  f16x8 kl[MB];       // A: K_L, rows = links (ordered as above), k = d_h
+  f16x8 qlt[MB];      // B: Q_L^T, cols = links 16*c + r, k = d_h
+  f16x8 vlt[2][KBL];  // A: V_L^T, rows = 8*(r/4) + 4*c2 + r%4, k = links
 };
 
 template <int ELL, int D>
@@ -278,21 +278,21 @@ __device__ __forceinline__ void load_head_ops(HeadOps<ELL>& o, const bf16_t* QK,
 #pragma unroll
   for (int c = 0; c < HeadOps<ELL>::MB; ++c) {
     const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-    o.kl[c] = ld16(QK + (H + h) * L.ps + (lrow + link) * L.rs + 8 * g);
-    o.qlt[c] = ld16(QK + h * L.ps + (lrow + 16 * c + r) * L.rs + 8 * g);
+    o.kl[c] = ldh16(QK + (H + h) * L.ps + (lrow + link) * L.rs + 8 * g);
+    o.qlt[c] = ldh16(QK + h * L.ps + (lrow + 16 * c + r) * L.rs + 8 * g);
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
     for (int kb = 0; kb < HeadOps<ELL>::KBL; ++kb)
-      o.vlt[c2][kb] = ld16(Vp + vp_index(lrow + kb * 32 + 8 * g, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
+      o.vlt[c2][kb] = ldh16(Vp + vp_index(lrow + kb * 32 + 8 * g, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
 }
 
 // Operands of one 32-row chunk of history rows c0 + [0, 32) for head h:
 // Q rows (E-branch B operands), K rows in the L-branch row order (A
 // operands) and two packed V column blocks (A operands of V^T P^T).
 struct ChunkOps {
-  bf16x8 qe[2], ke[2], ve[2];
+  f16x8 qe[2], ke[2], ve[2];
 };
 
 template <int D>
@@ -301,13 +301,13 @@ __device__ __forceinline__ void load_chunk(ChunkOps& c, const bf16_t* QK, const 
   constexpr int H = D / 32;
   if (with_q) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ld16(QK + h * L.ps + (hrow + c0 + 16 * rb + r) * L.rs + 8 * g);
+    for (int rb = 0; rb < 2; ++rb) c.qe[rb] = ldh16(QK + h * L.ps + (hrow + c0 + 16 * rb + r) * L.rs + 8 * g);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    c.ke[k] = ld16(QK + (H + h) * L.ps + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * L.rs + 8 * g);
-  c.ve[0] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + r, D));
-  c.ve[1] = ld16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
+    c.ke[k] = ldh16(QK + (H + h) * L.ps + (hrow + c0 + 8 * (r >> 2) + 4 * k + (r & 3)) * L.rs + 8 * g);
+  c.ve[0] = ldh16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + r, D));
+  c.ve[1] = ldh16(Vp + vp_index(hrow + c0 + 8 * g, h * 32 + 16 + r, D));
 }
 
 // LIME-XOR+Window (LIME notes, "Key design 3"): history row j also attends
@@ -326,7 +326,7 @@ struct WinArgs {
 template <int NKW>
 struct WinOps {
   static constexpr int MBW = NKW / 16, KBW = NKW / 32;
-  bf16x8 kw[MBW];      // A: window keys, rows in the link-block order
+  f16x8 kw[MBW];      // A: window keys, rows in the link-block order
 };
 template <>
 struct WinOps<0> {};
@@ -346,7 +346,7 @@ __device__ __forceinline__ void load_window(WinOps<NKW>& w, const bf16_t* QK, co
   for (int c = 0; c < WinOps<NKW>::MBW; ++c) {
     const int t = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
     const int64_t row = clamp64(hrow + key0 + t, 0, rmax - 1);
-    w.kw[c] = ld16(QK + (H + h) * L.ps + row * L.rs + 8 * g);
+    w.kw[c] = ldh16(QK + (H + h) * L.ps + row * L.rs + 8 * g);
   }
   (void)Vp;
 }
@@ -354,9 +354,9 @@ __device__ __forceinline__ void load_window(WinOps<NKW>& w, const bf16_t* QK, co
 // A operand of the window's value product for 32 keys kb (V transposed):
 // loaded where it is used, so it is not live through the scores.
 template <int D>
-__device__ __forceinline__ bf16x8 window_v(const WinArgs& wa, int64_t key0, int kb, int c2, int h, int r, int g) {
+__device__ __forceinline__ f16x8 window_v(const WinArgs& wa, int64_t key0, int kb, int c2, int h, int r, int g) {
   const int64_t row = clamp64(wa.hrow + key0 + 32 * kb + 8 * g, 0, wa.rmax - 8);
-  return ld16(wa.Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
+  return ldh16(wa.Vp + vp_index(row, h * 32 + 8 * (r >> 2) + 4 * c2 + (r & 3), D));
 }
 
 // phi in log2 units (exp2_f, silu2 and silu2_div are defined with the
@@ -446,7 +446,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
     floatx4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KBL; ++kb) {
-      const bf16x8 pb = pack8(v + 8 * kb);
+      const f16x8 pb = packh8(v + 8 * kb);
       y0 = mma(o.vlt[0][kb], pb, y0);
       y1 = mma(o.vlt[1][kb], pb, y1);
     }
@@ -454,7 +454,7 @@ __device__ __forceinline__ void e_branch(const HeadOps<ELL>& o, const ChunkOps& 
       const int64_t key0 = win_key0(c0, wa->half);
 #pragma unroll
       for (int kb = 0; kb < NKW / 32; ++kb) {
-        const bf16x8 pb = pack8(ws + 8 * kb);
+        const f16x8 pb = packh8(ws + 8 * kb);
         y0 = mma(window_v<D>(*wa, key0, kb, 0, h, r, g), pb, y0);
         y1 = mma(window_v<D>(*wa, key0, kb, 1, h, r, g), pb, y1);
       }
@@ -503,13 +503,13 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
   // V of rows outside [lo, hi) (another user's, or past the history end) is
   // zeroed, not only their weights: a non-finite value there must not reach
   // this split through 0 * inf
-  bf16x8 ve[2] = {ci.ve[0], ci.ve[1]};
+  f16x8 ve[2] = {ci.ve[0], ci.ve[1]};
   if constexpr (MASK) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (!valid[q]) {
-        ve[0][q] = static_cast<__bf16>(0.f);
-        ve[1][q] = static_cast<__bf16>(0.f);
+        ve[0][q] = static_cast<_Float16>(0.f);
+        ve[1][q] = static_cast<_Float16>(0.f);
       }
   }
 #pragma unroll
@@ -549,7 +549,7 @@ __device__ __forceinline__ void l_branch_rows(LState<ELL>& st, const HeadOps<ELL
     }
     // (V^T P^T): P's lane layout (link r, rows 8g..8g+7) is the B operand as
     // it stands, and the product's columns are the links
-    const bf16x8 pb = pack8(p);
+    const f16x8 pb = packh8(p);
     st.acc[nb][0] = mma(ve[0], pb, st.acc[nb][0]);
     st.acc[nb][1] = mma(ve[1], pb, st.acc[nb][1]);
   }
@@ -1060,7 +1060,7 @@ __device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf
 // with row stride ldw.
 template <int D>
 __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
-                                             float f, int r, int g, bf16x8 (&out)[2]) {
+                                             float f, int r, int g, f16x8 (&out)[2]) {
   constexpr int KB = D / 32;
   floatx4 acc[2][2] = {};
 #pragma unroll
@@ -1077,7 +1077,7 @@ __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], cons
   for (int rb = 0; rb < 2; ++rb) {
     const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                         acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-    out[rb] = pack8(v);
+    out[rb] = packh8(v);
   }
 }
 
@@ -1085,7 +1085,7 @@ __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], cons
 // lane r: row 8*(r/4) + 4*rb + r%4), operands swapped: lane (r, g) ends with
 // V of rows 8g .. 8g+7 for column `col_of(r)` of w_qkv's V part.
 template <int D, typename F>
-__device__ __forceinline__ bf16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw,
+__device__ __forceinline__ f16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw,
                                               F&& col_of, int r, int g) {
   constexpr int KB = D / 32;
   const bf16_t* wr = W + (2 * D + col_of(r)) * ldw + 8 * g;
@@ -1097,7 +1097,7 @@ __device__ __forceinline__ bf16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], con
     a1 = mma(hb[1][kb], bq, a1);
   }
   const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-  return pack8(v);
+  return packh8(v);
 }
 
 // The link operands of user b and head h (the HeadOps layouts) computed
@@ -1114,7 +1114,7 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
   for (int kb2 = 0; kb2 < ELL / 32; ++kb2) {
     bf16x8 hb[2][D / 32];
     ln_operands<D>(X, [&](int rb) { return l0 + kb2 * 32 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
-    bf16x8 k2[2];
+    f16x8 k2[2];
     proj_qk_regs<D>(hb, W, ldw, H + h, qs, r, g, k2);
     o.kl[2 * kb2] = k2[0];
     o.kl[2 * kb2 + 1] = k2[1];
@@ -1123,7 +1123,7 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
       o.vlt[c2][kb2] = proj_v_regs<D>(hb, W, ldw, [&](int rr) { return 32 * h + 8 * (rr >> 2) + 4 * c2 + (rr & 3); },
                                       r, g);
     ln_operands<D>(X, [&](int rb) { return l0 + kb2 * 32 + 16 * rb + r; }, g, hb);
-    bf16x8 q2[2];
+    f16x8 q2[2];
     proj_qk_regs<D>(hb, W, ldw, h, qs, r, g, q2);
     o.qlt[2 * kb2] = q2[0];
     o.qlt[2 * kb2 + 1] = q2[1];
@@ -1525,7 +1525,7 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
             const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
             const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
                                 acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-            st8(QK + ((CR * k) / 32 + pp) * (R_pad * 32) + row * 32 + 8 * g, v);  // head-planar
+            st8h(QK + ((CR * k) / 32 + pp) * (R_pad * 32) + row * 32 + 8 * g, v);  // head-planar
           }
         }
       } else {
@@ -1541,7 +1541,7 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
             acc1 = mma(hb[1][kb], b, acc1);
           }
           const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-          st8(Vp + vp_index(row0 + 8 * g, CR * (k - NQK) + 16 * nn + r, D), v);
+          st8h(Vp + vp_index(row0 + 8 * g, CR * (k - NQK) + 16 * nn + r, D), v);
         }
       }
     }

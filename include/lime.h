@@ -28,7 +28,13 @@
  *   state between calls except a per-thread error message.
  * - Element type: LIME_F32 (float) or LIME_BF16 (bfloat16 bit patterns).
  *   Arithmetic accumulates in float32; bf16 results are stored rounded to
- *   nearest-even.  Candidate ids and offsets are int64.
+ *   nearest-even.  Candidate ids and offsets are int64.  Inside the bf16
+ *   user side, the XOR attention's matrix products take their operands
+ *   (queries, keys, values and attention weights) as float16, rounded to
+ *   nearest-even: the same matrix-core rate, three more mantissa bits.
+ *   Their magnitudes stay far inside float16's range (+-65504) for any
+ *   weights whose rows have norm below about 65504 / sqrt(d); the
+ *   projections' and the gated MLP's operands stay bf16.
  * - Each call enqueues its kernels on `stream` (a hipStream_t; NULL is the
  *   default stream) and returns without waiting.  Outputs are valid once the
  *   stream has reached that point.  Calls that share output or workspace
