@@ -1551,36 +1551,65 @@ __global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_
 }
 
 // Post-attention block, weights streamed: 16 chunks of 64 weight rows per
-// 64-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
-// each: one pair), 12..15 w_down (two pairs each).  One wave owns 16 rows.
-// Chunks travel global -> LDS directly (gfx950 LDS-DMA loads, 16 bytes per
-// lane), so no registers carry them.  LDS rows are unpadded (D bf16) with
-// their 16-byte slots XOR-swizzled by swz(row): the 8 rows one fragment
-// read touches per lane group land in distinct banks.
+// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
+// each: one pair), 12..15 w_down (two pairs each).  One wave of eight owns
+// 16 rows, so each chunk in LDS feeds 128 rows.  Chunks travel global ->
+// LDS directly (LDS-DMA buffer loads, 16 bytes per lane), so no registers
+// carry them; three chunk buffers keep two chunks in flight while one is
+// computed, and the next tile's Y and X rows are fetched during the w_down
+// chunks.  LDS rows are unpadded (D bf16) with their 16-byte slots
+// XOR-swizzled by swz(row): the 8 rows one fragment read touches per lane
+// group land in distinct banks.
 template <int D>
 struct PostStreamCfg {
-  static constexpr int NW = 4, NT = 64 * NW, CR = 64;
+  static constexpr int NW = 8, NT = 64 * NW, CR = 64, NBUF = 3;
   static constexpr int SPR = D / 8;                  // 16-byte slots per row
   static constexpr int CPT = CR * SPR / NT;          // slots per thread per chunk
-  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * D * 2;
+  static constexpr size_t lds_bytes = static_cast<size_t>(NBUF) * CR * D * 2;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
+
+// A raw buffer descriptor over `elems` bf16 elements at p (gfx9-family
+// word 3: raw 32-bit accesses, no stride); loads past the extent return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const bf16_t* p, int elems) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), 0, elems * 2, 0x00020000);
+}
+
+// wait until at most n of this wave's vector memory operations are
+// outstanding (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15)
+  // at their maxima, so only vector memory is waited for
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for waves that only read the LDS buffers which their
+// own LDS-DMA loads fill: each wave has already waited (vmcnt) for its
+// loads, so the barrier needs no memory fence; a fence would make the
+// compiler wait for every LDS-DMA load in flight, including chunks loaded
+// ahead.  The compiler-only fences keep LDS reads on their side of it.
+__device__ __forceinline__ void dma_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __restrict__ Y, int64_t yR,
-                                                            Rows Xres, Rows Out, int64_t nrows,
+__global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restrict__ Y, int64_t yR,
+                                                         Rows Xres, Rows Out, int64_t nrows,
                                                          const bf16_t* __restrict__ Wo,
                                                          const bf16_t* __restrict__ Wg,
                                                          const bf16_t* __restrict__ Wu,
                                                          const bf16_t* __restrict__ Wd) {
   using C = PostStreamCfg<D>;
-  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, NCH = 16, SPR = C::SPR;
+  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, NCH = 16, SPR = C::SPR, CPT = C::CPT;
   static_assert(D == 256, "chunk schedule is written for d = 256");
-  static_assert(C::NT / SPR == 8 && C::CPT == 8, "load pattern assumes 8 rows per step");
+  static_assert(C::NT / SPR == 16 && CPT == 4, "load pattern assumes 16 rows per step");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1589,63 +1618,87 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __rest
   const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
   if (my_tiles <= 0) return;
 
-  // chunk k of the schedule -> LDS buffer: slot e = i * NT + tid of the
-  // chunk, i.e. row 8 i + tid / 32 and swizzled slot tid % 32, is fetched by
-  // this thread with one LDS-DMA load; a wave's 64 lanes fill 1 KB of LDS in
-  // a row.  Chunk bases are uniform; the per-lane part is one 32-bit offset,
-  // recomputed per chunk so that no per-chunk address stays live.
+  // Chunk step i of a chunk (CPT steps, 16 weight rows each): row 16 i +
+  // tid / 32, swizzled slot tid % 32, fetched by this thread with one
+  // LDS-DMA load; a wave's 64 lanes fill 1 KB of LDS in a row.  Each weight
+  // matrix is one buffer descriptor, so a load is a scalar row offset (a
+  // constant of the unrolled schedule) plus this lane's offset for the step
+  // into a descriptor: no per-load vector address arithmetic.
+  const __amdgpu_buffer_rsrc_t rs_o = weight_rsrc(Wo, D * D), rs_g = weight_rsrc(Wg, D * D),
+                               rs_u = weight_rsrc(Wu, D * D), rs_d = weight_rsrc(Wd, D * D);
+  const int lrow = tid >> 5;  // row within a 16-row step
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform LDS segment
   auto issue_chunk = [&](int k, bf16_t* buf) {
-    const int lrow = (tid >> 5) + opaque_zero();  // row within an 8-row group
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int slot = (tid & 31) ^ ((lrow & 3) | ((i & 3) << 2));  // = slot ^ swz(8 i + lrow)
-      const int loff = lrow * D + 8 * slot;
-      const bf16_t* base;
-      if (k < 4) base = Wo + (64 * k + 8 * i) * D;
-      else if (k < 12) base = (i < 4 ? Wg : Wu) + (32 * (k - 4) + 8 * (i & 3)) * D;
-      else base = Wd + (64 * (k - 12) + 8 * i) * D;
-      // (address-space casts: the builtin takes a global source and an LDS
-      // destination; a wave's destination is its uniform 1 KB segment)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(base + loff), (lds_void_t*)(buf + (i * C::NT + w * 64) * 8),
-                                       16, 0, 0);
+    for (int i = 0; i < CPT; ++i) {
+      // this lane's byte offset within the step (the same for every chunk)
+      const unsigned vo = static_cast<unsigned>((lrow * D + 8 * ((tid & 31) ^ swz(16 * i + lrow))) * 2);
+      lds_void_t* dst = (lds_void_t*)(buf + (i * C::NT + wu * 64) * 8);
+      // the first weight row of this step in its matrix, as a byte offset
+      if (k < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_o, dst, 16, vo, (64 * k + 16 * i) * D * 2, 0, 0);
+      else if (k < 12 && i < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_g, dst, 16, vo, (32 * (k - 4) + 16 * i) * D * 2, 0, 0);
+      else if (k < 12)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_u, dst, 16, vo, (32 * (k - 4) + 16 * (i - 2)) * D * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_d, dst, 16, vo, (64 * (k - 12) + 16 * i) * D * 2, 0, 0);
     }
-  };
-  // this wave's LDS-DMA loads complete, then the workgroup barrier
-  auto chunk_barrier = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
   };
   // the A fragment of weight row `row`, k-slice kb, of a chunk buffer; every
   // row this kernel reads as lane (r, g) has swz(row) = r
   auto frag = [&](const bf16_t* wb, int row, int kb) {
     return ld16(wb + row * D + 8 * ((4 * kb + g) ^ r));
   };
+  // the Y rows of tile `it` (fetched during the previous tile's last
+  // chunks) and its X rows (fetched at the tile's start, first used when
+  // the w_o product is complete); rows past the end read row 0, unused
+  auto tile_row = [&](int64_t it) {
+    const int64_t row = (blockIdx.x + it * gridDim.x) * 16 * NW + 16 * w + r;
+    return row < nrows ? row : int64_t(0);
+  };
+  bf16x8 yn[KB];
+  auto load_y = [&](int64_t it) {
+    const bf16_t* yr = Y + tile_row(it) * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) yn[kb] = ld16(yr + kb * yR * 32);
+  };
 
+  // chunk c of the whole sequence (tile c / 16, schedule step c % 16) sits
+  // in buffer c % 3; chunks c + 1 and c + 2 are in flight while c is used.
+  // The waits count this wave's vector memory operations, which complete in
+  // issue order: after chunk c + 1's loads come chunk c + 2's (CPT) and,
+  // where noted, row loads (KB each) and the previous tile's stores.
+  load_y(0);
   issue_chunk(0, buf0);
-  chunk_barrier();
+  issue_chunk(1, buf0 + CR * D);
+  wait_vm<CPT>();  // Y and chunk 0 have landed
+  dma_barrier();
+  int t3 = 0;  // (tile index) % 3: chunk k of this tile is in buffer (t3 + k) % 3
   for (int64_t it = 0; it < my_tiles; ++it) {
-    const int64_t tile = blockIdx.x + it * gridDim.x;
-    const int64_t row = tile * 16 * NW + 16 * w + r;
+    const int64_t row = (blockIdx.x + it * gridDim.x) * 16 * NW + 16 * w + r;
     const bool rowok = row < nrows;
-    bf16x8 yb[1][KB];
-    float x1[1][D / 4];
+    const bool next = it + 1 < my_tiles;
+    bf16x8 yb[1][KB], xr[KB];
     {
-      const bf16_t* yr = Y + row * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
-      const bf16_t* xr = rowok ? row_in<bf16_t>(Xres, row) + 8 * g : nullptr;
+      const bf16_t* xp = row_in<bf16_t>(Xres, tile_row(it)) + 8 * g;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        yb[0][kb] = rowok ? ld16(yr + kb * yR * 32) : zero8();
-        const bf16x8 x = rowok ? ld16(xr + kb * 32) : zero8();
-#pragma unroll
-        for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] = static_cast<float>(x[q]);
+        yb[0][kb] = yn[kb];
+        xr[kb] = ld16(xp + kb * 32);
       }
     }
+    float x1[1][D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) x1[0][i] = 0.f;
     bf16x8 gb[KB], mb[KB];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
-      const bool more = (k + 1 < NCH) || (it + 1 < my_tiles);
-      if (more) issue_chunk((k + 1) % NCH, buf0 + ((k + 1) & 1) * (CR * D));
-      const bf16_t* wb = buf0 + (k & 1) * (CR * D) + opaque_zero();
+      // chunk k + 2 (of this tile or the next) goes to the buffer chunk
+      // k - 1 used, which every wave has left (the barrier ending step k - 1)
+      const bool more2 = (k + 2 < NCH) || next;
+      if (more2) issue_chunk((k + 2) % NCH, buf0 + ((t3 + k + 2) % 3) * (CR * D));
+      const bf16_t* wb = buf0 + ((t3 + k) % 3) * (CR * D) + opaque_zero();
       if (k < 4 || k >= 12) {
         // x1 += (Y or M) W^T for column pairs 2k', 2k'+1
         const int kk = k < 4 ? k : k - 12;
@@ -1670,6 +1723,12 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __rest
           __builtin_amdgcn_sched_barrier(0);
         }
         if (k == 3) {
+          // the residual: x1 = X + Y W_o^T (one addition per element, the
+          // same sum as starting from X)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x1[0][8 * kb + q] += static_cast<float>(xr[kb][q]);
           float t[8 * KB];
 #pragma unroll
           for (int i = 0; i < 8 * KB; ++i) t[i] = x1[0][i];
@@ -1701,7 +1760,17 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __rest
         }
         mb[k - 4] = pack8(v);
       }
-      chunk_barrier();
+      // chunk k + 1 must have landed before the barrier:
+      //   step 0: after it come the previous tile's stores (if any), this
+      //           tile's X rows (KB) and chunk k + 2 (CPT);
+      //   step 13: after it come the next tile's Y rows (KB, loaded after
+      //           step 12's wait) and chunk k + 2;
+      //   otherwise only chunk k + 2, or nothing once no chunk follows.
+      if (!more2) wait_vm<0>();
+      else if (k == 0 || (k == 13 && next)) wait_vm<CPT + KB>();
+      else wait_vm<CPT>();
+      if (k == 12 && next) load_y(it + 1);
+      dma_barrier();
     }
     if (rowok) {
       bf16_t* orow = row_out<bf16_t>(Out, row);
@@ -1709,6 +1778,7 @@ __global__ __launch_bounds__(256, 2) void post_block_stream(const bf16_t* __rest
 #pragma unroll
         for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[0][8 * p]);
     }
+    t3 = (t3 + 16) % 3;
   }
 }
 
