@@ -215,7 +215,8 @@ __device__ __forceinline__ float quantize_i8(const float* v, int8_t* q) {
 template <int ELL, bool I8>
 __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], float scale, int phi, int64_t item,
                                                int64_t n_items, int H, int head, void* __restrict__ cache_out,
-                                               float* __restrict__ qscale, int g) {
+                                               float* __restrict__ qscale, int g, int64_t item0,
+                                               bf16_t* stage) {
   constexpr int MB = ELL / 16;
   // logits in log2 units
   const float k = scale * LOG2E;
@@ -261,6 +262,26 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
       }
       if (g == 0) qscale[item * H + head] = sc;
     }
+  } else if constexpr (ELL == 64) {
+    // One (item, head) row is 128 bytes, one memory line, of which this
+    // lane holds 32 (links 16 g .. +16).  Written as they stand, each store
+    // instruction would fill half of 16 lines; instead the 16 rows pass
+    // through the wave's LDS area `stage` (16 rows, 72 bf16 apart), and each
+    // store instruction then writes 8 whole lines: lane l stores piece l % 8
+    // of row 8 s + l / 8 of the block.  (Within one wave: LDS accesses keep
+    // their order, so no barrier is needed.)
+    const int r = static_cast<int>(item - item0);
+    st8(stage + r * 72 + g * 16, v);
+    st8(stage + r * 72 + g * 16 + 8, v + 8);
+    const int lane = 16 * g + r;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int row = 8 * s2 + (lane >> 3), piece = lane & 7;
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(stage + row * 72 + piece * 8);
+      const int64_t it = item0 + row;
+      if (it < n_items)
+        *reinterpret_cast<bf16x8*>(static_cast<bf16_t*>(cache_out) + (it * H + head) * ELL + piece * 8) = o;
+    }
   } else {
     if (item < n_items) {
       bf16_t* o = static_cast<bf16_t*>(cache_out) + (item * H + head) * ELL + g * 4 * MB;
@@ -276,7 +297,11 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H, I8>::NT)) void qk_cache(
     float* __restrict__ qscale, int64_t n_items, float scale, int phi, int64_t ntiles) {
   using C = QkCfg<ELL, D, H, I8>;
   __shared__ __attribute__((aligned(16))) char lds[C::TI * C::STRIDE];
+  // each wave's staging rows for line-sized output stores (ell = 64, bf16)
+  constexpr int STG = (ELL == 64 && !I8) ? 16 * 72 : 8;
+  __shared__ __attribute__((aligned(16))) bf16_t stage[C::NW * STG];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  bf16_t* const stage_w = stage + w * STG;
   const int g = lane >> 4, r = lane & 15;
   const int head0 = (C::WPH > 1) ? (w / C::WPH) : w * C::HPW;
   const int nb0 = (C::WPH > 1) ? (w % C::WPH) * C::NBW : 0;
@@ -335,7 +360,8 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H, I8>::NT)) void qk_cache(
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) acc[c] = mma(a[hh][c][kb], b[kb], acc[c]);
         }
-        cache_epilogue<ELL, I8>(acc, scale, phi, item, n_items, H, head0 + hh, cache_out, qscale, g);
+        cache_epilogue<ELL, I8>(acc, scale, phi, item, n_items, H, head0 + hh, cache_out, qscale, g,
+                                tile * C::TI + nb * 16, stage_w);
       }
     }
     lds_barrier();
