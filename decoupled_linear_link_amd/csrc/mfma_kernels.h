@@ -410,8 +410,18 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
   // those heads only, so large head counts do not exhaust the registers
   constexpr int HG = H < 4 ? H : 4, NG = H / HG;
   __shared__ int64_t off_s[C::MAXB + 1];
+  // Output staging (HG >= 2): a candidate's HG heads are HG * 64 contiguous
+  // bytes of its output row, whole memory lines, but each head's product
+  // leaves a lane with 16 of them, so a store per head would fill each line
+  // in pieces from separate instructions.  The tile's 16 rows are collected
+  // in the wave's LDS rows (SROW bf16 apart) and stored in memory order,
+  // 1 KB of whole lines per instruction, as many instructions as heads.
+  constexpr bool STAGE = HG >= 2;
+  constexpr int SROW = HG * 32 + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t stg_all[STAGE ? 4 * 16 * SROW : 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
+  bf16_t* const stg = stg_all + (STAGE ? (tid >> 6) * 16 * SROW : 0);
   const bool in_lds = B <= C::MAXB;
   if (in_lds)
     for (int i = tid; i <= B; i += 256) off_s[i] = off_g[i];
@@ -530,8 +540,26 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
           const float sc = qs_c[hh];
           const float v[8] = {acc0[0] * sc, acc0[1] * sc, acc0[2] * sc, acc0[3] * sc,
                               acc1[0] * sc, acc1[1] * sc, acc1[2] * sc, acc1[3] * sc};
-          st8_stream(out + i * D + (hbase + hh) * 32 + 8 * g, v);
+          if constexpr (STAGE)
+            st8(stg + r * SROW + hh * 32 + 8 * g, v);
+          else
+            st8_stream(out + i * D + (hbase + hh) * 32 + 8 * g, v);
         }
+      }
+    }
+    if constexpr (STAGE) {
+      // every valid row of the tile is staged (each belongs to one user);
+      // store them in memory order: byte f = 1024 s + 16 lane of the tile's
+      // 16 x HG * 64 bytes is row f / (HG * 64), byte f % (HG * 64) of it
+#pragma unroll
+      for (int s2 = 0; s2 < HG; ++s2) {
+        const int f = 1024 * s2 + 16 * lane;
+        const int row = f / (HG * 64), within = (f % (HG * 64)) / 2;
+        const int64_t ir = t * 16 + row;
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(stg + row * SROW + within);
+        if (ir < total_M)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, o),
+                                      reinterpret_cast<u32x4_t*>(out + ir * D + hbase * 32 + within));
       }
     }
     u = __shfl(ul, last);
