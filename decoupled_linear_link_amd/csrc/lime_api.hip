@@ -424,7 +424,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                                                      static_cast<int>(lds)) == hipSuccess;
         (void)attr;
         static const int per_cu = blocks_per_cu_lds(k, mfma::StreamCfg<D>::NT, lds);
-        const int64_t ntiles = (P.R_pad + 255) / 256;
+        const int64_t ntiles = (P.R_pad + mfma::StreamCfg<D>::TILE - 1) / mfma::StreamCfg<D>::TILE;
         int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
         if (grid > ntiles) grid = ntiles;
         LIME_LAUNCH("qkv_proj_stream", k, dim3(static_cast<unsigned>(grid)), dim3(mfma::StreamCfg<D>::NT), lds, st, Xin, R,

@@ -1412,164 +1412,9 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
 // post-attention block (4 waves, 16 rows each) loads them straight into LDS
 // into unpadded rows with swizzled 16-byte slots.
 // ---------------------------------------------------------------------------
-template <int D>
-struct StreamCfg {
-  static constexpr int NW = 8, NT = 64 * NW;
-  static constexpr int CR = 64;                       // weight rows per chunk
-  static constexpr int LDW = D + 8;                   // padded row
-  static constexpr int CPT = CR * (D / 8) / NT;       // 16-byte pieces per thread per chunk
-  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * LDW * 2;
-  static_assert((CR * (D / 8)) % NT == 0, "chunk split");
-};
-
-// chunk loader: rows [r0, r0 + CR) of a [*, K] weight matrix (K == D here)
-template <int D>
-__device__ __forceinline__ void chunk_load(bf16x8 (&reg)[StreamCfg<D>::CPT], const bf16_t* __restrict__ W,
-                                           int r0, int tid) {
-  constexpr int C8 = D / 8;
-  W += opaque_zero();  // loop-invariant loads: keep them where they are issued
-#pragma unroll
-  for (int i = 0; i < StreamCfg<D>::CPT; ++i) {
-    const int e = tid + i * StreamCfg<D>::NT;
-    reg[i] = ld16(W + static_cast<int64_t>(r0 + e / C8) * D + 8 * (e % C8));
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void chunk_store(const bf16x8 (&reg)[StreamCfg<D>::CPT], bf16_t* buf, int tid) {
-  constexpr int C8 = D / 8, LDW = StreamCfg<D>::LDW;
-#pragma unroll
-  for (int i = 0; i < StreamCfg<D>::CPT; ++i) {
-    const int e = tid + i * StreamCfg<D>::NT;
-    *reinterpret_cast<bf16x8*>(buf + (e / C8) * LDW + 8 * (e % C8)) = reg[i];
-  }
-}
-
-// LN + QKV projection, weights streamed: 12 chunks of 64 rows of w_qkv per
-// 256-row tile (chunks 0..7: Q|K column pairs, 8..11: V blocks).
-template <int D>
-__global__ __launch_bounds__(512) void qkv_proj_stream(Rows X, int64_t R, int64_t R_pad,
-                                                       const bf16_t* __restrict__ W,
-                                                       bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
-                                                       float qs, int64_t q_rows) {
-  using C = StreamCfg<D>;
-  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, LDW = C::LDW;
-  constexpr int NCH = 3 * D / CR, NQK = 2 * D / CR;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int64_t ntiles = (R_pad + 32 * NW - 1) / (32 * NW);
-  const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
-  const int64_t total = my_tiles * NCH;
-  if (total <= 0) return;
-  bf16x8 reg[C::CPT];
-  chunk_load<D>(reg, W, 0, tid);
-  chunk_store<D>(reg, buf0, tid);
-  lds_barrier();
-  bf16x8 hb[2][KB];
-  bool active = false;
-  int64_t row0 = 0;
-  for (int64_t c = 0; c < total; ++c) {
-    const int k = static_cast<int>(c % NCH);
-    if (k == 0) {
-      const int64_t tile = blockIdx.x + (c / NCH) * gridDim.x;
-      row0 = tile * 32 * NW + 32 * w;
-      active = row0 < R_pad;
-      if (active) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-          float v[8 * KB];
-          if (row < R) {
-            const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const bf16x8 x = ld16(xr + kb * 32);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
-          }
-          ln_rows<8 * KB>(v, D);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
-        }
-      }
-    }
-    const bool more = c + 1 < total;
-    if (more) chunk_load<D>(reg, W, static_cast<int>(((c + 1) % NCH) * CR), tid);
-    const bf16_t* wb = buf0 + (c & 1) * (CR * LDW) + opaque_zero();
-    // Q columns only for rows below q_rows (a multiple of 32)
-    if (active && (CR * k >= D || row0 < q_rows)) {
-      if (k < NQK) {
-        // output columns [64k, 64k + 64) of Q|K: two 32-column pairs
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          floatx4 acc[2][2] = {};
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const bf16_t* wr = wb + (32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3)) * LDW + 8 * g;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              const bf16x8 a = ld16(wr + kb * 32);
-              acc[cc][0] = mma(a, hb[0][kb], acc[cc][0]);
-              acc[cc][1] = mma(a, hb[1][kb], acc[cc][1]);
-            }
-          }
-          const float f = CR * k < D ? qs : 1.f;  // Q columns carry the logit scale
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-            const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
-                                acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
-            st8h(QK + ((CR * k) / 32 + pp) * (R_pad * 32) + row * 32 + 8 * g, v);  // head-planar
-          }
-        }
-      } else {
-        // V columns [64(k-NQK), +64): four 16-column blocks, operands swapped
-#pragma unroll
-        for (int nn = 0; nn < 4; ++nn) {
-          const bf16_t* wr = wb + (16 * nn + r) * LDW + 8 * g;
-          floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 b = ld16(wr + kb * 32);
-            acc0 = mma(hb[0][kb], b, acc0);
-            acc1 = mma(hb[1][kb], b, acc1);
-          }
-          const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-          st8h(Vp + vp_index(row0 + 8 * g, CR * (k - NQK) + 16 * nn + r, D), v);
-        }
-      }
-    }
-    if (more) chunk_store<D>(reg, buf0 + ((c + 1) & 1) * (CR * LDW), tid);
-    lds_barrier();
-  }
-}
-
-// Post-attention block, weights streamed: 16 chunks of 64 weight rows per
-// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
-// each: one pair), 12..15 w_down (two pairs each).  One wave of eight owns
-// 16 rows, so each chunk in LDS feeds 128 rows.  Chunks travel global ->
-// LDS directly (LDS-DMA buffer loads, 16 bytes per lane), so no registers
-// carry them; three chunk buffers keep two chunks in flight while one is
-// computed, and the next tile's Y and X rows are fetched during the w_down
-// chunks.  LDS rows are unpadded (D bf16) with their 16-byte slots
-// XOR-swizzled by swz(row): the 8 rows one fragment read touches per lane
-// group land in distinct banks.
-template <int D>
-struct PostStreamCfg {
-  static constexpr int NW = 8, NT = 64 * NW, CR = 64, NBUF = 3;
-  static constexpr int SPR = D / 8;                  // 16-byte slots per row
-  static constexpr int CPT = CR * SPR / NT;          // slots per thread per chunk
-  static constexpr size_t lds_bytes = static_cast<size_t>(NBUF) * CR * D * 2;
-};
-
-__device__ __forceinline__ int swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
-
+// ---------------------------------------------------------------------------
+// Weight streaming through LDS by LDS-DMA (d = 256 kernels)
+// ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // A raw buffer descriptor over `elems` bf16 elements at p (gfx9-family
@@ -1598,6 +1443,179 @@ __device__ __forceinline__ void dma_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+
+// LN + QKV projection with w_qkv streamed through LDS (d = 256: 384 KB of
+// weights).  Workgroups of 4 waves, two per CU, each wave 32 rows: a tile
+// is 128 rows and 12 chunks of 64 weight rows (0..7: Q|K column pairs,
+// 8..11: V blocks).  Chunks travel global -> LDS directly (LDS-DMA buffer
+// loads); two buffers, the next chunk in flight while one is computed, and
+// the second workgroup of the CU covers the first's tile-start loads.  LDS
+// rows are unpadded with their 16-byte slots XOR-swizzled by swz_qkv(row),
+// which keeps both fragment patterns conflict-free: the Q|K rows
+// 32 p + 8 (r / 4) + 4 c + r % 4 and the V rows 16 n + r of lanes r = 0..15.
+template <int D>
+struct StreamCfg {
+  static constexpr int NW = 4, NT = 64 * NW;
+  static constexpr int CR = 64;                       // weight rows per chunk
+  static constexpr int SPR = D / 8;                   // 16-byte slots per row
+  static constexpr int CPT = CR * SPR / NT;           // LDS-DMA slots per thread per chunk
+  static constexpr int TILE = 32 * NW;                // rows per tile
+  static constexpr size_t lds_bytes = static_cast<size_t>(2) * CR * D * 2;
+  static_assert((CR * SPR) % NT == 0, "chunk split");
+};
+
+__device__ __forceinline__ int swz_qkv(int row) { return (row & 3) | ((((row >> 3) ^ (row >> 2)) & 3) << 2); }
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void qkv_proj_stream(Rows X, int64_t R, int64_t R_pad,
+                                                          const bf16_t* __restrict__ W,
+                                                          bf16_t* __restrict__ QK, bf16_t* __restrict__ Vp,
+                                                          float qs, int64_t q_rows) {
+  using C = StreamCfg<D>;
+  constexpr int KB = D / 32, NW = C::NW, CR = C::CR, CPT = C::CPT;
+  constexpr int NCH = 3 * D / CR, NQK = 2 * D / CR;
+  static_assert(C::NT / C::SPR == 8 && CPT == 8, "load pattern assumes 8 rows per step");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int64_t ntiles = (R_pad + C::TILE - 1) / C::TILE;
+  const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int64_t total = my_tiles * NCH;
+  if (total <= 0) return;
+
+  // chunk k: weight rows [64 k, 64 k + 64) of w_qkv.  Step i of a chunk is
+  // its row 8 i + tid / 32, physical slot tid % 32, fetched by this thread
+  // with one LDS-DMA load (a wave fills 1 KB of LDS in a row): the chunk
+  // base is a scalar offset into one buffer descriptor, the lane's part a
+  // constant per step.
+  const __amdgpu_buffer_rsrc_t rsw = weight_rsrc(W, 3 * D * D);
+  const int lrow = tid >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto issue_chunk = [&](int k, bf16_t* buf) {
+    const unsigned base = static_cast<unsigned>(CR * k * D * 2);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int row = 8 * i + lrow;
+      const unsigned vo = static_cast<unsigned>((row * D + 8 * ((tid & 31) ^ swz_qkv(row))) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void_t*)(buf + (i * C::NT + wu * 64) * 8), 16, vo,
+                                               base, 0, 0);
+    }
+  };
+  // the fragment of chunk row `row` (lane's k-slice kb) in a chunk buffer
+  auto frag = [&](const bf16_t* wb, int row, int kb) {
+    return ld16(wb + row * D + 8 * ((4 * kb + g) ^ swz_qkv(row)));
+  };
+
+  issue_chunk(0, buf0);
+  wait_vm<0>();
+  dma_barrier();
+  bf16x8 hb[2][KB];
+  bool active = false;
+  int64_t row0 = 0;
+  for (int64_t c = 0; c < total; ++c) {
+    const int k = static_cast<int>(c % NCH);
+    if (k == 0) {
+      const int64_t tile = blockIdx.x + (c / NCH) * gridDim.x;
+      row0 = tile * C::TILE + 32 * w;
+      active = row0 < R_pad;
+      if (active) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+          float v[8 * KB];
+          if (row < R) {
+            const bf16_t* xr = row_in<bf16_t>(X, row) + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 x = ld16(xr + kb * 32);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[8 * kb + j] = static_cast<float>(x[j]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8 * KB; ++i) v[i] = 0.f;
+          }
+          ln_rows<8 * KB>(v, D);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) hb[rb][kb] = pack8(v + 8 * kb);
+        }
+      }
+    }
+    const bool more = c + 1 < total;
+    if (more) issue_chunk(static_cast<int>((c + 1) % NCH), buf0 + ((c + 1) & 1) * (CR * D));
+    const bf16_t* wb = buf0 + (c & 1) * (CR * D) + opaque_zero();
+    // Q columns only for rows below q_rows (a multiple of 32)
+    const bool work = active && (CR * k >= D || row0 < q_rows);
+    if (work) {
+      if (k < NQK) {
+        // output columns [64k, 64k + 64) of Q|K: two 32-column pairs
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          floatx4 acc[2][2] = {};
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int wrow = 32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const bf16x8 a = frag(wb, wrow, kb);
+              acc[cc][0] = mma(a, hb[0][kb], acc[cc][0]);
+              acc[cc][1] = mma(a, hb[1][kb], acc[cc][1]);
+            }
+          }
+          const float f = CR * k < D ? qs : 1.f;  // Q columns carry the logit scale
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const int64_t row = row0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+            const float v[8] = {acc[0][rb][0] * f, acc[0][rb][1] * f, acc[0][rb][2] * f, acc[0][rb][3] * f,
+                                acc[1][rb][0] * f, acc[1][rb][1] * f, acc[1][rb][2] * f, acc[1][rb][3] * f};
+            st8h(QK + ((CR * k) / 32 + pp) * (R_pad * 32) + row * 32 + 8 * g, v);  // head-planar
+          }
+        }
+      } else {
+        // V columns [64(k-NQK), +64): four 16-column blocks, operands swapped
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn) {
+          floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 b = frag(wb, 16 * nn + r, kb);
+            acc0 = mma(hb[0][kb], b, acc0);
+            acc1 = mma(hb[1][kb], b, acc1);
+          }
+          const float v[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+          st8h(Vp + vp_index(row0 + 8 * g, CR * (k - NQK) + 16 * nn + r, D), v);
+        }
+      }
+    }
+    // the next chunk's loads must have landed; after them this wave issued
+    // its 4 output stores of this chunk (if it had work), which may still
+    // be in flight
+    if (work) wait_vm<4>();
+    else wait_vm<0>();
+    dma_barrier();
+  }
+}
+
+// Post-attention block, weights streamed: 16 chunks of 64 weight rows per
+// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
+// each: one pair), 12..15 w_down (two pairs each).  One wave of eight owns
+// 16 rows, so each chunk in LDS feeds 128 rows.  Chunks travel global ->
+// LDS directly (LDS-DMA buffer loads, 16 bytes per lane), so no registers
+// carry them; three chunk buffers keep two chunks in flight while one is
+// computed, and the next tile's Y and X rows are fetched during the w_down
+// chunks.  LDS rows are unpadded (D bf16) with their 16-byte slots
+// XOR-swizzled by swz(row): the 8 rows one fragment read touches per lane
+// group land in distinct banks.
+template <int D>
+struct PostStreamCfg {
+  static constexpr int NW = 8, NT = 64 * NW, CR = 64, NBUF = 3;
+  static constexpr int SPR = D / 8;                  // 16-byte slots per row
+  static constexpr int CPT = CR * SPR / NT;          // slots per thread per chunk
+  static constexpr size_t lds_bytes = static_cast<size_t>(NBUF) * CR * D * 2;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 
 template <int D>
 __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restrict__ Y, int64_t yR,
