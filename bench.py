@@ -158,11 +158,21 @@ def against_roof(bytes_, flops, seconds, peak_tflops):
             "algorithmic_bytes": int(bytes_), "algorithmic_flops": float(flops)}
 
 
+# the source files that hold each kernel's device code (their launch code in
+# lime_api.hip is unchanged since the summaries were taken):
+# a counter summary stays valid while these are unchanged
+KERNEL_SOURCES = {
+    "qk_cache": ("common.h", "mfma_kernels.h"),
+    "cand_score": ("common.h", "mfma_kernels.h"),
+}
+ALL_SOURCES = ("common.h", "generic_kernels.h", "lime_api.hip", "mfma_kernels.h", "user_kernels.h")
+
+
 def traffic_from_profiles(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary
     profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE in
     KiB per dispatch, scaled by the copy-kernel factors recorded there), or
-    None if there is none or the kernel sources changed since it was taken."""
+    None if there is none or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -172,7 +182,8 @@ def traffic_from_profiles(workload, kernel):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        if kv.get("sources_sha256") != sources_sha256():
+        files = tuple(kv.get("sources", "").split()) or ALL_SOURCES
+        if kv.get("sources_sha256") != sources_sha256(files):
             return None
         return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])
                    + float(kv["write_kib"]) * 1024 * float(kv["write_factor"]))
@@ -180,10 +191,11 @@ def traffic_from_profiles(workload, kernel):
         return None
 
 
-def sources_sha256():
+def sources_sha256(files=ALL_SOURCES):
+    """sha256 over the named files of the library's sources, in name order."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decoupled_linear_link_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
