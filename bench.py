@@ -117,6 +117,18 @@ def kernel_work(w, es, total_N, n_cand):
             return (R + N) * d * es, 2.0 * d * 3 * d * R + 8.0 * ell * N * d
         return R * d * es, 2.0 * d * 2 * d * N + 2.0 * d * 3 * d * nlr + 4.0 * ell * N * d
 
+    def attn_h(full):
+        # d = 256: the projection inside the attention, from the LayerNorm rows
+        # the post block stored: read those rows, write Y_E (the links' Y
+        # comes from the split combine)
+        if full:
+            return (R + N) * d * es, 2.0 * d * 3 * d * R + 8.0 * ell * N * d
+        return R * d * es, 2.0 * d * 2 * d * N + 2.0 * d * 3 * d * nlr + 4.0 * ell * N * d
+
+    def ln_rows(full):
+        # the first layer's LayerNorm rows: read X, write them
+        return 2 * R * d * es, 0.0
+
     def post(full):
         rows = R if full else nlr
         return 3 * rows * d * es, rows * (2.0 * d * d + 6.0 * d * f)
@@ -140,6 +152,7 @@ def kernel_work(w, es, total_N, n_cand):
         return n_cand * (H * ell * es + d * es + 8), 2.0 * n_cand * ell * d
 
     return {"qkv_proj_stream": qkv, "qkv_proj_lds": qkv, "xor_attn": attn, "xor_attn_qkv": attn_fused,
+            "xor_attn_h": attn_h, "ln_rows": ln_rows,
             "xor_combine": combine, "post_block_stream": post, "post_block_lds": post,
             "xor_fwd_resident": resident, "xor_fwd_resident_score": resident_score,
             "qk_cache": cache, "cand_score": cand}
@@ -346,8 +359,8 @@ def main():
         log(f"trace dropped {dropped} launches")
     # each record: (name, ms, full) where full = the layer updates history
     # rows; layers are counted by the launch that opens each of them
-    opens = ("qkv_proj_stream", "qkv_proj_lds", "xor_attn_qkv")
-    per_layer = ("xor_attn", "xor_attn_qkv", "qkv_proj_stream", "qkv_proj_lds", "post_block_stream",
+    opens = ("qkv_proj_stream", "qkv_proj_lds", "xor_attn_qkv", "xor_attn_h")
+    per_layer = ("xor_attn", "xor_attn_qkv", "xor_attn_h", "qkv_proj_stream", "qkv_proj_lds", "post_block_stream",
                  "post_block_lds")
     per = {}
     layer = -1

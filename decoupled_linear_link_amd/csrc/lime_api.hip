@@ -195,6 +195,7 @@ struct XorPlan {
   int64_t chunk = 1;       // history rows per split
   int64_t G = 0;           // matrix-core path: split slots (an upper bound on the splits)
   size_t o_x = 0, o_qkv = 0, o_v = 0, o_y = 0, o_h = 0, o_part = 0, o_soff = 0, o_suser = 0, total = 0;
+  size_t o_ln = 0;         // matrix-core path, d = 256: LayerNorm rows of the next layer [R, d]
 };
 
 lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
@@ -277,6 +278,9 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
     p.o_part = off; off = up256(off + static_cast<size_t>(p.G) * heads * ell * mfma::PART_LD * 4);
     p.o_soff = off; off = up256(off + static_cast<size_t>(B + 1) * 4);
     p.o_suser = off; off = up256(off + static_cast<size_t>(p.G) * 4);
+    if (d == 256) {
+      p.o_ln = off;  off = up256(off + static_cast<size_t>(p.R) * d * es);
+    }
   } else {
     p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
     p.o_qkv = off;  off = up256(off + static_cast<size_t>(p.R) * 3 * d * es);
@@ -376,6 +380,12 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   int32_t* suser = reinterpret_cast<int32_t*>(ws + P.o_suser);
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
+  // d = 256, LIME-XOR: the projection runs inside the attention, from the
+  // LayerNorm rows the previous post block stored (the first layer
+  // normalises the input rows itself)
+  const bool fused_h = D == 256 && va.half == 0 && !va.links_only;
+  bf16_t* LNr = fused_h ? reinterpret_cast<bf16_t*>(ws + P.o_ln) : nullptr;
+  const Rows LNrows{LNr, LNr + nlr * D, nlr, D};
   // the splits of every layer's attention
   LIME_LAUNCH("split_plan", mfma::split_plan, dim3(1), dim3(mfma::SPLIT_PLAN_NT), 0, st, off, B, total_N, P.chunk,
                      soff, suser, static_cast<int>(P.G));
@@ -397,7 +407,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
     const int64_t q_rows = full ? P.R_pad : nlr;
     // d <= 128 without the window: the projection runs inside the attention
     // kernel
-    const bool fused = D <= 128 && !(va.half > 0 && full);
+    const bool fused = (D <= 128 && !(va.half > 0 && full)) || fused_h;
     if (!fused) {
       if constexpr (D <= 128) {
         // weights staged in LDS, persistent workgroups (one per CU)
@@ -439,7 +449,27 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       // the windowed form runs at most 4 heads per workgroup (registers)
       constexpr int HBW = H > 4 ? 4 : H;
       const dim3 grid_w(static_cast<unsigned>(P.G * (H / HBW)));
-      if (fused) {
+      if (fused_h) {
+        if constexpr (D == 256) {
+          using FC = mfma::FusedHCfg<ELL>;
+          auto launch_h = [&](auto kern, const Rows& src) {
+            static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         static_cast<int>(FC::lds_bytes)) == hipSuccess;
+            (void)attr;
+            LIME_LAUNCH("xor_attn_h", kern, dim3(static_cast<unsigned>(FC::grid(P.G))), dim3(64 * FC::NW),
+                        FC::lds_bytes, st, src, static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser, B,
+                        static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, qs);
+          };
+          if (l == 0) {
+            // the first layer's LayerNorm rows
+            LIME_LAUNCH("ln_rows", mfma::ln_rows_kernel<D>, dim3(static_cast<unsigned>(cu_count() * 8)), dim3(256), 0,
+                        st, Xin, R, LNr);
+            LIME_CHECK_LAUNCH("layer-0 LayerNorm rows");
+          }
+          launch_h(mfma::xor_attn_h<ELL, false>, LNrows);
+        }
+      } else if (fused) {
         if constexpr (D <= 128) {
           using FC = mfma::FusedCfg<ELL, H>;
           auto k = mfma::xor_attn_qkv<ELL, H>;
@@ -496,10 +526,12 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       const int64_t ntiles = (rows_post + 16 * PC::NW - 1) / (16 * PC::NW);
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
       if (grid > ntiles) grid = ntiles;
+      // the next layer's LayerNorm rows for the fused attention
+      const Rows Hout = (fused_h && !last) ? LNrows : Rows{nullptr, nullptr, 0, 0};
       LIME_LAUNCH("post_block_stream", k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, static_cast<const bf16_t*>(Y), R, Xin,
                          Xout, rows_post, static_cast<const bf16_t*>(w[l].w_o),
                          static_cast<const bf16_t*>(w[l].w_gate), static_cast<const bf16_t*>(w[l].w_up),
-                         static_cast<const bf16_t*>(w[l].w_down));
+                         static_cast<const bf16_t*>(w[l].w_down), Hout);
     }
     LIME_CHECK_LAUNCH("post-attention block (mfma)");
   }
@@ -718,11 +750,12 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
              "combine, post); splits of %lld history rows, at most %lld splits",
              static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else if (P.mfma) {
-    launches = 4 * layers + 1;
+    launches = 3 * layers + 2;
     snprintf(line, sizeof(line),
-             "streaming matrix-core: a split plan, then 4 launches per layer (qkv, xor_attn, combine, "
-             "post); splits of %lld history rows, at most %lld splits", static_cast<long long>(P.chunk),
-             static_cast<long long>(P.G));
+             "streaming matrix-core: a split plan and the first layer's LayerNorm rows, then 3 launches per "
+             "layer (xor_attn with the projection fused in, from LayerNorm rows the post block stores; "
+             "combine; post); splits of %lld history rows, at most %lld splits",
+             static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else {
     launches = 6 * layers;
     snprintf(line, sizeof(line),

@@ -951,6 +951,19 @@ __global__ __launch_bounds__(256) void xor_combine(const float* __restrict__ par
 // end re-read the last chunk and are not stored), so a thread waits on one
 // round trip per batch rather than one per chunk.
 constexpr int SU = 8;
+
+// Where row `row` of w_qkv sits when staged for the projection helpers
+// below: inside each 32-row block, bit 2 of the row index is flipped when
+// bit 4 is set.  A 16-lane group of their fragment reads touches rows
+// {0-3, 8-11, 16-19, 24-27} (or the same plus 4), or 16 consecutive rows; with
+// any uniform row stride rows r and r + 16 fall on the same banks, and this
+// permutation puts each group's 16 rows on 16 different bank groups in both
+// patterns (the padded stride D + 8 is an odd number of 16-byte units, so a
+// read's bank group is an odd multiple of its stored row plus its column
+// chunk, modulo 16).  Rows are permuted inside 32-row blocks only.
+__device__ __forceinline__ int wqkv_slot(int row) { return row ^ ((row >> 2) & 4); }
+
+template <bool WQKV = false>
 __device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict__ src, int rows, int K,
                                            int tid, int nthreads) {
   const int c8n = K / 8, total = rows * c8n;
@@ -965,7 +978,8 @@ __device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict
 #pragma unroll
     for (int u = 0; u < SU; ++u) {
       const int e = e0 + u * nthreads;
-      if (e < total) *reinterpret_cast<bf16x8*>(dst + (e / c8n) * (K + 8) + 8 * (e % c8n)) = v[u];
+      const int row = WQKV ? wqkv_slot(e / c8n) : e / c8n;
+      if (e < total) *reinterpret_cast<bf16x8*>(dst + row * (K + 8) + 8 * (e % c8n)) = v[u];
     }
   }
 }
@@ -1057,7 +1071,7 @@ __device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf
 // Q or K of head part p (p < H: Q, else K), multiplied by f, for the two row
 // blocks of hb, in the transposed form: out[rb] lane (r, g) holds features
 // 8g .. 8g+7 of the row that hb[rb] lane r carries.  W: w_qkv rows in LDS
-// with row stride ldw.
+// with row stride ldw, placed by wqkv_slot.
 template <int D>
 __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
                                              float f, int r, int g, f16x8 (&out)[2]) {
@@ -1065,12 +1079,16 @@ __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], cons
   floatx4 acc[2][2] = {};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const bf16_t* wr = W + (32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
+    const bf16_t* wr = W + wqkv_slot(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const bf16x8 a = ld16(wr + kb * 32);
       acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
       acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
+      // at d = 256 keep the weight fragments in flight bounded (registers)
+      if constexpr (KB > 4) {
+        if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 #pragma unroll
@@ -1086,15 +1104,18 @@ __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], cons
 // V of rows 8g .. 8g+7 for column `col_of(r)` of w_qkv's V part.
 template <int D, typename F>
 __device__ __forceinline__ f16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw,
-                                              F&& col_of, int r, int g) {
+                                              F&& col_of, int r, int g, int vrow0 = 2 * D) {
   constexpr int KB = D / 32;
-  const bf16_t* wr = W + (2 * D + col_of(r)) * ldw + 8 * g;
+  const bf16_t* wr = W + wqkv_slot(vrow0 + col_of(r)) * ldw + 8 * g;
   floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const bf16x8 bq = ld16(wr + kb * 32);
     a0 = mma(hb[0][kb], bq, a0);
     a1 = mma(hb[1][kb], bq, a1);
+    if constexpr (KB > 4) {
+      if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
   }
   const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
   return packh8(v);
@@ -1189,7 +1210,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
   bf16_t* hbuf = Wl + C::w_elems;  // [SPW][2][32][LDW]
   int* nchs = reinterpret_cast<int*>(hbuf + 2 * SPW * C::buf_elems);
-  stage_rows(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
+  stage_rows<true>(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int sidx = w / H, h = w % H;
@@ -1307,6 +1328,208 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
     });
   });
   if (!has) return;
+  float* p0 = part + ((x * H + h) * ELL) * PART_LD;
+#pragma unroll
+  for (int nb = 0; nb < MB; ++nb) {
+    // partials in natural units: max * ln 2; silu sums * ln 2
+    float* pl = p0 + (16 * nb + r) * PART_LD;
+    if (g == 0) {
+      pl[0] = softmax ? st.m[nb] * LN2 : 0.f;
+      pl[1] = softmax ? st.l[nb] : static_cast<float>(hi - lo);
+    }
+    const float f = softmax ? 1.f : LN2;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      *reinterpret_cast<floatx4*>(pl + 4 + 16 * c2 + 4 * g) =
+          floatx4{st.acc[nb][c2][0] * f, st.acc[nb][c2][1] * f, st.acc[nb][c2][2] * f, st.acc[nb][c2][3] * f};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// XOR attention with the history rows' QKV projection fused in, for d = 256,
+// whose w_qkv (384 KB) LDS cannot hold: a workgroup serves SPW = 4 splits
+// and a group of HG = 2 heads, with those heads' 192 rows of w_qkv staged in
+// LDS (Q rows, then K rows, then V rows, 32 per head); one wave per (split,
+// head) projects its user's link rows and each 32-row chunk of its split
+// itself, so Q, K and V never leave the registers.  The rows come from Hs,
+// LayerNorm(X) of every row that the previous layer's post block stored as
+// bf16 (LNX = false), or, in the first layer, from X normalised here
+// (LNX = true).  Each head group reads a split's rows once; block indices
+// are laid out so that the NHG head groups of a split run on one XCD close
+// together and share its rows in L2.  The next chunk's rows load into the
+// operand registers as soon as the projection has used them, while the
+// attention of the current chunk runs.
+// ---------------------------------------------------------------------------
+template <int ELL>
+struct FusedHCfg {
+  static constexpr int D = 256, H = 8, HG = 2, NW = 8, SPW = NW / HG, NHG = H / HG, LDW = D + 8;
+  static constexpr size_t w_elems = static_cast<size_t>(3) * HG * 32 * LDW;
+  static constexpr size_t lds_bytes = w_elems * 2;
+  // workgroups for G split slots: split groups rounded up to a multiple of
+  // the 8 XCDs, times the head groups
+  static constexpr int64_t grid(int64_t G) { return ((G + SPW - 1) / SPW + 7) / 8 * 8 * NHG; }
+};
+
+// Operands of two 16-row blocks (lane (r, g) of block rb: row row_of(rb) of
+// src, columns 32 kb + 8 g .. +8): the rows as stored (H rows), or their
+// LayerNorm (X rows, LNX).
+template <int D, bool LNX, typename F>
+__device__ __forceinline__ void row_operands(const Rows& src, F&& row_of, int g, bf16x8 (&hb)[2][D / 32]) {
+  if constexpr (LNX) {
+    ln_operands<D>(src, row_of, g, hb);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const bf16_t* xr = row_in<bf16_t>(src, row_of(rb)) + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb) hb[rb][kb] = ld16(xr + kb * 32);
+    }
+  }
+}
+
+// link operands of user b for head slot j of the staged head group (Q rows
+// at 32 j, K rows at 32 (HG + j), V rows at 32 (2 HG + j) of W); as link_ops
+template <int ELL, int D, int HG, bool LNX>
+__device__ __forceinline__ void link_ops_hg(HeadOps<ELL>& o, const Rows& src, const bf16_t* W, int ldw, int b,
+                                            int j, int r, int g, float qs) {
+  const int64_t l0 = static_cast<int64_t>(b) * ELL;
+#pragma unroll
+  for (int kb2 = 0; kb2 < ELL / 32; ++kb2) {
+    bf16x8 hb[2][D / 32];
+    row_operands<D, LNX>(src, [&](int rb) { return l0 + kb2 * 32 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
+    f16x8 k2[2];
+    proj_qk_regs<D>(hb, W, ldw, HG + j, qs, r, g, k2);
+    o.kl[2 * kb2] = k2[0];
+    o.kl[2 * kb2 + 1] = k2[1];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      o.vlt[c2][kb2] = proj_v_regs<D>(hb, W, ldw, [&](int rr) { return 32 * j + 8 * (rr >> 2) + 4 * c2 + (rr & 3); },
+                                      r, g, 2 * HG * 32);
+    row_operands<D, LNX>(src, [&](int rb) { return l0 + kb2 * 32 + 16 * rb + r; }, g, hb);
+    f16x8 q2[2];
+    proj_qk_regs<D>(hb, W, ldw, j, qs, r, g, q2);
+    o.qlt[2 * kb2] = q2[0];
+    o.qlt[2 * kb2 + 1] = q2[1];
+  }
+}
+
+// LayerNorm (no affine, eps 1e-5) of every row of X as bf16 [R, D]: the
+// first layer's operands of xor_attn_h (later layers get theirs from the
+// post block).  D / 8 lanes per row, 16 bytes each; two-pass statistics.
+template <int D>
+__global__ __launch_bounds__(256) void ln_rows_kernel(Rows X, int64_t R, bf16_t* __restrict__ out) {
+  constexpr int LPR = D / 8;            // lanes per row
+  constexpr int RPB = 256 / LPR;        // rows per block step
+  static_assert(LPR == 32, "written for d = 256");
+  const int tid = threadIdx.x, c8 = tid % LPR;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / LPR; row < R;
+       row += static_cast<int64_t>(gridDim.x) * RPB) {
+    const bf16x8 x = ld16(row_in<bf16_t>(X, row) + 8 * c8);
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = static_cast<float>(x[q]);
+    float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
+    const float mu = s * (1.f / static_cast<float>(D));
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float u = v[q] - mu;
+      t = fmaf(u, u, t);
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) t += __shfl_xor(t, o);
+    const float rs = rsqrtf(t * (1.f / static_cast<float>(D)) + 1e-5f);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = (v[q] - mu) * rs;
+    st8(out + row * D + 8 * c8, v);
+  }
+}
+
+template <int ELL, bool LNX>
+__global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __restrict__ W,
+                                                  bf16_t* __restrict__ Y, float* __restrict__ part,
+                                                  const int64_t* __restrict__ off,
+                                                  const int32_t* __restrict__ split_off,
+                                                  const int32_t* __restrict__ split_user, int B, int G,
+                                                  int64_t chunk, int64_t total_N, int phi, int do_e, float qs) {
+  using C = FusedHCfg<ELL>;
+  constexpr int D = C::D, H = C::H, HG = C::HG, SPW = C::SPW, NHG = C::NHG, MB = ELL / 16, LDW = C::LDW;
+  // block -> (split group, head group): the NHG head groups of a split
+  // group take consecutive slots of one XCD (blocks are spread over the 8
+  // XCDs round-robin)
+  const int64_t slot = blockIdx.x >> 3;
+  const int hgi = static_cast<int>(slot % NHG);
+  const int64_t sg = (slot / NHG) * 8 + (blockIdx.x & 7);
+  {
+    const int64_t x0 = sg * SPW;
+    if (x0 >= G || split_user[x0] < 0) return;  // slots past the last split
+  }
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
+  // the head group's rows of w_qkv: Q, K, V parts, HG * 32 rows each
+#pragma unroll
+  for (int part3 = 0; part3 < 3; ++part3)
+    stage_rows<true>(Wl + part3 * HG * 32 * LDW, W + (static_cast<int64_t>(part3) * D + hgi * HG * 32) * D, HG * 32, D,
+               threadIdx.x, C::NW * 64);
+  lds_barrier();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int j = w % HG, h = hgi * HG + j;
+  const int64_t x = sg * SPW + w / HG;  // split
+  const int b = x < G ? split_user[x] : -1;
+  if (b < 0) return;  // no barrier follows
+  const int64_t nlr = static_cast<int64_t>(B) * ELL;
+  int64_t lo = 0, hi = 0;
+  {
+    const int64_t sx = x - split_off[b];
+    const int64_t u0 = clamp64(off[b], 0, total_N);
+    const int64_t u1 = clamp64(off[b + 1], u0, total_N);
+    split_rows(u0, u1, sx, chunk, &lo, &hi);
+  }
+  const int64_t c0s = lo & ~int64_t(7);
+  const int nch = c0s < hi ? static_cast<int>((hi - 1 - c0s) >> 5) + 1 : 0;
+  const bool softmax = (phi == PHI_SOFTMAX);
+  const bf16_t* Wb = Wl + opaque_zero();
+
+  HeadOps<ELL> o;
+  link_ops_hg<ELL, D, HG, LNX>(o, src, Wb, LDW, b, j, r, g, qs);
+  LState<ELL> st;
+  st.init();
+  const Lay yl{32, (nlr + total_N) * 32};
+  with_phi(softmax, [&](auto phi_tag) {
+    with_flag(do_e != 0, [&](auto e_tag) {
+      constexpr bool SM = decltype(phi_tag)::value, DO_E = decltype(e_tag)::value;
+      // chunk i's rows in the projection order (clamped: past the history
+      // end they are read but not used)
+      bf16x8 hb[2][D / 32];
+      auto load = [&](int i) {
+        const int64_t c0 = c0s + 32 * i;
+        row_operands<D, LNX>(src, [&](int rb) {
+          int64_t jj = c0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+          jj = jj < total_N ? jj : total_N - 1;
+          return nlr + jj;
+        }, g, hb);
+      };
+      if (nch > 0) load(0);
+      for (int i = 0; i < nch; ++i) {
+        const int64_t c0 = c0s + 32 * i;
+        ChunkOps ci;
+        // (the logit scale is on the link side)
+        if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, j, 1.f, r, g, ci.qe);
+        proj_qk_regs<D>(hb, Wb, LDW, HG + j, 1.f, r, g, ci.ke);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+          ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * j + 16 * c2 + rr; }, r, g, 2 * HG * 32);
+        // the operand registers are free: the next chunk's rows load while
+        // this chunk's attention runs
+        if (i + 1 < nch) load(i + 1);
+        if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+      }
+    });
+  });
   float* p0 = part + ((x * H + h) * ELL) * PART_LD;
 #pragma unroll
   for (int nb = 0; nb < MB; ++nb) {
@@ -1617,13 +1840,15 @@ struct PostStreamCfg {
 
 __device__ __forceinline__ int swz(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
 
+// Hout (Hout.a non-null): also LayerNorm(output row) as bf16, the next
+// layer's attention operands.
 template <int D>
 __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restrict__ Y, int64_t yR,
                                                          Rows Xres, Rows Out, int64_t nrows,
                                                          const bf16_t* __restrict__ Wo,
                                                          const bf16_t* __restrict__ Wg,
                                                          const bf16_t* __restrict__ Wu,
-                                                         const bf16_t* __restrict__ Wd) {
+                                                         const bf16_t* __restrict__ Wd, Rows Hout) {
   using C = PostStreamCfg<D>;
   constexpr int KB = D / 32, NW = C::NW, CR = C::CR, NCH = 16, SPR = C::SPR, CPT = C::CPT;
   static_assert(D == 256, "chunk schedule is written for d = 256");
@@ -1795,6 +2020,15 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
       if (orow != nullptr)
 #pragma unroll
         for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[0][8 * p]);
+    }
+    if (Hout.a != nullptr) {
+      // (all lanes: the LN reduces over the lanes of each row)
+      ln_rows<8 * KB>(x1[0], D);
+      if (rowok) {
+        bf16_t* hrow = row_out<bf16_t>(Hout, row);
+#pragma unroll
+        for (int p = 0; p < KB; ++p) st8(hrow + 32 * p + 8 * g, &x1[0][8 * p]);
+      }
     }
     t3 = (t3 + 16) % 3;
   }
