@@ -207,6 +207,8 @@ lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
   if (d % heads != 0) return fail(LIME_ERR_INVALID_ARG, "d (%d) must be a multiple of heads (%d)", d, heads);
   if (d_ff < 1) return fail(LIME_ERR_INVALID_ARG, "d_ff must be >= 1");
   if (total_N < 0 || max_N < 0) return fail(LIME_ERR_INVALID_ARG, "total_N and max_N must be >= 0");
+  // (row blocks of 16 are counted in 32 bits on the device)
+  if (total_N > (int64_t(1) << 34)) return fail(LIME_ERR_UNSUPPORTED, "total_N above 2^34 rows is unsupported");
   if (ell > 256) return fail(LIME_ERR_UNSUPPORTED, "ell > 256 unsupported (got %d)", ell);
   if (d % 8 != 0 || d > 1024) return fail(LIME_ERR_UNSUPPORTED, "d must be a multiple of 8 and <= 1024 (got %d)", d);
   if (d_ff % 8 != 0 || d_ff > 4096) return fail(LIME_ERR_UNSUPPORTED, "d_ff must be a multiple of 8 and <= 4096 (got %d)", d_ff);
@@ -523,9 +525,10 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                                                    static_cast<int>(lds)) == hipSuccess;
       (void)attr;
       static const int per_cu = blocks_per_cu_lds(k, PC::NT, lds);
-      const int64_t ntiles = (rows_post + 16 * PC::NW - 1) / (16 * PC::NW);
+      // every workgroup gets at least one 16-row block
+      const int64_t nblk = (rows_post + 15) / 16;
       int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
-      if (grid > ntiles) grid = ntiles;
+      if (grid > nblk) grid = nblk;
       // the next layer's LayerNorm rows for the fused attention
       const Rows Hout = (fused_h && !last) ? LNrows : Rows{nullptr, nullptr, 0, 0};
       LIME_LAUNCH("post_block_stream", k, dim3(static_cast<unsigned>(grid)), dim3(PC::NT), lds, st, static_cast<const bf16_t*>(Y), R, Xin,

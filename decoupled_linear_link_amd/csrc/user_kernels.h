@@ -1821,9 +1821,13 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_stream(Rows X, int64_t R, int
 }
 
 // Post-attention block, weights streamed: 16 chunks of 64 weight rows per
-// 128-row tile: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of
-// each: one pair), 12..15 w_down (two pairs each).  One wave of eight owns
-// 16 rows, so each chunk in LDS feeds 128 rows.  Chunks travel global ->
+// step: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of each:
+// one pair), 12..15 w_down (two pairs each).  One wave of eight owns a
+// 16-row block per step, so each chunk in LDS feeds up to 128 rows.  Each
+// workgroup takes an equal contiguous range of 16-row blocks (rounded), 8
+// per step: its last step may hold fewer blocks, and the waves without one
+// only stream and wait.  (Whole 128-row tiles dealt round-robin left, at
+// 3.1 rounds, a fourth round of full tiles on a tenth of the CUs.)  Chunks travel global ->
 // LDS directly (LDS-DMA buffer loads, 16 bytes per lane), so no registers
 // carry them; three chunk buffers keep two chunks in flight while one is
 // computed, and the next tile's Y and X rows are fetched during the w_down
@@ -1857,8 +1861,12 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
   bf16_t* const buf0 = reinterpret_cast<bf16_t*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int64_t ntiles = (nrows + 16 * NW - 1) / (16 * NW);
-  const int64_t my_tiles = (ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  // this workgroup's 16-row blocks [blk0, blk1), NW per step (block
+  // indices fit 32 bits: the host caps nrows below 2^35)
+  const int nblk = static_cast<int>((nrows + 15) / 16);
+  const int blk0 = static_cast<int>(static_cast<int64_t>(blockIdx.x) * nblk / gridDim.x);
+  const int blk1 = static_cast<int>((static_cast<int64_t>(blockIdx.x) + 1) * nblk / gridDim.x);
+  const int my_tiles = (blk1 - blk0 + NW - 1) / NW;
   if (my_tiles <= 0) return;
 
   // Chunk step i of a chunk (CPT steps, 16 weight rows each): row 16 i +
@@ -1893,15 +1901,18 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
   auto frag = [&](const bf16_t* wb, int row, int kb) {
     return ld16(wb + row * D + 8 * ((4 * kb + g) ^ r));
   };
-  // the Y rows of tile `it` (fetched during the previous tile's last
-  // chunks) and its X rows (fetched at the tile's start, first used when
-  // the w_o product is complete); rows past the end read row 0, unused
-  auto tile_row = [&](int64_t it) {
-    const int64_t row = (blockIdx.x + it * gridDim.x) * 16 * NW + 16 * w + r;
-    return row < nrows ? row : int64_t(0);
+  // the Y rows of step `it` (fetched during the previous step's last
+  // chunks) and its X rows (fetched at the step's start, first used when
+  // the w_o product is complete); rows past the end, or of a wave without
+  // a block, read row 0, unused (every wave issues the same loads: the
+  // counted waits below rely on it)
+  auto tile_row = [&](int it) {
+    const int blk = blk0 + it * NW + w;
+    const int64_t row = static_cast<int64_t>(blk) * 16 + r;
+    return blk < blk1 && row < nrows ? row : int64_t(0);
   };
   bf16x8 yn[KB];
-  auto load_y = [&](int64_t it) {
+  auto load_y = [&](int it) {
     const bf16_t* yr = Y + tile_row(it) * 32 + 8 * g;  // head-planar: head kb at kb * yR * 32
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) yn[kb] = ld16(yr + kb * yR * 32);
@@ -1918,9 +1929,11 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
   wait_vm<CPT>();  // Y and chunk 0 have landed
   dma_barrier();
   int t3 = 0;  // (tile index) % 3: chunk k of this tile is in buffer (t3 + k) % 3
-  for (int64_t it = 0; it < my_tiles; ++it) {
-    const int64_t row = (blockIdx.x + it * gridDim.x) * 16 * NW + 16 * w + r;
-    const bool rowok = row < nrows;
+  for (int it = 0; it < my_tiles; ++it) {
+    const int blk = blk0 + it * NW + w;
+    const bool active = blk < blk1;  // wave-uniform
+    const int64_t row = static_cast<int64_t>(blk) * 16 + r;
+    const bool rowok = active && row < nrows;
     const bool next = it + 1 < my_tiles;
     bf16x8 yb[1][KB], xr[KB];
     {
@@ -1942,7 +1955,9 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
       const bool more2 = (k + 2 < NCH) || next;
       if (more2) issue_chunk((k + 2) % NCH, buf0 + ((t3 + k + 2) % 3) * (CR * D));
       const bf16_t* wb = buf0 + ((t3 + k) % 3) * (CR * D) + opaque_zero();
-      if (k < 4 || k >= 12) {
+      if (!active) {
+        // no block this step: stream and wait only
+      } else if (k < 4 || k >= 12) {
         // x1 += (Y or M) W^T for column pairs 2k', 2k'+1
         const int kk = k < 4 ? k : k - 12;
 #pragma unroll
@@ -2021,8 +2036,8 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
 #pragma unroll
         for (int p = 0; p < KB; ++p) st8(orow + 32 * p + 8 * g, &x1[0][8 * p]);
     }
-    if (Hout.a != nullptr) {
-      // (all lanes: the LN reduces over the lanes of each row)
+    if (Hout.a != nullptr && active) {
+      // (all lanes of the wave: the LN reduces over the lanes of each row)
       ln_rows<8 * KB>(x1[0], D);
       if (rowok) {
         bf16_t* hrow = row_out<bf16_t>(Hout, row);

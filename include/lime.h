@@ -125,7 +125,8 @@ size_t lime_xor_fwd_workspace_size(lime_dtype_t dtype, int32_t B, int32_t ell, i
  *                                     off[B] = total_N are required (other
  *                                     values give unspecified outputs but no
  *                                     access outside the buffers).
- *   total_N      host, rows of hist.
+ *   total_N      host, rows of hist, at most 2^34 (LIME_ERR_UNSUPPORTED
+ *                above).
  *   max_N        host, an upper bound of every N_b (it sizes the on-chip
  *                buffers).  A user with N_b > max_N gets unspecified
  *                outputs, but no access falls outside the passed buffers.
