@@ -79,6 +79,7 @@ def _call_xor(L, a):
     (dict(total_N=-1), 1), (dict(links_ctx=None), 1), (dict(off=None), 1), (dict(lp=None), 1),
     (dict(hist=None), 1), (dict(links_ctx=PM), 1), (dict(ho=PM), 1),
     (dict(ell=300), 2), (dict(d=96, heads=1), 2), (dict(d=60, heads=2), 2), (dict(d_ff=60), 2),
+    (dict(total_N=(1 << 34) + 1), 2),
     (dict(ws=None), 3), (dict(ws_bytes=1024), 3), (dict(ws=P + 16), 3),
 ])
 def test_xor_fwd_rejects(L, kw, code):
@@ -124,6 +125,7 @@ def test_workspace_size_is_monotone_and_zero_on_bad_sizes(L):
     assert 0 < a < b
     assert f(1, 0, 32, 128, 4, 128, 100, 10) == 0
     assert f(9, 4, 32, 128, 4, 128, 100, 10) == 0
+    assert f(1, 8, 64, 256, 8, 256, (1 << 34) + 1, 16384) == 0  # beyond the row cap
 
 
 @pytest.mark.parametrize("kw,code", [
