@@ -174,9 +174,15 @@ def against_roof(bytes_, flops, seconds, peak_tflops):
 # the source files that hold each kernel's device code (their launch code in
 # lime_api.hip is unchanged since the summaries were taken):
 # a counter summary stays valid while these are unchanged
+# the files that hold each kernel's code: a traffic summary is used only while
+# their hash matches the one it records
+_USER = ("common.h", "mfma_kernels.h", "user_kernels.h")
 KERNEL_SOURCES = {
     "qk_cache": ("common.h", "mfma_kernels.h"),
     "cand_score": ("common.h", "mfma_kernels.h"),
+    **{k: _USER for k in ("xor_attn_h", "xor_attn_qkv", "xor_attn", "post_block_stream", "post_block_lds",
+                          "qkv_proj_stream", "qkv_proj_lds", "ln_rows", "xor_combine", "xor_fwd_resident",
+                          "xor_fwd_resident_score")},
 }
 ALL_SOURCES = ("common.h", "generic_kernels.h", "lime_api.hip", "mfma_kernels.h", "user_kernels.h")
 
@@ -195,7 +201,7 @@ def traffic_from_profiles(workload, kernel):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        files = tuple(kv.get("sources", "").split()) or ALL_SOURCES
+        files = tuple(kv.get("sources", "").split()) or KERNEL_SOURCES.get(kernel, ALL_SOURCES)
         if kv.get("sources_sha256") != sources_sha256(files):
             return None
         return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])

@@ -1525,8 +1525,12 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
         // the operand registers are free: the next chunk's rows load while
         // this chunk's attention runs
         if (i + 1 < nch) load(i + 1);
+        // the attention's dependent VALU chains take issue priority over the
+        // projection products of the SIMD's other wave (3% per layer)
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
         l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+        __builtin_amdgcn_s_setprio(0);
       }
     });
   });
