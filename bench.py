@@ -130,8 +130,12 @@ def kernel_work(w, es, total_N, n_cand):
         return 2 * R * d * es, 0.0
 
     def post(full):
+        # read Y and X, write the new rows; at d = 256 a full layer's post
+        # block also writes the next layer's LayerNorm rows (the operands of
+        # the attention with the projection fused in)
         rows = R if full else nlr
-        return 3 * rows * d * es, rows * (2.0 * d * d + 6.0 * d * f)
+        passes = 4 if (full and d == 256) else 3
+        return passes * rows * d * es, rows * (2.0 * d * d + 6.0 * d * f)
 
     def combine(full):
         return nlr * d * es, 0.0
