@@ -210,9 +210,9 @@ def xor_fwd_workspace_size(dtype, B, ell, d, heads, d_ff, total_N, max_N) -> int
 
 def xor_fwd_plan(dtype, B, ell, d, heads, layers, d_ff, total_N, max_N, with_hist=False):
     """(number of kernel launches, description) of the plan lime_xor_fwd uses."""
-    buf = ctypes.create_string_buffer(256)
+    buf = ctypes.create_string_buffer(512)
     n = lib.lime_xor_fwd_plan(DTYPE[dtype], B, ell, d, heads, layers, d_ff, total_N, max_N,
-                              int(bool(with_hist)), buf, 256)
+                              int(bool(with_hist)), buf, 512)
     return int(n), buf.value.decode()
 
 

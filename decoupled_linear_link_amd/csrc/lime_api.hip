@@ -742,7 +742,7 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
   const XorPlan P = plan_xor(dtype, B, ell, d, heads, d_ff, total_N, max_N);
   const bool resident = P.mfma && P.resident && d <= 128 && layers <= mfma::RES_MAX_LAYERS;
   int32_t launches;
-  char line[256];
+  char line[512];
   if (resident) {
     launches = 1;
     snprintf(line, sizeof(line), "user-resident: 1 launch for %d layers, one workgroup per user", layers);
@@ -756,7 +756,7 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
     launches = 3 * layers + 2;
     snprintf(line, sizeof(line),
              "streaming matrix-core: a split plan and the first layer's LayerNorm rows, then 3 launches per "
-             "layer (xor_attn with the projection fused in, from LayerNorm rows the post block stores; "
+             "layer (xor_attn_h: the attention with the projection fused in, from LayerNorm rows the post block stores; "
              "combine; post); splits of %lld history rows, at most %lld splits",
              static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else {
