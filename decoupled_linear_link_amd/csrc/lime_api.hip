@@ -454,22 +454,26 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
       if (fused_h) {
         if constexpr (D == 256) {
           using FC = mfma::FusedHCfg<ELL>;
-          auto launch_h = [&](auto kern, const Rows& src) {
-            static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+          // (the same signature for both forms: each sets its own LDS limit)
+          auto kf = mfma::xor_attn_h<ELL, false, true>;
+          auto kl = mfma::xor_attn_h<ELL, false, false>;
+          static const bool attr_f = hipFuncSetAttribute(reinterpret_cast<const void*>(kf),
                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                                          static_cast<int>(FC::lds_bytes)) == hipSuccess;
-            (void)attr;
-            LIME_LAUNCH("xor_attn_h", kern, dim3(static_cast<unsigned>(FC::grid(P.G))), dim3(64 * FC::NW),
-                        FC::lds_bytes, st, src, static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser, B,
-                        static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), full ? 1 : 0, qs);
-          };
+          static const bool attr_l = hipFuncSetAttribute(reinterpret_cast<const void*>(kl),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         static_cast<int>(FC::lds_bytes)) == hipSuccess;
+          (void)attr_f;
+          (void)attr_l;
           if (l == 0) {
             // the first layer's LayerNorm rows
             LIME_LAUNCH("ln_rows", mfma::ln_rows_kernel<D>, dim3(static_cast<unsigned>(cu_count() * 8)), dim3(256), 0,
                         st, Xin, R, LNr);
             LIME_CHECK_LAUNCH("layer-0 LayerNorm rows");
           }
-          launch_h(mfma::xor_attn_h<ELL, false>, LNrows);
+          LIME_LAUNCH("xor_attn_h", full ? kf : kl, dim3(static_cast<unsigned>(FC::grid(P.G))), dim3(64 * FC::NW),
+                      FC::lds_bytes, st, LNrows, static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser,
+                      B, static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), qs);
         }
       } else if (fused) {
         if constexpr (D <= 128) {

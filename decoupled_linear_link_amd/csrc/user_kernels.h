@@ -1447,13 +1447,16 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(Rows X, int64_t R, bf16_t*
   }
 }
 
-template <int ELL, bool LNX>
+// DO_E: the layer also updates history rows (the E-branch).  Without it
+// (a last layer) Q_E, K_L and V_L are dead, and the freed registers hold a
+// second operand buffer: the rows are loaded two chunks ahead.
+template <int ELL, bool LNX, bool DO_E>
 __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __restrict__ W,
                                                   bf16_t* __restrict__ Y, float* __restrict__ part,
                                                   const int64_t* __restrict__ off,
                                                   const int32_t* __restrict__ split_off,
                                                   const int32_t* __restrict__ split_user, int B, int G,
-                                                  int64_t chunk, int64_t total_N, int phi, int do_e, float qs) {
+                                                  int64_t chunk, int64_t total_N, int phi, float qs) {
   using C = FusedHCfg<ELL>;
   constexpr int D = C::D, H = C::H, HG = C::HG, SPW = C::SPW, NHG = C::NHG, MB = ELL / 16, LDW = C::LDW;
   // block -> (split group, head group): the NHG head groups of a split
@@ -1499,40 +1502,65 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
   st.init();
   const Lay yl{32, (nlr + total_N) * 32};
   with_phi(softmax, [&](auto phi_tag) {
-    with_flag(do_e != 0, [&](auto e_tag) {
-      constexpr bool SM = decltype(phi_tag)::value, DO_E = decltype(e_tag)::value;
-      // chunk i's rows in the projection order (clamped: past the history
-      // end they are read but not used)
-      bf16x8 hb[2][D / 32];
-      auto load = [&](int i) {
-        const int64_t c0 = c0s + 32 * i;
-        row_operands<D, LNX>(src, [&](int rb) {
-          int64_t jj = c0 + 8 * (r >> 2) + 4 * rb + (r & 3);
-          jj = jj < total_N ? jj : total_N - 1;
-          return nlr + jj;
-        }, g, hb);
-      };
-      if (nch > 0) load(0);
-      for (int i = 0; i < nch; ++i) {
-        const int64_t c0 = c0s + 32 * i;
-        ChunkOps ci;
-        // (the logit scale is on the link side)
-        if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, j, 1.f, r, g, ci.qe);
-        proj_qk_regs<D>(hb, Wb, LDW, HG + j, 1.f, r, g, ci.ke);
+    constexpr bool SM = decltype(phi_tag)::value;
+    using Ops = bf16x8[2][D / 32];
+    // chunk i's rows in the projection order (clamped: past the history
+    // end they are read but not used)
+    auto load = [&](Ops& hb, int i) {
+      const int64_t c0 = c0s + 32 * i;
+      row_operands<D, LNX>(src, [&](int rb) {
+        int64_t jj = c0 + 8 * (r >> 2) + 4 * rb + (r & 3);
+        jj = jj < total_N ? jj : total_N - 1;
+        return nlr + jj;
+      }, g, hb);
+    };
+    auto project = [&](const Ops& hb, ChunkOps& ci) {
+      // (the logit scale is on the link side)
+      if constexpr (DO_E) proj_qk_regs<D>(hb, Wb, LDW, j, 1.f, r, g, ci.qe);
+      proj_qk_regs<D>(hb, Wb, LDW, HG + j, 1.f, r, g, ci.ke);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-          ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * j + 16 * c2 + rr; }, r, g, 2 * HG * 32);
-        // the operand registers are free: the next chunk's rows load while
-        // this chunk's attention runs
-        if (i + 1 < nch) load(i + 1);
-        // the attention's dependent VALU chains take issue priority over the
-        // projection products of the SIMD's other wave (3% per layer)
-        __builtin_amdgcn_s_setprio(1);
-        if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
-        l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
-        __builtin_amdgcn_s_setprio(0);
+      for (int c2 = 0; c2 < 2; ++c2)
+        ci.ve[c2] = proj_v_regs<D>(hb, Wb, LDW, [&](int rr) { return 32 * j + 16 * c2 + rr; }, r, g, 2 * HG * 32);
+    };
+    auto attend = [&](const ChunkOps& ci, int64_t c0) {
+      // the attention's dependent VALU chains take issue priority over the
+      // projection products of the SIMD's other wave (3% per layer)
+      __builtin_amdgcn_s_setprio(1);
+      if constexpr (DO_E) e_branch<ELL, D, SM, 0, true>(o, ci, Y, nlr, c0, lo, hi, h, r, g, yl);
+      l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    if constexpr (DO_E) {
+      // one chunk ahead, into the operand registers the projections have
+      // just freed, while this chunk's attention runs
+      Ops hb;
+      if (nch > 0) load(hb, 0);
+      for (int i = 0; i < nch; ++i) {
+        ChunkOps ci;
+        project(hb, ci);
+        if (i + 1 < nch) load(hb, i + 1);
+        attend(ci, c0s + 32 * i);
       }
-    });
+    } else if (nch > 0) {
+      // two chunks ahead in two buffers that alternate by name; every step
+      // issues its load (past the last chunk it rereads that chunk, unused)
+      // so that the waits stay exact
+      Ops ha, hz;
+      auto step = [&](Ops& hb, int i) {
+        ChunkOps ci;
+        project(hb, ci);
+        load(hb, i + 2 < nch ? i + 2 : nch - 1);
+        attend(ci, c0s + 32 * i);
+      };
+      load(ha, 0);
+      load(hz, nch > 1 ? 1 : 0);
+      int i = 0;
+      for (; i + 2 <= nch; i += 2) {
+        step(ha, i);
+        step(hz, i + 1);
+      }
+      if (i < nch) step(ha, i);
+    }
   });
   float* p0 = part + ((x * H + h) * ELL) * PART_LD;
 #pragma unroll
