@@ -952,18 +952,20 @@ __global__ __launch_bounds__(256) void xor_combine(const float* __restrict__ par
 // round trip per batch rather than one per chunk.
 constexpr int SU = 8;
 
-// Where row `row` of w_qkv sits when staged for the projection helpers
-// below: inside each 32-row block, bit 2 of the row index is flipped when
-// bit 4 is set.  A 16-lane group of their fragment reads touches rows
-// {0-3, 8-11, 16-19, 24-27} (or the same plus 4), or 16 consecutive rows; with
-// any uniform row stride rows r and r + 16 fall on the same banks, and this
-// permutation puts each group's 16 rows on 16 different bank groups in both
-// patterns (the padded stride D + 8 is an odd number of 16-byte units, so a
-// read's bank group is an odd multiple of its stored row plus its column
-// chunk, modulo 16).  Rows are permuted inside 32-row blocks only.
+// Where row `row` sits when staged for the projection helpers below (w_qkv
+// rows, and the fused kernels' LN chunk rows): inside each 32-row block,
+// bit 2 of the row index is flipped when bit 4 is set.  A fragment read
+// (ds_read_b128: 16 rows, 4 adjacent 16-byte columns per row) touches 16
+// consecutive rows, or rows {0-3, 8-11, 16-19, 24-27} (or those plus 4).
+// Measured with the LDS bank-conflict counter on gfx950: with rows padded by
+// 16 bytes every one of these reads conflicts (half of its LDS cycles);
+// with 32 bytes of padding consecutive rows are conflict-free, and so are
+// the strided sets once permuted by this slot map.  Rows are permuted inside
+// 32-row blocks only.
 __device__ __forceinline__ int wqkv_slot(int row) { return row ^ ((row >> 2) & 4); }
 
-template <bool WQKV = false>
+// PAD: elements of padding per staged row (8 = 16 bytes, 16 = 32 bytes)
+template <bool WQKV = false, int PAD = 8>
 __device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict__ src, int rows, int K,
                                            int tid, int nthreads) {
   const int c8n = K / 8, total = rows * c8n;
@@ -979,7 +981,7 @@ __device__ __forceinline__ void stage_rows(bf16_t* dst, const bf16_t* __restrict
     for (int u = 0; u < SU; ++u) {
       const int e = e0 + u * nthreads;
       const int row = WQKV ? wqkv_slot(e / c8n) : e / c8n;
-      if (e < total) *reinterpret_cast<bf16x8*>(dst + row * (K + 8) + 8 * (e % c8n)) = v[u];
+      if (e < total) *reinterpret_cast<bf16x8*>(dst + row * (K + PAD) + 8 * (e % c8n)) = v[u];
     }
   }
 }
@@ -1169,7 +1171,9 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
 // them); a split out of chunks only joins the barriers.
 template <int ELL, int H>
 struct FusedCfg {
-  static constexpr int D = 32 * H, NW = 8, SPW = NW / H, LDW = D + 8;
+  // rows padded by 32 bytes (LDW): with the wqkv_slot row order, fragment
+  // reads of the staged weights and of the LN chunk rows are conflict-free
+  static constexpr int D = 32 * H, NW = 8, SPW = NW / H, LDW = D + 16;
   static constexpr int RPWV = 32 / H;  // chunk rows each wave normalizes
   static constexpr size_t w_elems = static_cast<size_t>(3) * D * LDW;
   static constexpr size_t buf_elems = static_cast<size_t>(32) * LDW;
@@ -1210,7 +1214,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
   bf16_t* hbuf = Wl + C::w_elems;  // [SPW][2][32][LDW]
   int* nchs = reinterpret_cast<int*>(hbuf + 2 * SPW * C::buf_elems);
-  stage_rows<true>(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
+  stage_rows<true, LDW - D>(Wl, W, 3 * D, D, threadIdx.x, C::NW * 64);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int sidx = w / H, h = w % H;
@@ -1292,7 +1296,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
             float v[8];
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) v[jj] = fmaf(static_cast<float>(xc[u][jj]), rs, nb);
-            *reinterpret_cast<bf16x8*>(buf + crow * LDW + 16 * fg + 8 * u) = pack8(v);
+            *reinterpret_cast<bf16x8*>(buf + wqkv_slot(crow) * LDW + 16 * fg + 8 * u) = pack8(v);
           }
         }
         lds_barrier();
@@ -1305,7 +1309,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
               hb[rb][kb] = *reinterpret_cast<const bf16x8*>(
-                  buf + (8 * (r >> 2) + 4 * rb + (r & 3)) * LDW + 32 * kb + 8 * g);
+                  buf + wqkv_slot(8 * (r >> 2) + 4 * rb + (r & 3)) * LDW + 32 * kb + 8 * g);
           const bf16_t* Wb = Wl + opaque_zero();
           ChunkOps ci;
           // (the logit scale is on the link side)
@@ -1362,7 +1366,7 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
 // ---------------------------------------------------------------------------
 template <int ELL>
 struct FusedHCfg {
-  static constexpr int D = 256, H = 8, HG = 2, NW = 8, SPW = NW / HG, NHG = H / HG, LDW = D + 8;
+  static constexpr int D = 256, H = 8, HG = 2, NW = 8, SPW = NW / HG, NHG = H / HG, LDW = D + 16;
   static constexpr size_t w_elems = static_cast<size_t>(3) * HG * 32 * LDW;
   static constexpr size_t lds_bytes = w_elems * 2;
   // workgroups for G split slots: split groups rounded up to a multiple of
@@ -1474,7 +1478,7 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
   // the head group's rows of w_qkv: Q, K, V parts, HG * 32 rows each
 #pragma unroll
   for (int part3 = 0; part3 < 3; ++part3)
-    stage_rows<true>(Wl + part3 * HG * 32 * LDW, W + (static_cast<int64_t>(part3) * D + hgi * HG * 32) * D, HG * 32, D,
+    stage_rows<true, LDW - D>(Wl + part3 * HG * 32 * LDW, W + (static_cast<int64_t>(part3) * D + hgi * HG * 32) * D, HG * 32, D,
                threadIdx.x, C::NW * 64);
   lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
