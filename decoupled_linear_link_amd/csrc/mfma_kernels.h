@@ -162,8 +162,8 @@ __device__ __forceinline__ void st8(bf16_t* p, const float* v) {
 // so lane group g holds links [g*4*MB, (g+1)*4*MB) of its item.
 //
 // Work: a workgroup takes tiles of TI items (persistent, grid-stride).  The
-// tile is staged once in LDS (rows padded by 16 bytes against bank
-// conflicts) and shared by all waves; each wave keeps the keys of its heads
+// tile is staged once in LDS (rows padded by 16 bytes) and shared by all
+// waves; each wave keeps the keys of its heads
 // in registers for the whole kernel.  The next tile's rows are prefetched
 // into registers while the current tile is computed.
 // ---------------------------------------------------------------------------

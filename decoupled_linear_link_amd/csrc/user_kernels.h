@@ -942,11 +942,12 @@ __global__ __launch_bounds__(256) void xor_combine(const float* __restrict__ par
 
 // ---------------------------------------------------------------------------
 // Persistent variants with the weights staged once per workgroup in LDS
-// (rows padded by 16 bytes so the 16 rows read by one fragment load fall in
-// distinct banks).  NW waves per workgroup; each wave walks 32-row blocks
-// strided by the whole grid.
+// (rows padded by 16 bytes).  NW waves per workgroup; each wave walks
+// 32-row blocks strided by the whole grid.
 // ---------------------------------------------------------------------------
-// Copies rows x K bf16 from global memory into LDS rows padded by 16 bytes.
+// Copies rows x K bf16 from global memory into LDS rows padded by PAD
+// elements (16 or 32 bytes; see wqkv_slot for what each costs in bank
+// conflicts).
 // SU loads per thread are issued before their LDS stores (indexes past the
 // end re-read the last chunk and are not stored), so a thread waits on one
 // round trip per batch rather than one per chunk.
@@ -1161,7 +1162,7 @@ __device__ __forceinline__ void link_ops(HeadOps<ELL>& o, const Rows& X, const b
 // would write Q|K and V to HBM and read them back.  Each wave also projects
 // its user's link rows for its head (K_L, V_L, Q_L: the HeadOps operands),
 // so a layer needs no projection launch.
-// A workgroup of 8 waves holds w_qkv in LDS (rows padded by 16 bytes) and
+// A workgroup of 8 waves holds w_qkv in LDS (rows padded by 32 bytes) and
 // runs SPW = 8 / H splits with one wave per (split, head); splits and
 // partials as in xor_attn.  The H waves of a split share each chunk's LN:
 // every wave normalizes 32 / H of its rows into an LDS chunk buffer (two per
@@ -2140,8 +2141,7 @@ struct ResCfg {
   static constexpr int NW = 8;
   static constexpr int NT = 64 * NW;
   static constexpr int XS = D + 4;  // float32 row stride of the residual stream
-  // bf16 row strides of QK and Y padded by 16 bytes: the 16 rows one
-  // fragment access touches then start in distinct banks
+  // bf16 row strides of QK and Y padded by 16 bytes
   static constexpr int LQK = 2 * D + 8, LY = D + 8;
   static constexpr size_t bytes_per_row = static_cast<size_t>(XS) * 4 + LQK * 2 + D * 2 + LY * 2;
   static constexpr bool WL = D <= 64;  // weights staged in LDS
