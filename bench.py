@@ -191,11 +191,12 @@ KERNEL_SOURCES = {
 ALL_SOURCES = ("common.h", "generic_kernels.h", "lime_api.hip", "mfma_kernels.h", "user_kernels.h")
 
 
-def traffic_from_profiles(workload, kernel):
+def traffic_from_profiles(workload, kernel, last=False):
     """HBM bytes per launch of `kernel` from the committed counter summary
     profiles/<kernel>_<workload>_traffic.txt (FETCH_SIZE and WRITE_SIZE in
-    KiB per dispatch, scaled by the copy-kernel factors recorded there), or
-    None if there is none or the kernel's sources changed since it was taken."""
+    KiB per dispatch, scaled by the copy-kernel factors recorded there; with
+    `last`, a per-layer kernel's last-layer launches), or None if there is
+    none or the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -208,8 +209,11 @@ def traffic_from_profiles(workload, kernel):
         files = tuple(kv.get("sources", "").split()) or KERNEL_SOURCES.get(kernel, ALL_SOURCES)
         if kv.get("sources_sha256") != sources_sha256(files):
             return None
-        return int(float(kv["fetch_kib"]) * 1024 * float(kv["fetch_factor"])
-                   + float(kv["write_kib"]) * 1024 * float(kv["write_factor"]))
+        pre = "last_" if last else ""
+        if pre + "fetch_kib" not in kv:
+            return None
+        return int(float(kv[pre + "fetch_kib"]) * 1024 * float(kv["fetch_factor"])
+                   + float(kv[pre + "write_kib"]) * 1024 * float(kv["write_factor"]))
     except (KeyError, ValueError, OSError):
         return None
 
@@ -392,6 +396,9 @@ def main():
         if v["name"] in work:
             b, f = work[v["name"]](v["full"])
             entry.update(against_roof(b, f, t_mean, peak_tf))
+            # measured HBM bytes per launch (committed counter summary), if current
+            entry["traffic"] = traffic_from_profiles(w.name, v["name"],
+                                                     last=v["name"] in per_layer and not v["full"])
         rooflines[key] = entry
     # the MFMA ceiling of the cache build: its intensity over the MFMA ridge
     if "qk_cache" in rooflines:
