@@ -193,17 +193,31 @@ struct QkCfg {
 // Symmetric int8 codes of the values a lane holds for one (item, head): the
 // other values of the row are in lanes ^16, ^32.  scale = max|v| / 127,
 // code = round-half-even(v * 127 / max|v|); an all-zero row gets scale 0.
+// The codes come out packed, four per dword (value 4j + b in byte b of
+// q[j]).  Rounding: adding 1.5 * 2^23 to a float of magnitude at most 127
+// leaves round-half-even of it, two's complement, in the low byte of the
+// sum's bits, so one fused multiply-add per value replaces the multiply,
+// round, clamp and conversion (|v * inv| <= 127 by the choice of inv; a
+// non-finite row gets inv = 0 or a NaN product, whose low byte is 0 or
+// unspecified, never a fault).
 template <int N>
-__device__ __forceinline__ float quantize_i8(const float* v, int8_t* q) {
+__device__ __forceinline__ float quantize_i8(const float* v, uint32_t* q) {
+  static_assert(N % 4 == 0, "codes pack four per dword");
   float m = 0.f;
 #pragma unroll
   for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(v[i]));
   m = rows_max(m);
   const float inv = m > 0.f ? 127.f / m : 0.f;
+  constexpr float RND = 12582912.f;  // 1.5 * 2^23
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float c = __builtin_rintf(v[i] * inv);
-    q[i] = static_cast<int8_t>(fminf(fmaxf(c, -127.f), 127.f));
+  for (int j = 0; j < N / 4; ++j) {
+    const uint32_t b0 = __float_as_uint(fmaf(v[4 * j], inv, RND));
+    const uint32_t b1 = __float_as_uint(fmaf(v[4 * j + 1], inv, RND));
+    const uint32_t b2 = __float_as_uint(fmaf(v[4 * j + 2], inv, RND));
+    const uint32_t b3 = __float_as_uint(fmaf(v[4 * j + 3], inv, RND));
+    // byte selectors: 0x00 = low byte of the second operand, 0x04 = low
+    // byte of the first, 0x0c = zero
+    q[j] = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
   }
   return m / 127.f;
 }
@@ -247,19 +261,13 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
     for (int q = 0; q < 4 * MB; ++q) v[q] = silu2_div(v[q], c);
   }
   if constexpr (I8) {
-    int8_t qv[4 * MB];
+    static_assert(MB % 2 == 0, "int8 codes leave in 8-byte pieces");
+    uint32_t qv[MB];
     const float sc = quantize_i8<4 * MB>(v, qv);
     if (item < n_items) {
       int8_t* o = static_cast<int8_t*>(cache_out) + (item * H + head) * ELL + g * 4 * MB;
 #pragma unroll
-      for (int q = 0; q < MB / 2; ++q) {
-        uint2 pk;
-        pk.x = (uint32_t)(uint8_t)qv[8 * q] | ((uint32_t)(uint8_t)qv[8 * q + 1] << 8) |
-               ((uint32_t)(uint8_t)qv[8 * q + 2] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 3] << 24);
-        pk.y = (uint32_t)(uint8_t)qv[8 * q + 4] | ((uint32_t)(uint8_t)qv[8 * q + 5] << 8) |
-               ((uint32_t)(uint8_t)qv[8 * q + 6] << 16) | ((uint32_t)(uint8_t)qv[8 * q + 7] << 24);
-        *reinterpret_cast<uint2*>(o + 8 * q) = pk;
-      }
+      for (int q = 0; q < MB / 2; ++q) *reinterpret_cast<uint2*>(o + 8 * q) = uint2{qv[2 * q], qv[2 * q + 1]};
       if (g == 0) qscale[item * H + head] = sc;
     }
   } else if constexpr (ELL == 64) {
