@@ -117,13 +117,23 @@ def kernel_work(w, es, total_N, n_cand):
             return (R + N) * d * es, 2.0 * d * 3 * d * R + 8.0 * ell * N * d
         return R * d * es, 2.0 * d * 2 * d * N + 2.0 * d * 3 * d * nlr + 4.0 * ell * N * d
 
-    def attn_h(full):
-        # d = 256: the projection inside the attention, from the LayerNorm rows
-        # the post block stored: read those rows, write Y_E (the links' Y
-        # comes from the split combine)
+    # the link operands of every (user, head): f16 registers of one wave
+    lops_bytes = w.B * H * (2 * (ell // 16) + 2 * (ell // 32)) * 64 * 16
+
+    def link_h(full):
+        # d = 256: the link rows' Q, K, V (Q only in a links-only last layer)
+        # from their LayerNorm rows, once per user and head
         if full:
-            return (R + N) * d * es, 2.0 * d * 3 * d * R + 8.0 * ell * N * d
-        return R * d * es, 2.0 * d * 2 * d * N + 2.0 * d * 3 * d * nlr + 4.0 * ell * N * d
+            return nlr * d * es + lops_bytes, 2.0 * d * 3 * d * nlr
+        return nlr * d * es + lops_bytes / 3, 2.0 * d * d * nlr
+
+    def attn_h(full):
+        # d = 256: the history rows' projection inside the attention, from
+        # the LayerNorm rows the post block stored: read those rows and the
+        # link operands, write Y_E (the links' Y comes from the split combine)
+        if full:
+            return 2 * N * d * es + lops_bytes, 2.0 * d * 3 * d * N + 8.0 * ell * N * d
+        return N * d * es + lops_bytes / 3, 2.0 * d * 2 * d * N + 4.0 * ell * N * d
 
     def ln_rows(full):
         # the first layer's LayerNorm rows: read X, write them
@@ -156,7 +166,7 @@ def kernel_work(w, es, total_N, n_cand):
         return n_cand * (H * ell * es + d * es + 8), 2.0 * n_cand * ell * d
 
     return {"qkv_proj_stream": qkv, "qkv_proj_lds": qkv, "xor_attn": attn, "xor_attn_qkv": attn_fused,
-            "xor_attn_h": attn_h, "ln_rows": ln_rows,
+            "xor_attn_h": attn_h, "link_qkv_h": link_h, "ln_rows": ln_rows,
             "xor_combine": combine, "post_block_stream": post, "post_block_lds": post,
             "xor_fwd_resident": resident, "xor_fwd_resident_score": resident_score,
             "qk_cache": cache, "cand_score": cand}
@@ -175,16 +185,13 @@ def against_roof(bytes_, flops, seconds, peak_tflops):
             "algorithmic_bytes": int(bytes_), "algorithmic_flops": float(flops)}
 
 
-# the source files that hold each kernel's device code (their launch code in
-# lime_api.hip is unchanged since the summaries were taken):
-# a counter summary stays valid while these are unchanged
 # the files that hold each kernel's code: a traffic summary is used only while
 # their hash matches the one it records
 _USER = ("common.h", "mfma_kernels.h", "user_kernels.h")
 KERNEL_SOURCES = {
     "qk_cache": ("common.h", "mfma_kernels.h"),
     "cand_score": ("common.h", "mfma_kernels.h"),
-    **{k: _USER for k in ("xor_attn_h", "xor_attn_qkv", "xor_attn", "post_block_stream", "post_block_lds",
+    **{k: _USER for k in ("xor_attn_h", "link_qkv_h", "xor_attn_qkv", "xor_attn", "post_block_stream", "post_block_lds",
                           "qkv_proj_stream", "qkv_proj_lds", "ln_rows", "xor_combine", "xor_fwd_resident",
                           "xor_fwd_resident_score")},
 }
@@ -373,8 +380,9 @@ def main():
         log(f"trace dropped {dropped} launches")
     # each record: (name, ms, full) where full = the layer updates history
     # rows; layers are counted by the launch that opens each of them
-    opens = ("qkv_proj_stream", "qkv_proj_lds", "xor_attn_qkv", "xor_attn_h")
-    per_layer = ("xor_attn", "xor_attn_qkv", "xor_attn_h", "qkv_proj_stream", "qkv_proj_lds", "post_block_stream",
+    # (at d = 256 link_qkv_h opens a layer, xor_attn_h follows it)
+    opens = ("qkv_proj_stream", "qkv_proj_lds", "xor_attn_qkv", "link_qkv_h")
+    per_layer = ("xor_attn", "xor_attn_qkv", "xor_attn_h", "link_qkv_h", "qkv_proj_stream", "qkv_proj_lds", "post_block_stream",
                  "post_block_lds")
     per = {}
     layer = -1

@@ -201,6 +201,7 @@ struct XorPlan {
   int64_t G = 0;           // matrix-core path: split slots (an upper bound on the splits)
   size_t o_x = 0, o_qkv = 0, o_v = 0, o_y = 0, o_h = 0, o_part = 0, o_soff = 0, o_suser = 0, total = 0;
   size_t o_ln = 0;         // matrix-core path, d = 256: LayerNorm rows of the next layer [R, d]
+  size_t o_lops = 0;       // matrix-core path, d = 256: the link operands of every (user, head)
 };
 
 lime_status_t check_sizes(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t heads,
@@ -287,6 +288,9 @@ XorPlan plan_xor(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d, int32_t 
     p.o_suser = off; off = up256(off + static_cast<size_t>(p.G) * 4);
     if (d == 256) {
       p.o_ln = off;  off = up256(off + static_cast<size_t>(p.R) * d * es);
+      // f16 registers of one wave: 2 (ell / 16) + 2 (ell / 32) of 64 lanes x 16 bytes
+      const size_t nreg = static_cast<size_t>(2 * (ell / 16) + 2 * (ell / 32));
+      p.o_lops = off; off = up256(off + static_cast<size_t>(B) * heads * nreg * 1024);
     }
   } else {
     p.o_x = off;    off = up256(off + static_cast<size_t>(p.R) * d * es);
@@ -393,6 +397,7 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   const bool fused_h = D == 256 && va.half == 0 && !va.links_only;
   bf16_t* LNr = fused_h ? reinterpret_cast<bf16_t*>(ws + P.o_ln) : nullptr;
   const Rows LNrows{LNr, LNr + nlr * D, nlr, D};
+  void* lops = fused_h ? ws + P.o_lops : nullptr;
   // the splits of every layer's attention
   LIME_LAUNCH("split_plan", mfma::split_plan, dim3(1), dim3(mfma::SPLIT_PLAN_NT), 0, st, off, B, total_N, P.chunk,
                      soff, suser, static_cast<int>(P.G));
@@ -462,6 +467,8 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
           // (the same signature for both forms: each sets its own LDS limit)
           auto kf = mfma::xor_attn_h<ELL, false, true>;
           auto kl = mfma::xor_attn_h<ELL, false, false>;
+          auto pf = mfma::link_qkv_h<ELL, true>;
+          auto pl = mfma::link_qkv_h<ELL, false>;
           static const bool attr_f = hipFuncSetAttribute(reinterpret_cast<const void*>(kf),
                                                          hipFuncAttributeMaxDynamicSharedMemorySize,
                                                          static_cast<int>(FC::lds_bytes)) == hipSuccess;
@@ -476,9 +483,14 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
                         st, Xin, R, LNr);
             LIME_CHECK_LAUNCH("layer-0 LayerNorm rows");
           }
+          // the link operands once per (user, head), then the attention
+          const int64_t pgrid = full ? mfma::LinkQkvCfg<ELL, true>::grid(B) : mfma::LinkQkvCfg<ELL, false>::grid(B);
+          LIME_LAUNCH("link_qkv_h", full ? pf : pl, dim3(static_cast<unsigned>(pgrid)), dim3(64), 0, st, LNrows,
+                      static_cast<const bf16_t*>(w[l].w_qkv), lops, qs);
+          LIME_CHECK_LAUNCH("link operands (d = 256)");
           LIME_LAUNCH("xor_attn_h", full ? kf : kl, dim3(static_cast<unsigned>(FC::grid(P.G))), dim3(64 * FC::NW),
-                      FC::lds_bytes, st, LNrows, static_cast<const bf16_t*>(w[l].w_qkv), Y, part, off, soff, suser,
-                      B, static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi), qs);
+                      FC::lds_bytes, st, LNrows, static_cast<const bf16_t*>(w[l].w_qkv), lops, Y, part, off, soff,
+                      suser, B, static_cast<int>(P.G), P.chunk, total_N, static_cast<int>(phi));
         }
       } else if (fused) {
         if constexpr (D <= 128) {
@@ -762,11 +774,12 @@ int32_t lime_xor_fwd_plan(lime_dtype_t dtype, int32_t B, int32_t ell, int32_t d,
              "combine, post); splits of %lld history rows, at most %lld splits",
              static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else if (P.mfma) {
-    launches = 3 * layers + 2;
+    launches = 4 * layers + 2;
     snprintf(line, sizeof(line),
-             "streaming matrix-core: a split plan and the first layer's LayerNorm rows, then 3 launches per "
-             "layer (xor_attn_h: the attention with the projection fused in, from LayerNorm rows the post block stores; "
-             "combine; post); splits of %lld history rows, at most %lld splits",
+             "streaming matrix-core: a split plan and the first layer's LayerNorm rows, then 4 launches per "
+             "layer (link_qkv_h: the link rows' Q, K, V once per user and head; xor_attn_h: the attention with the "
+             "history rows' projection fused in, from LayerNorm rows the post block stores; combine; post); "
+             "splits of %lld history rows, at most %lld splits",
              static_cast<long long>(P.chunk), static_cast<long long>(P.G));
   } else {
     launches = 6 * layers;

@@ -1071,25 +1071,22 @@ __device__ __forceinline__ void ln_operands(const Rows& X, F&& row_of, int g, bf
   for (int rb = 0; rb < 2; ++rb) ln_bf16<KB>(xv[rb], D, hb[rb]);
 }
 
-// Q or K of head part p (p < H: Q, else K), multiplied by f, for the two row
-// blocks of hb, in the transposed form: out[rb] lane (r, g) holds features
-// 8g .. 8g+7 of the row that hb[rb] lane r carries.  W: w_qkv rows in LDS
-// with row stride ldw, placed by wqkv_slot.
-template <int D>
-__device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
-                                             float f, int r, int g, f16x8 (&out)[2]) {
+// The products of the two projections below, with the weight fragments
+// from wf: wf(c, kb) for Q or K (row 8 (r / 4) + 4 c + r % 4 of the head
+// part, columns 32 kb + 8 g ..), wf(kb) for V.  FENCE keeps the fragments
+// in flight bounded at d = 256 (registers) where wf loads them.
+template <int D, bool FENCE, typename WF>
+__device__ __forceinline__ void qk_products(const bf16x8 (&hb)[2][D / 32], WF&& wf, float f, f16x8 (&out)[2]) {
   constexpr int KB = D / 32;
   floatx4 acc[2][2] = {};
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const bf16_t* wr = W + wqkv_slot(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 a = ld16(wr + kb * 32);
+      const bf16x8 a = wf(c, kb);
       acc[c][0] = mma(a, hb[0][kb], acc[c][0]);
       acc[c][1] = mma(a, hb[1][kb], acc[c][1]);
-      // at d = 256 keep the weight fragments in flight bounded (registers)
-      if constexpr (KB > 4) {
+      if constexpr (KB > 4 && FENCE) {
         if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1102,26 +1099,43 @@ __device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], cons
   }
 }
 
+template <int D, bool FENCE, typename WF>
+__device__ __forceinline__ f16x8 v_products(const bf16x8 (&hb)[2][D / 32], WF&& wf) {
+  constexpr int KB = D / 32;
+  floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const bf16x8 bq = wf(kb);
+    a0 = mma(hb[0][kb], bq, a0);
+    a1 = mma(hb[1][kb], bq, a1);
+    if constexpr (KB > 4 && FENCE) {
+      if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  return packh8(v);
+}
+
+// Q or K of head part p (p < H: Q, else K), multiplied by f, for the two row
+// blocks of hb, in the transposed form: out[rb] lane (r, g) holds features
+// 8g .. 8g+7 of the row that hb[rb] lane r carries.  W: w_qkv rows in LDS
+// with row stride ldw, placed by wqkv_slot.
+template <int D>
+__device__ __forceinline__ void proj_qk_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw, int p,
+                                             float f, int r, int g, f16x8 (&out)[2]) {
+  qk_products<D, true>(hb, [&](int c, int kb) {
+    return ld16(W + wqkv_slot(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * ldw + 8 * g + kb * 32);
+  }, f, out);
+}
+
 // V of two 16-row blocks whose rows are in the projection order (block rb,
 // lane r: row 8*(r/4) + 4*rb + r%4), operands swapped: lane (r, g) ends with
 // V of rows 8g .. 8g+7 for column `col_of(r)` of w_qkv's V part.
 template <int D, typename F>
 __device__ __forceinline__ f16x8 proj_v_regs(const bf16x8 (&hb)[2][D / 32], const bf16_t* W, int ldw,
                                               F&& col_of, int r, int g, int vrow0 = 2 * D) {
-  constexpr int KB = D / 32;
   const bf16_t* wr = W + wqkv_slot(vrow0 + col_of(r)) * ldw + 8 * g;
-  floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-    const bf16x8 bq = ld16(wr + kb * 32);
-    a0 = mma(hb[0][kb], bq, a0);
-    a1 = mma(hb[1][kb], bq, a1);
-    if constexpr (KB > 4) {
-      if (kb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-  return packh8(v);
+  return v_products<D, true>(hb, [&](int kb) { return ld16(wr + kb * 32); });
 }
 
 // The link operands of user b and head h (the HeadOps layouts) computed
@@ -1355,8 +1369,9 @@ __global__ __launch_bounds__(512) void xor_attn_qkv(Rows X, const bf16_t* __rest
 // whose w_qkv (384 KB) LDS cannot hold: a workgroup serves SPW = 4 splits
 // and a group of HG = 2 heads, with those heads' 192 rows of w_qkv staged in
 // LDS (Q rows, then K rows, then V rows, 32 per head); one wave per (split,
-// head) projects its user's link rows and each 32-row chunk of its split
-// itself, so Q, K and V never leave the registers.  The rows come from Hs,
+// head) loads its user's link operands (projected once per user and head by
+// link_qkv_h) and projects each 32-row chunk of its split itself, so the
+// history rows' Q, K and V never leave the registers.  The rows come from Hs,
 // LayerNorm(X) of every row that the previous layer's post block stored as
 // bf16 (LNX = false), or, in the first layer, from X normalised here
 // (LNX = true).  Each head group reads a split's rows once; block indices
@@ -1392,29 +1407,79 @@ __device__ __forceinline__ void row_operands(const Rows& src, F&& row_of, int g,
   }
 }
 
-// link operands of user b for head slot j of the staged head group (Q rows
-// at 32 j, K rows at 32 (HG + j), V rows at 32 (2 HG + j) of W); as link_ops
-template <int ELL, int D, int HG, bool LNX>
-__device__ __forceinline__ void link_ops_hg(HeadOps<ELL>& o, const Rows& src, const bf16_t* W, int ldw, int b,
-                                            int j, int r, int g, float qs) {
-  const int64_t l0 = static_cast<int64_t>(b) * ELL;
+// Link operands of xor_attn_h, projected once per (user, head) instead of
+// by every split of the user: the HeadOps registers of one wave, stored
+// lane-major.  Register k of lane t of (user b, head h) is element
+// ((b H + h) NREG + k) 64 + t, in the order kl[0..MB), qlt[0..MB),
+// vlt[0][0..KBL), vlt[1][0..KBL): each split's waves then load them with one
+// coalesced 16-byte load per register.
+template <int ELL>
+struct LinkOpsLayout {
+  static constexpr int MB = ELL / 16, KBL = ELL / 32, NREG = 2 * MB + 2 * KBL;
+  static constexpr int KL = 0, QLT = MB, VLT = 2 * MB;
+};
+
+// One wave per (user, head, job), each job one 32-link block: K_L and V_L
+// from its rows in the projection order, or Q_L from its rows in natural
+// order (without DO_E, a last layer, only Q_L is used).  The weight
+// fragments come straight from w_qkv in global memory (384 KB, L2-resident
+// after the first of the 8 XCDs' reads): a workgroup that staged them in
+// LDS first would spend most of its time on that.  Both Q_L and K_L carry
+// the logit scale qs (the history rows' Q and K are left unscaled, and
+// each branch's scores come out in log2 units).
+template <int ELL, bool DO_E>
+struct LinkQkvCfg {
+  static constexpr int KBL = ELL / 32, JOBS = DO_E ? 2 * KBL : KBL;
+  static constexpr int64_t grid(int B) { return static_cast<int64_t>(B) * 8 * JOBS; }
+};
+
+template <int ELL, bool DO_E>
+__global__ __launch_bounds__(64) void link_qkv_h(Rows src, const bf16_t* __restrict__ W, void* __restrict__ ops_,
+                                                 float qs) {
+  using LO = LinkOpsLayout<ELL>;
+  constexpr int D = 256, H = 8, KBL = LO::KBL, JOBS = LinkQkvCfg<ELL, DO_E>::JOBS;
+  const int job = static_cast<int>(blockIdx.x % JOBS) + (DO_E ? 0 : KBL);
+  const int h = static_cast<int>((blockIdx.x / JOBS) % H), b = static_cast<int>(blockIdx.x / (JOBS * H));
+  const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
+  f16x8* rec = static_cast<f16x8*>(ops_) + (static_cast<int64_t>(b) * H + h) * LO::NREG * 64 + lane;
+  // jobs [0, KBL): K_L and V_L of link block kb2 = job; [KBL, 2 KBL): Q_L.
+  // Every operand is loaded before the first product (one memory latency;
+  // the fused kernels load weight fragments as they go, from LDS).
+  constexpr int KB = D / 32;
+  const int kb2 = job < KBL ? job : job - KBL;
+  const int64_t l0 = static_cast<int64_t>(b) * ELL + 32 * kb2;
+  bf16x8 hb[2][KB];
+  bf16x8 wa[2][KB];
+  const int p = job < KBL ? H + h : h;
 #pragma unroll
-  for (int kb2 = 0; kb2 < ELL / 32; ++kb2) {
-    bf16x8 hb[2][D / 32];
-    row_operands<D, LNX>(src, [&](int rb) { return l0 + kb2 * 32 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
-    f16x8 k2[2];
-    proj_qk_regs<D>(hb, W, ldw, HG + j, qs, r, g, k2);
-    o.kl[2 * kb2] = k2[0];
-    o.kl[2 * kb2 + 1] = k2[1];
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      wa[c][kb] = ld16(W + static_cast<int64_t>(32 * p + 8 * (r >> 2) + 4 * c + (r & 3)) * D + 8 * g + 32 * kb);
+  if (job < KBL) {
+    row_operands<D, false>(src, [&](int rb) { return l0 + 8 * (r >> 2) + 4 * rb + (r & 3); }, g, hb);
+    bf16x8 wv[2][KB];
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
-      o.vlt[c2][kb2] = proj_v_regs<D>(hb, W, ldw, [&](int rr) { return 32 * j + 8 * (rr >> 2) + 4 * c2 + (rr & 3); },
-                                      r, g, 2 * HG * 32);
-    row_operands<D, LNX>(src, [&](int rb) { return l0 + kb2 * 32 + 16 * rb + r; }, g, hb);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        wv[c2][kb] = ld16(W + static_cast<int64_t>(2 * D + 32 * h + 8 * (r >> 2) + 4 * c2 + (r & 3)) * D + 8 * g +
+                          32 * kb);
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 k2[2];
+    qk_products<D, false>(hb, [&](int c, int kb) { return wa[c][kb]; }, qs, k2);
+    rec[(LO::KL + 2 * kb2) * 64] = k2[0];
+    rec[(LO::KL + 2 * kb2 + 1) * 64] = k2[1];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+      rec[(LO::VLT + c2 * KBL + kb2) * 64] = v_products<D, false>(hb, [&](int kb) { return wv[c2][kb]; });
+  } else {
+    row_operands<D, false>(src, [&](int rb) { return l0 + 16 * rb + r; }, g, hb);
+    __builtin_amdgcn_sched_barrier(0);
     f16x8 q2[2];
-    proj_qk_regs<D>(hb, W, ldw, j, qs, r, g, q2);
-    o.qlt[2 * kb2] = q2[0];
-    o.qlt[2 * kb2 + 1] = q2[1];
+    qk_products<D, false>(hb, [&](int c, int kb) { return wa[c][kb]; }, qs, q2);
+    rec[(LO::QLT + 2 * kb2) * 64] = q2[0];
+    rec[(LO::QLT + 2 * kb2 + 1) * 64] = q2[1];
   }
 }
 
@@ -1457,11 +1522,11 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(Rows X, int64_t R, bf16_t*
 // second operand buffer: the rows are loaded two chunks ahead.
 template <int ELL, bool LNX, bool DO_E>
 __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __restrict__ W,
-                                                  bf16_t* __restrict__ Y, float* __restrict__ part,
-                                                  const int64_t* __restrict__ off,
+                                                  const void* __restrict__ lops, bf16_t* __restrict__ Y,
+                                                  float* __restrict__ part, const int64_t* __restrict__ off,
                                                   const int32_t* __restrict__ split_off,
                                                   const int32_t* __restrict__ split_user, int B, int G,
-                                                  int64_t chunk, int64_t total_N, int phi, float qs) {
+                                                  int64_t chunk, int64_t total_N, int phi) {
   using C = FusedHCfg<ELL>;
   constexpr int D = C::D, H = C::H, HG = C::HG, SPW = C::SPW, NHG = C::NHG, MB = ELL / 16, LDW = C::LDW;
   // block -> (split group, head group): the NHG head groups of a split
@@ -1476,9 +1541,10 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* Wl = reinterpret_cast<bf16_t*>(smem);
-  // the head group's rows of w_qkv: Q, K, V parts, HG * 32 rows each
+  // the head group's rows of w_qkv: Q, K, V parts, HG * 32 rows each (the
+  // history rows' Q only where they are updated)
 #pragma unroll
-  for (int part3 = 0; part3 < 3; ++part3)
+  for (int part3 = DO_E ? 0 : 1; part3 < 3; ++part3)
     stage_rows<true, LDW - D>(Wl + part3 * HG * 32 * LDW, W + (static_cast<int64_t>(part3) * D + hgi * HG * 32) * D, HG * 32, D,
                threadIdx.x, C::NW * 64);
   lds_barrier();
@@ -1501,8 +1567,24 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
   const bool softmax = (phi == PHI_SOFTMAX);
   const bf16_t* Wb = Wl + opaque_zero();
 
+  // the user's link operands for head h, from link_qkv_h (without DO_E
+  // only Q_L is live)
   HeadOps<ELL> o;
-  link_ops_hg<ELL, D, HG, LNX>(o, src, Wb, LDW, b, j, r, g, qs);
+  {
+    using LO = LinkOpsLayout<ELL>;
+    const f16x8* rec = static_cast<const f16x8*>(lops) + (static_cast<int64_t>(b) * H + h) * LO::NREG * 64 + lane;
+#pragma unroll
+    for (int c = 0; c < MB; ++c) {
+      if constexpr (DO_E) o.kl[c] = rec[(LO::KL + c) * 64];
+      o.qlt[c] = rec[(LO::QLT + c) * 64];
+    }
+    if constexpr (DO_E) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int kb = 0; kb < LO::KBL; ++kb) o.vlt[c2][kb] = rec[(LO::VLT + c2 * LO::KBL + kb) * 64];
+    }
+  }
   LState<ELL> st;
   st.init();
   const Lay yl{32, (nlr + total_N) * 32};
