@@ -261,6 +261,36 @@ def test_xor_fwd_ragged_empty_and_odd_shapes(L, dt, phi):
         assert_close(host_f64(ho), np.concatenate(href), dt, f"hist_out odd {B,ell,d,H} {dt} {phi}")
 
 
+@pytest.mark.parametrize("ell", [32, 64])
+@pytest.mark.parametrize("want_hist", [False, True])
+def test_xor_fwd_d256_many_users(L, ell, want_hist):
+    """d = 256 with many users: the link rows' Q, K, V are projected once
+    per (user, head) and every split of the user reads them; 37 users with
+    ragged lengths (empty, single-row, and lengths around the split size)
+    put users at every offset of a split group.  Two layers: a full one,
+    then the last one links-only (without hist_out) or full (with it)."""
+    rng = np.random.default_rng(11 + ell)
+    B, d, H, layers = 37, 256, 8, 2
+    lens = [int(x) for x in rng.integers(0, 300, B)]
+    lens[0], lens[5], lens[17] = 0, 1, 64
+    off = W.offsets_from_lengths(lens)
+    lc = W.as_storage(rng.standard_normal((B, ell, d)).astype(np.float32), "bf16")
+    hs = W.as_storage((rng.standard_normal((int(off[-1]), d)) * 0.5).astype(np.float32), "bf16")
+    ws = [{k: W.as_storage((rng.standard_normal(s) * s[1] ** -0.5).astype(np.float32), "bf16")
+           for k, s in (("w_qkv", (3 * d, d)), ("w_o", (d, d)), ("w_gate", (d, d)), ("w_up", (d, d)),
+                        ("w_down", (d, d)))} for _ in range(layers)]
+    scale = (d // H) ** -0.5
+    print(f"xor_fwd d=256 B={B} ell={ell} total_N={int(off[-1])} want_hist={want_hist}", flush=True)
+    for phi in ("softmax", "silu_mean"):
+        lp, ho = L.xor_fwd(dev(lc), dev(hs), dev(off), dev_weights(ws), heads=H, phi=phi, scale=scale,
+                           max_N=int(max(lens)), want_hist=want_hist)
+        torch.cuda.synchronize()
+        ref, href = O.xor_fwd(lc, hs, off, ws, H, scale, phi)
+        assert_close(host_f64(lp), ref, "bf16", f"L^P d=256 B={B} ell={ell} {phi}")
+        if want_hist:
+            assert_close(host_f64(ho), np.concatenate(href), "bf16", f"hist_out d=256 B={B} ell={ell} {phi}")
+
+
 def test_xor_fwd_max_n_too_small_stays_in_bounds(L):
     """max_N below the real maximum breaks the precondition: the call must
     still finish without fault and leave finite outputs."""
