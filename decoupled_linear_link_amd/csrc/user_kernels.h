@@ -1422,22 +1422,22 @@ struct LinkOpsLayout {
 // One wave per (user, head, job), each job one 32-link block: K_L and V_L
 // from its rows in the projection order, or Q_L from its rows in natural
 // order (without DO_E, a last layer, only Q_L is used).  The weight
-// fragments come straight from w_qkv in global memory (384 KB, L2-resident
-// after the first of the 8 XCDs' reads): a workgroup that staged them in
-// LDS first would spend most of its time on that.  Both Q_L and K_L carry
+// fragments come straight from w_qkv in global memory (384 KB, read into
+// each XCD's L2 once): a workgroup that staged them in LDS first would
+// spend most of its time on that.  Both Q_L and K_L carry
 // the logit scale qs (the history rows' Q and K are left unscaled, and
 // each branch's scores come out in log2 units).
 template <int ELL, bool DO_E>
 struct LinkQkvCfg {
   static constexpr int KBL = ELL / 32, JOBS = DO_E ? 2 * KBL : KBL;
-  static constexpr int64_t grid(int B) { return static_cast<int64_t>(B) * 8 * JOBS; }
+  static constexpr int64_t grid(int B) { return static_cast<int64_t>(B) * FusedHCfg<ELL>::H * JOBS; }
 };
 
 template <int ELL, bool DO_E>
 __global__ __launch_bounds__(64) void link_qkv_h(Rows src, const bf16_t* __restrict__ W, void* __restrict__ ops_,
                                                  float qs) {
   using LO = LinkOpsLayout<ELL>;
-  constexpr int D = 256, H = 8, KBL = LO::KBL, JOBS = LinkQkvCfg<ELL, DO_E>::JOBS;
+  constexpr int D = FusedHCfg<ELL>::D, H = FusedHCfg<ELL>::H, KBL = LO::KBL, JOBS = LinkQkvCfg<ELL, DO_E>::JOBS;
   const int job = static_cast<int>(blockIdx.x % JOBS) + (DO_E ? 0 : KBL);
   const int h = static_cast<int>((blockIdx.x / JOBS) % H), b = static_cast<int>(blockIdx.x / (JOBS * H));
   const int lane = threadIdx.x, g = lane >> 4, r = lane & 15;
