@@ -1939,6 +1939,33 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_stream(Rows X, int64_t R, int
   }
 }
 
+// The 32 products of one chunk and wave as 4 groups of 8 (fragment read
+// from LDS, product): group g + 1's 8 reads are issued after group g's
+// first two products, so a wave keeps 6 to 14 reads in flight while its
+// products run instead of waiting one LDS round trip per product.  The
+// products of a group alternate between two accumulators.
+template <typename FragOf, typename Mul>
+__device__ __forceinline__ void chunk_products(FragOf&& frag_of, Mul&& mul) {
+  bf16x8 buf[2][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) buf[0][j] = frag_of(0, j);
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) {
+    __builtin_amdgcn_sched_barrier(0);
+    mul(grp, 0, buf[grp & 1][0]);
+    mul(grp, 1, buf[grp & 1][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp < 3) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) buf[(grp + 1) & 1][j] = frag_of(grp + 1, j);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 2; j < 8; ++j) mul(grp, j, buf[grp & 1][j]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Post-attention block, weights streamed: 16 chunks of 64 weight rows per
 // step: 0..3 w_o (two column pairs each), 4..11 gate/up (32 rows of each:
 // one pair), 12..15 w_down (two pairs each).  One wave of eight owns a
@@ -2077,27 +2104,26 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
       if (!active) {
         // no block this step: stream and wait only
       } else if (k < 4 || k >= 12) {
-        // x1 += (Y or M) W^T for column pairs 2k', 2k'+1
+        // x1 += (Y or M) W^T for column pairs 2k', 2k'+1.  Group (pp, kh):
+        // k-slices 4 kh .. +4 of both column halves cc, alternating
         const int kk = k < 4 ? k : k - 12;
+        floatx4 acc[2][2] = {};
+        chunk_products(
+            [&](int grp, int j) {
+              return frag(wb, 32 * (grp >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3), 4 * (grp & 1) + (j >> 1));
+            },
+            [&](int grp, int j, const bf16x8& f) {
+              const int kb = 4 * (grp & 1) + (j >> 1);
+              acc[grp >> 1][j & 1] = mma(f, k < 4 ? yb[0][kb] : mb[kb], acc[grp >> 1][j & 1]);
+            });
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          floatx4 acc[2] = {};
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const int wrow = 32 * pp + 8 * (r >> 2) + 4 * cc + (r & 3);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-              acc[cc] = mma(frag(wb, wrow, kb), k < 4 ? yb[0][kb] : mb[kb], acc[cc]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
           const int p = 2 * kk + pp;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            x1[0][8 * p + q] += acc[0][q];
-            x1[0][8 * p + 4 + q] += acc[1][q];
+            x1[0][8 * p + q] += acc[pp][0][q];
+            x1[0][8 * p + 4 + q] += acc[pp][1][q];
           }
-          // bound the fragment loads the scheduler keeps in flight
-          __builtin_amdgcn_sched_barrier(0);
         }
         if (k == 3) {
           // the residual: x1 = X + Y W_o^T (one addition per element, the
@@ -2114,21 +2140,20 @@ __global__ __launch_bounds__(512) void post_block_stream(const bf16_t* __restric
           for (int kb = 0; kb < KB; ++kb) gb[kb] = pack8(t + 8 * kb);
         }
       } else {
-        // gate/up column pair q2 = k - 4: rows [0,32) gate, [32,64) up
+        // gate/up column pair q2 = k - 4: rows [0,32) gate, [32,64) up.
+        // Group (cc, kh): k-slices 4 kh .. +4 of gate and up, alternating
         floatx4 ag[2] = {}, au[2] = {};
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int orow = 8 * (r >> 2) + 4 * cc + (r & 3);
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-            for (int kb = kh * KB / 2; kb < (kh + 1) * KB / 2; ++kb) {
-              ag[cc] = mma(frag(wb, orow, kb), gb[kb], ag[cc]);
-              au[cc] = mma(frag(wb, 32 + orow, kb), gb[kb], au[cc]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
+        chunk_products(
+            [&](int grp, int j) {
+              return frag(wb, 32 * (j & 1) + 8 * (r >> 2) + 4 * (grp >> 1) + (r & 3), 4 * (grp & 1) + (j >> 1));
+            },
+            [&](int grp, int j, const bf16x8& f) {
+              const int kb = 4 * (grp & 1) + (j >> 1);
+              if (j & 1)
+                au[grp >> 1] = mma(f, gb[kb], au[grp >> 1]);
+              else
+                ag[grp >> 1] = mma(f, gb[kb], ag[grp >> 1]);
+            });
         float v[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
