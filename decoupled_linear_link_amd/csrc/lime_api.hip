@@ -122,6 +122,25 @@ template <int ELL, int D, int H, bool I8>
 lime_status_t launch_qk_mfma(const void* items, const void* keys, void* cache, float* qscale,
                              int64_t n_items, float scale, int phi, hipStream_t st) {
   using C = mfma::QkCfg<ELL, D, H, I8>;
+  if constexpr (!I8) {
+    // bf16: item tiles by LDS-DMA, two in flight per workgroup
+    using Q = mfma::QkDmaCfg<ELL, D, H>;
+    auto k = mfma::qk_cache_dma<ELL, D, H>;
+    constexpr size_t lds = Q::lds_bytes;
+    static const bool attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(lds)) == hipSuccess;
+    (void)attr;
+    static const int per_cu = blocks_per_cu_lds(k, C::NT, lds);
+    const int64_t ntiles = (n_items + C::TI - 1) / C::TI;
+    int64_t grid = static_cast<int64_t>(cu_count()) * per_cu;
+    if (grid > ntiles) grid = ntiles;
+    LIME_LAUNCH("qk_cache", k, dim3(static_cast<unsigned>(grid)), dim3(C::NT), lds, st,
+                       static_cast<const bf16_t*>(items), static_cast<const bf16_t*>(keys),
+                       static_cast<bf16_t*>(cache), n_items, scale, phi, ntiles);
+    LIME_CHECK_LAUNCH("qk cache build (mfma)");
+    return ok();
+  }
   auto k = mfma::qk_cache<ELL, D, H, I8>;
   static const int per_cu = blocks_per_cu(k, C::NT);
   const int64_t ntiles = (n_items + C::TI - 1) / C::TI;

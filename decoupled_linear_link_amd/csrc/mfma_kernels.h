@@ -155,6 +155,38 @@ __device__ __forceinline__ void st8(bf16_t* p, const float* v) {
 }
 
 // ---------------------------------------------------------------------------
+// LDS-DMA (global -> LDS buffer loads) and counted waits
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// wait until at most n of this wave's vector memory operations are
+// outstanding (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15)
+  // at their maxima, so only vector memory is waited for
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for waves that only read the LDS buffers which their
+// own LDS-DMA loads fill: each wave has already waited (vmcnt) for its
+// loads, so the barrier needs no memory fence; a fence would make the
+// compiler wait for every LDS-DMA load in flight, including chunks loaded
+// ahead.  The compiler-only fences keep LDS reads on their side of it.
+__device__ __forceinline__ void dma_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A raw buffer descriptor over `bytes` bytes at p (raw 32-bit offsets, no
+// stride): loads past the extent return 0, stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// ---------------------------------------------------------------------------
 // QK cache build.  Per item m and head h:  cache[m,h,:] = phi(scale * K_h T_m)
 // GEMM in transposed form: A = link keys (rows = links of a head, K = d),
 // B = item rows (cols = 16 items, K = d), D = logits [links x items].
@@ -224,17 +256,13 @@ __device__ __forceinline__ float quantize_i8(const float* v, uint32_t* q) {
 
 // phi over the ell links of one (item, head) whose scores a lane group
 // holds (lane (r, g): item r, links 4 MB g .. +4 MB in acc[c][j], link order
-// of the cache kernels' A operands), then the store of the lane's links:
-// bf16 weights, or int8 codes plus the row's float32 scale.
-template <int ELL, bool I8>
-__device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], float scale, int phi, int64_t item,
-                                               int64_t n_items, int H, int head, void* __restrict__ cache_out,
-                                               float* __restrict__ qscale, int g, int64_t item0,
-                                               bf16_t* stage) {
+// of the cache kernels' A operands), into v (4 MB values per lane).
+template <int ELL>
+__device__ __forceinline__ void cache_phi(const floatx4 (&acc)[ELL / 16], float scale, int phi,
+                                          float (&v)[ELL / 4]) {
   constexpr int MB = ELL / 16;
   // logits in log2 units
   const float k = scale * LOG2E;
-  float v[4 * MB];
 #pragma unroll
   for (int c = 0; c < MB; ++c)
 #pragma unroll
@@ -260,6 +288,18 @@ __device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], f
 #pragma unroll
     for (int q = 0; q < 4 * MB; ++q) v[q] = silu2_div(v[q], c);
   }
+}
+
+// cache_phi, then the store of the lane's links: bf16 weights, or int8
+// codes plus the row's float32 scale.
+template <int ELL, bool I8>
+__device__ __forceinline__ void cache_epilogue(const floatx4 (&acc)[ELL / 16], float scale, int phi, int64_t item,
+                                               int64_t n_items, int H, int head, void* __restrict__ cache_out,
+                                               float* __restrict__ qscale, int g, int64_t item0,
+                                               bf16_t* stage) {
+  constexpr int MB = ELL / 16;
+  float v[4 * MB];
+  cache_phi<ELL>(acc, scale, phi, v);
   if constexpr (I8) {
     static_assert(MB % 2 == 0, "int8 codes leave in 8-byte pieces");
     uint32_t qv[MB];
@@ -374,6 +414,156 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H, I8>::NT)) void qk_cache(
     }
     lds_barrier();
   }
+}
+
+// The bf16 QK cache build with two item tiles in flight per workgroup: tiles
+// travel global -> LDS by LDS-DMA loads (16 bytes per lane, no registers)
+// into three buffers, so tiles t + 1 and t + 2 load while tile t is
+// computed; one barrier per tile.  Rows are unpadded, with their 16-byte
+// slots XOR-swizzled by the row's low bits so that a fragment read (16
+// consecutive rows, one slot each) meets distinct banks.  Each tile has its
+// own buffer descriptors for the item rows it reads and the cache rows it
+// writes: rows past the catalogue load as 0 and their stores are dropped,
+// so every wave issues the same loads and stores for every tile and the
+// counted waits stay exact.  Products, phi and the order of the stored
+// values are those of qk_cache.
+template <int ELL, int D, int H>
+struct QkDmaCfg {
+  using C = QkCfg<ELL, D, H, false>;
+  static constexpr int NBUF = 3;
+  static constexpr int ROWB = D * 2;                            // bytes per item row
+  static constexpr int TB = C::TI * ROWB;                       // bytes per tile
+  static constexpr int SPR = ROWB / 16;                         // 16-byte slots per row
+  static constexpr int LPT = TB / (16 * C::NT);                 // DMA loads per thread and tile
+  static constexpr int OROWB = H * ELL * 2;                     // cache bytes per item
+  // stores per wave and tile: two per (16-item block, head) at ell = 64
+  // (whole lines through the wave's staging rows), MB / 2 otherwise
+  static constexpr int SPW = C::NBW * C::HPW * (ELL == 64 ? 2 : C::MB / 2);
+  static constexpr int STG = ELL == 64 ? 16 * 72 : 8;           // staging bf16 per wave
+  static constexpr size_t lds_bytes = static_cast<size_t>(NBUF) * TB + static_cast<size_t>(C::NW) * STG * 2;
+  static_assert(TB % (16 * C::NT) == 0, "tile load split");
+  static_assert(2 * SPW + LPT < 64, "vmcnt");
+};
+
+__device__ __forceinline__ int qk_swz(int row, int spr) { return row & (spr < 16 ? spr - 1 : 15); }
+
+template <int ELL, int D, int H>
+__global__ __launch_bounds__((QkCfg<ELL, D, H, false>::NT)) void qk_cache_dma(
+    const bf16_t* __restrict__ items, const bf16_t* __restrict__ keys, bf16_t* __restrict__ cache_out,
+    int64_t n_items, float scale, int phi, int64_t ntiles) {
+  using C = QkCfg<ELL, D, H, false>;
+  using Q = QkDmaCfg<ELL, D, H>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* const stage = reinterpret_cast<bf16_t*>(smem + Q::NBUF * Q::TB);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  bf16_t* const stage_w = stage + w * Q::STG;
+  const int g = lane >> 4, r = lane & 15;
+  const int head0 = (C::WPH > 1) ? (w / C::WPH) : w * C::HPW;
+  const int nb0 = (C::WPH > 1) ? (w % C::WPH) * C::NBW : 0;
+
+  // link keys of this wave's heads, as A fragments
+  bf16x8 a[C::HPW][C::MB][C::KB];
+#pragma unroll
+  for (int hh = 0; hh < C::HPW; ++hh)
+#pragma unroll
+    for (int c = 0; c < C::MB; ++c) {
+      const int link = (r >> 2) * (4 * C::MB) + 4 * c + (r & 3);
+      const bf16_t* kr = keys + (static_cast<int64_t>(head0 + hh) * ELL + link) * D + 8 * g;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) a[hh][c][kb] = ld16(kr + kb * 32);
+    }
+
+  // rows of tile t that exist (0 past the last tile)
+  auto tile_rows = [&](int64_t t) {
+    const int64_t left = n_items - t * C::TI;
+    return left <= 0 ? 0 : (left < C::TI ? static_cast<int>(left) : C::TI);
+  };
+  // tile t into buffer b: load i of this thread fills slot e = i NT + tid
+  // of the buffer (row e / SPR, swizzled slot e % SPR)
+  auto issue_tile = [&](int64_t t, int b) {
+    const int nrow = tile_rows(t);
+    const __amdgpu_buffer_rsrc_t rs =
+        bytes_rsrc(items + (nrow > 0 ? t * C::TI * D : 0), static_cast<uint32_t>(nrow) * Q::ROWB);
+#pragma unroll
+    for (int i = 0; i < Q::LPT; ++i) {
+      const int e = i * C::NT + tid;
+      const int row = e / Q::SPR, ps = e % Q::SPR;
+      const unsigned vo = static_cast<unsigned>(row * Q::ROWB + (ps ^ qk_swz(row, Q::SPR)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(smem + b * Q::TB + (i * C::NT + wu * 64) * 16), 16,
+                                               vo, 0, 0, 0);
+    }
+  };
+
+  const int64_t G = gridDim.x;
+  int64_t tile = blockIdx.x;
+  issue_tile(tile, 0);
+  issue_tile(tile + G, 1);
+  int b = 0;
+  for (int it = 0; tile < ntiles; tile += G, ++it) {
+    // this tile's loads have landed: after them this wave issued the next
+    // tile's loads and the stores of the previous two tiles (exact counts)
+    if (it == 0) wait_vm<Q::LPT>();
+    else if (it == 1) wait_vm<Q::LPT + Q::SPW>();
+    else wait_vm<Q::LPT + 2 * Q::SPW>();
+    dma_barrier();  // every wave's part of this tile; every wave has left tile - G's buffer
+    issue_tile(tile + 2 * G, b == 0 ? 2 : b - 1);
+    const char* const buf = smem + b * Q::TB;
+    const int nrow = tile_rows(tile);
+    const __amdgpu_buffer_rsrc_t ro =
+        bytes_rsrc(cache_out + tile * C::TI * (H * ELL), static_cast<uint32_t>(nrow) * Q::OROWB);
+#pragma unroll
+    for (int nbi = 0; nbi < C::NBW; ++nbi) {
+      const int nb = nb0 + nbi;
+      const int row = nb * 16 + r;
+      const int sw = qk_swz(row, Q::SPR);
+      bf16x8 bf[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+        bf[kb] = *reinterpret_cast<const bf16x8*>(buf + row * Q::ROWB + ((kb * 4 + g) ^ sw) * 16);
+#pragma unroll
+      for (int hh = 0; hh < C::HPW; ++hh) {
+        floatx4 acc[C::MB];
+#pragma unroll
+        for (int c = 0; c < C::MB; ++c) {
+          acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) acc[c] = mma(a[hh][c][kb], bf[kb], acc[c]);
+        }
+        float v[ELL / 4];
+        cache_phi<ELL>(acc, scale, phi, v);
+        const int head = head0 + hh;
+        if constexpr (ELL == 64) {
+          // whole 128-byte lines through the wave's staging rows (as in
+          // qk_cache): lane l stores piece l % 8 of row 8 s + l / 8
+          st8(stage_w + r * 72 + g * 16, v);
+          st8(stage_w + r * 72 + g * 16 + 8, v + 8);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int srow = 8 * s2 + (lane >> 3), piece = lane & 7;
+            const bf16x8 o = *reinterpret_cast<const bf16x8*>(stage_w + srow * 72 + piece * 8);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, o), ro,
+                static_cast<unsigned>(((nb * 16 + srow) * H + head) * ELL * 2 + piece * 16), 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < C::MB / 2; ++q) {
+            bf16x8 o;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = static_cast<__bf16>(v[8 * q + j]);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, o), ro,
+                static_cast<unsigned>((row * H + head) * ELL * 2 + (g * 4 * C::MB + 8 * q) * 2), 0, 0);
+          }
+        }
+      }
+    }
+    b = b == 2 ? 0 : b + 1;
+  }
+  // every wave's loads and stores finish before the workgroup exits (the
+  // last two tiles' loads target no rows and move no data)
+  wait_vm<0>();
 }
 
 // ---------------------------------------------------------------------------

@@ -1757,33 +1757,10 @@ __global__ __launch_bounds__((64 * PostLds<D, DFF>::NW)) void post_block_lds(con
 // ---------------------------------------------------------------------------
 // Weight streaming through LDS by LDS-DMA (d = 256 kernels)
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // A raw buffer descriptor over `elems` bf16 elements at p (gfx9-family
 // word 3: raw 32-bit accesses, no stride); loads past the extent return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const bf16_t* p, int elems) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(p), 0, elems * 2, 0x00020000);
-}
-
-// wait until at most n of this wave's vector memory operations are
-// outstanding (they complete in issue order)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  // gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15)
-  // at their maxima, so only vector memory is waited for
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier for waves that only read the LDS buffers which their
-// own LDS-DMA loads fill: each wave has already waited (vmcnt) for its
-// loads, so the barrier needs no memory fence; a fence would make the
-// compiler wait for every LDS-DMA load in flight, including chunks loaded
-// ahead.  The compiler-only fences keep LDS reads on their side of it.
-__device__ __forceinline__ void dma_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // LN + QKV projection with w_qkv streamed through LDS (d = 256: 384 KB of
