@@ -150,6 +150,28 @@ def test_qk_cache_build_odd_shapes(L, phi):
             assert_close(host_f64(cache), ref, dt, f"qk_cache {dt} {n,d,H,ell}")
 
 
+@pytest.mark.parametrize("shape", [(256, 8, 64), (128, 4, 32), (64, 2, 32)])
+def test_qk_cache_build_persistent_partial_tail(L, shape):
+    """The matrix-core cache build with several item tiles per workgroup and
+    a partial last tile (rows past the catalogue are neither read nor
+    written): three and a bit rounds of 64- or 128-item tiles over a
+    256-slot grid, checked against the oracle on the last rows and a
+    sample, both phi."""
+    d, H, ell = shape
+    rng = np.random.default_rng(11)
+    n = 3 * 256 * 128 + 77
+    items = W.as_storage((rng.standard_normal((n, d)) * d ** -0.5).astype(np.float32), "bf16")
+    keys = W.as_storage(rng.standard_normal((H, ell, d)).astype(np.float32), "bf16")
+    sel = np.unique(np.concatenate([_sample(n, 2048, seed=3), np.arange(n - 300, n)]))
+    for phi in ("softmax", "silu_mean"):
+        print(f"qk_cache persistent tail n={n} d={d} H={H} ell={ell} {phi}", flush=True)
+        cache = L.qk_cache_build(dev(items), dev(keys), phi=phi, scale=32 ** -0.5)
+        torch.cuda.synchronize()
+        ref = O.qk_cache_build(items[sel], keys, 32 ** -0.5, phi)
+        got = host_f64(cache[torch.from_numpy(sel).cuda()])
+        assert_close(got, ref, "bf16", f"qk_cache tail {shape} {phi}")
+
+
 # ------------------------------------------------------------ user side
 
 def _users_for(w, off):
