@@ -1119,15 +1119,21 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == LIME_BF16 && d == 32 * heads) {
     const int64_t ntiles = (total_M + 15) / 16;
-    const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16;
-    int64_t tpw = (ntiles + target_waves - 1) / target_waves;
-    if (tpw < 1) tpw = 1;
-    const int64_t waves = (ntiles + tpw - 1) / tpw;
-    const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
 #define LIME_UC(E, DD, HH)                                                                             \
     if (ell == E && d == DD && heads == HH) {                                                          \
-      constexpr size_t lds = mfma::UcCfg<E, DD, HH>::lds_bytes;                                        \
-      LIME_LAUNCH("cand_score_uncached", (mfma::cand_score_uncached<E, DD, HH>), dim3(grid), dim3(256), lds, s,        \
+      using UC = mfma::UcCfg<E, DD, HH>;                                                               \
+      constexpr size_t lds = UC::lds_bytes;                                                            \
+      /* about 16 waves per CU over all head groups */                                                 \
+      const int64_t target_waves = static_cast<int64_t>(cu_count()) * 16 / UC::NHG;                    \
+      int64_t tpw = (ntiles + target_waves - 1) / target_waves;                                        \
+      if (tpw < 1) tpw = 1;                                                                            \
+      const int64_t waves = (ntiles + tpw - 1) / tpw;                                                  \
+      const dim3 grid(static_cast<unsigned>((waves + 3) / 4), UC::NHG);                                \
+      static const bool attr = hipFuncSetAttribute(                                                    \
+          reinterpret_cast<const void*>(mfma::cand_score_uncached<E, DD, HH>),                         \
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) == hipSuccess;            \
+      (void)attr;                                                                                      \
+      LIME_LAUNCH("cand_score_uncached", (mfma::cand_score_uncached<E, DD, HH>), grid, dim3(256), lds, s,        \
                          static_cast<const bf16_t*>(items), n_items, static_cast<const bf16_t*>(link_keys), \
                          static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B, total_M,   \
                          static_cast<bf16_t*>(out), bad_id_count, scale, static_cast<int>(phi), tpw);  \

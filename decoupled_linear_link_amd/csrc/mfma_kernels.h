@@ -781,16 +781,25 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
 // staged in LDS, phi over the links, then O^T = L^P_h^T P^T as in
 // cand_score.  Link order of the score blocks: M-block c, row 4*g + j ->
 // link (c/2)*32 + 8*g + 4*(c%2) + j, so the probabilities of each lane are
-// the K slices of the value product's B operand.
+// the K slices of the value product's B operand.  A workgroup serves a
+// group of HG heads (the grid's y dimension) whose keys it stages in LDS
+// once, so every score product reads its key fragment from LDS; each head
+// group gathers the candidates' rows itself and writes its own output
+// columns.
 // ---------------------------------------------------------------------------
 template <int ELL, int D, int H>
 struct UcCfg {
   static constexpr int KB = D / 32, MB = ELL / 16, KBL = ELL / 32;
-  static constexpr int LDK = D + 8;  // padded key row
-  // keys staged in LDS when they fit; otherwise read from global (L2)
-  static constexpr bool KLDS = static_cast<size_t>(H) * ELL * LDK * 2 <= 96 * 1024;
-  static constexpr size_t lds_bytes = KLDS ? static_cast<size_t>(H) * ELL * LDK * 2 : 0;
+  static constexpr int LDK = D + 16;  // key row padded by 32 bytes (conflict-free fragment reads)
+  // heads per workgroup: the most whose keys fit 72 KB of LDS (two
+  // workgroups per CU); the head groups are the grid's y dimension
+  static constexpr int HG = static_cast<size_t>(H) * ELL * LDK * 2 <= 72 * 1024       ? H
+                            : static_cast<size_t>(H / 2) * ELL * LDK * 2 <= 72 * 1024 ? H / 2
+                                                                                     : H / 4;
+  static constexpr int NHG = H / HG;
+  static constexpr size_t lds_bytes = static_cast<size_t>(HG) * ELL * LDK * 2;
   static_assert(D == 32 * H && ELL % 32 == 0, "shape");
+  static_assert(H % HG == 0 && HG >= 1 && lds_bytes <= 72 * 1024, "head groups");
 };
 
 template <int ELL, int D, int H>
@@ -800,26 +809,22 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
     int B, int64_t total_M, bf16_t* __restrict__ out, int* bad, float scale, int phi,
     int64_t tiles_per_wave) {
   using C = UcCfg<ELL, D, H>;
-  constexpr int KB = C::KB, MB = C::MB, KBL = C::KBL, LDK = C::LDK;
-  (void)LDK;
+  constexpr int KB = C::KB, MB = C::MB, KBL = C::KBL, LDK = C::LDK, HG = C::HG;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
-  const bf16_t* Ks;
-  int ldk;
-  if constexpr (C::KLDS) {
+  // this workgroup's heads [h0, h0 + HG): their keys staged in LDS once
+  const int h0 = static_cast<int>(blockIdx.y) * HG;
+  {
     bf16_t* ks = reinterpret_cast<bf16_t*>(smem);
-    for (int e = tid; e < H * ELL * (D / 8); e += 256) {
+    const bf16_t* kg = keys + static_cast<int64_t>(h0) * ELL * D;
+    for (int e = tid; e < HG * ELL * (D / 8); e += 256) {
       const int row = e / (D / 8), c8 = e % (D / 8);
-      *reinterpret_cast<bf16x8*>(ks + row * LDK + 8 * c8) = ld16(keys + static_cast<int64_t>(row) * D + 8 * c8);
+      *reinterpret_cast<bf16x8*>(ks + row * LDK + 8 * c8) = ld16(kg + static_cast<int64_t>(row) * D + 8 * c8);
     }
     lds_barrier();
-    Ks = ks;
-    ldk = LDK;
-  } else {
-    Ks = keys;
-    ldk = D;
   }
+  const bf16_t* const Ks = reinterpret_cast<const bf16_t*>(smem);
   const bool softmax = (phi == PHI_SOFTMAX);
   const float k2 = scale * LOG2E;
   const int64_t ntiles = (total_M + 15) >> 4;
@@ -828,7 +833,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
   const int64_t t1 = t0 + tiles_per_wave < ntiles ? t0 + tiles_per_wave : ntiles;
   if (t0 >= t1) return;
 
-  bf16x8 a[H][2][KBL];
+  bf16x8 a[HG][2][KBL];
   int cur = -1;
   int u = find_owner(off, B, t0 * 16);
   for (int64_t t = t0; t < t1; ++t) {
@@ -839,21 +844,21 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
       while (ul + 1 < B && off[ul + 1] <= i) ++ul;
     const int64_t id = valid ? ids[i] : -1;
     const bool okid = valid && id >= 0 && id < n_items;
-    if (valid && !okid && g == 0 && bad != nullptr) atomicAdd(bad, 1);
+    if (valid && !okid && g == 0 && bad != nullptr && blockIdx.y == 0) atomicAdd(bad, 1);
     bf16x8 tb[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) tb[kb] = okid ? ld16(items + id * D + kb * 32 + 8 * g) : zero8();
 
     // probabilities per head as B operands of the value product
     const bf16_t* Kt = Ks + opaque_zero();
-    bf16x8 pb[H][KBL];
+    bf16x8 pb[HG][KBL];
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
+    for (int h = 0; h < HG; ++h) {
       float v[4 * MB];
 #pragma unroll
       for (int c = 0; c < MB; ++c) {
         const int link = (c >> 1) * 32 + 8 * (r >> 2) + 4 * (c & 1) + (r & 3);
-        const bf16_t* kr = Kt + (h * ELL + link) * ldk + 8 * g;
+        const bf16_t* kr = Kt + (h * ELL + link) * LDK + 8 * g;
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) acc = mma(ld16(kr + kb * 32), tb[kb], acc);
@@ -897,10 +902,10 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
       if (uu != cur) {
         const bf16_t* lb = lp + static_cast<int64_t>(uu) * ELL * D;
 #pragma unroll
-        for (int h = 0; h < H; ++h)
+        for (int h = 0; h < HG; ++h)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            const int col = h * 32 + 8 * (r >> 2) + 4 * c + (r & 3);
+            const int col = (h0 + h) * 32 + 8 * (r >> 2) + 4 * c + (r & 3);
 #pragma unroll
             for (int kb = 0; kb < KBL; ++kb)
 #pragma unroll
@@ -911,7 +916,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
       }
       const bool mine = valid && ul == uu;
 #pragma unroll
-      for (int h = 0; h < H; ++h) {
+      for (int h = 0; h < HG; ++h) {
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBL; ++kb) {
@@ -922,7 +927,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
           const float zf = okid ? 1.f : 0.f;  // out-of-range ids give zero rows
           const float v[8] = {acc0[0] * zf, acc0[1] * zf, acc0[2] * zf, acc0[3] * zf,
                               acc1[0] * zf, acc1[1] * zf, acc1[2] * zf, acc1[3] * zf};
-          st8_stream(out + i * D + h * 32 + 8 * g, v);
+          st8_stream(out + i * D + (h0 + h) * 32 + 8 * g, v);
         }
       }
     }

@@ -46,8 +46,11 @@ def test_uncached_scoring(L, name):
 @pytest.mark.parametrize("phi", ["softmax", "silu_mean"])
 def test_uncached_ragged_users_bad_ids(L, phi):
     rng = np.random.default_rng(41)
+    # (the matrix-core shapes take their heads in groups whose keys fit
+    # LDS: 64, 256, 8 in four groups, 32, 256, 8 and 64, 128, 4 in two)
     for dt, B, ell, d, H, n in (("bf16", 21, 32, 64, 2, 300), ("bf16", 9, 32, 128, 4, 100),
-                                ("f32", 5, 7, 48, 3, 60), ("bf16", 6, 64, 256, 8, 50)):
+                                ("f32", 5, 7, 48, 3, 60), ("bf16", 6, 64, 256, 8, 50),
+                                ("bf16", 7, 32, 256, 8, 40), ("bf16", 5, 64, 128, 4, 70)):
         counts = rng.integers(0, 30, size=B)
         counts[1] = 0
         coff = W.offsets_from_lengths(counts)
