@@ -410,10 +410,12 @@ lime_status_t run_xor_mfma(const XorPlan& P, lime_phi_t phi, float scale, int B,
   int32_t* suser = reinterpret_cast<int32_t*>(ws + P.o_suser);
   const int64_t nlr = P.nlr, R = P.R;
   const Rows Xws{X, X + nlr * D, nlr, D};
-  // d = 256, LIME-XOR: the projection runs inside the attention, from the
-  // LayerNorm rows the previous post block stored (the first layer
-  // normalises the input rows itself)
-  const bool fused_h = D == 256 && va.half == 0 && !va.links_only;
+  // d = 256 without the window: the projection runs inside the attention,
+  // from the LayerNorm rows the previous post block stored (the first layer
+  // normalises the input rows itself).  LIME-MHA runs every layer in the
+  // links-only form of the last LIME-XOR layer; its history rows, never
+  // updated, keep the first layer's LayerNorm rows.
+  const bool fused_h = D == 256 && va.half == 0;
   bf16_t* LNr = fused_h ? reinterpret_cast<bf16_t*>(ws + P.o_ln) : nullptr;
   const Rows LNrows{LNr, LNr + nlr * D, nlr, D};
   void* lops = fused_h ? ws + P.o_lops : nullptr;
