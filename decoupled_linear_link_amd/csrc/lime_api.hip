@@ -1130,12 +1130,12 @@ lime_status_t lime_cand_score_uncached(lime_dtype_t dtype, lime_phi_t phi, float
       int64_t tpw = (ntiles + target_waves - 1) / target_waves;                                        \
       if (tpw < 1) tpw = 1;                                                                            \
       const int64_t waves = (ntiles + tpw - 1) / tpw;                                                  \
-      const dim3 grid(static_cast<unsigned>((waves + 3) / 4), UC::NHG);                                \
+      const dim3 grid(static_cast<unsigned>((waves + UC::NW - 1) / UC::NW), UC::NHG);                  \
       static const bool attr = hipFuncSetAttribute(                                                    \
           reinterpret_cast<const void*>(mfma::cand_score_uncached<E, DD, HH>),                         \
           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) == hipSuccess;            \
       (void)attr;                                                                                      \
-      LIME_LAUNCH("cand_score_uncached", (mfma::cand_score_uncached<E, DD, HH>), grid, dim3(256), lds, s,        \
+      LIME_LAUNCH("cand_score_uncached", (mfma::cand_score_uncached<E, DD, HH>), grid, dim3(UC::NT), lds, s,        \
                          static_cast<const bf16_t*>(items), n_items, static_cast<const bf16_t*>(link_keys), \
                          static_cast<const bf16_t*>(links_pers), cand_ids, cand_offsets, B, total_M,   \
                          static_cast<bf16_t*>(out), bad_id_count, scale, static_cast<int>(phi), tpw);  \

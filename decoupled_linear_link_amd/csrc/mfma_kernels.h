@@ -785,25 +785,26 @@ __global__ __launch_bounds__(256) void cand_score(const void* __restrict__ cache
 // group of HG heads (the grid's y dimension) whose keys it stages in LDS
 // once, so every score product reads its key fragment from LDS; each head
 // group gathers the candidates' rows itself and writes its own output
-// columns.
+// columns.  Each wave walks its own range of tiles.
 // ---------------------------------------------------------------------------
 template <int ELL, int D, int H>
 struct UcCfg {
   static constexpr int KB = D / 32, MB = ELL / 16, KBL = ELL / 32;
   static constexpr int LDK = D + 16;  // key row padded by 32 bytes (conflict-free fragment reads)
-  // heads per workgroup: the most whose keys fit 72 KB of LDS (two
-  // workgroups per CU); the head groups are the grid's y dimension
-  static constexpr int HG = static_cast<size_t>(H) * ELL * LDK * 2 <= 72 * 1024       ? H
-                            : static_cast<size_t>(H / 2) * ELL * LDK * 2 <= 72 * 1024 ? H / 2
-                                                                                     : H / 4;
+  // heads per workgroup: the most whose keys fit 144 KB of LDS; the head
+  // groups are the grid's y dimension.  Keys over 72 KB leave one
+  // workgroup per CU, which then has 8 waves instead of 4.
+  static constexpr size_t KEYB = static_cast<size_t>(ELL) * LDK * 2;  // bytes per head
+  static constexpr int HG = H * KEYB <= 144 * 1024 ? H : (H / 2) * KEYB <= 144 * 1024 ? H / 2 : H / 4;
   static constexpr int NHG = H / HG;
-  static constexpr size_t lds_bytes = static_cast<size_t>(HG) * ELL * LDK * 2;
+  static constexpr size_t lds_bytes = static_cast<size_t>(HG) * KEYB;
+  static constexpr int NW = lds_bytes > 72 * 1024 ? 8 : 4, NT = 64 * NW;
   static_assert(D == 32 * H && ELL % 32 == 0, "shape");
-  static_assert(H % HG == 0 && HG >= 1 && lds_bytes <= 72 * 1024, "head groups");
+  static_assert(H % HG == 0 && HG >= 1 && lds_bytes <= 144 * 1024, "head groups");
 };
 
 template <int ELL, int D, int H>
-__global__ __launch_bounds__(256) void cand_score_uncached(
+__global__ __launch_bounds__((UcCfg<ELL, D, H>::NT)) void cand_score_uncached(
     const bf16_t* __restrict__ items, int64_t n_items, const bf16_t* __restrict__ keys,
     const bf16_t* __restrict__ lp, const int64_t* __restrict__ ids, const int64_t* __restrict__ off,
     int B, int64_t total_M, bf16_t* __restrict__ out, int* bad, float scale, int phi,
@@ -818,7 +819,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
   {
     bf16_t* ks = reinterpret_cast<bf16_t*>(smem);
     const bf16_t* kg = keys + static_cast<int64_t>(h0) * ELL * D;
-    for (int e = tid; e < HG * ELL * (D / 8); e += 256) {
+    for (int e = tid; e < HG * ELL * (D / 8); e += C::NT) {
       const int row = e / (D / 8), c8 = e % (D / 8);
       *reinterpret_cast<bf16x8*>(ks + row * LDK + 8 * c8) = ld16(kg + static_cast<int64_t>(row) * D + 8 * c8);
     }
@@ -828,7 +829,7 @@ __global__ __launch_bounds__(256) void cand_score_uncached(
   const bool softmax = (phi == PHI_SOFTMAX);
   const float k2 = scale * LOG2E;
   const int64_t ntiles = (total_M + 15) >> 4;
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (tid >> 6);
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * C::NW + (tid >> 6);
   const int64_t t0 = gw * tiles_per_wave;
   const int64_t t1 = t0 + tiles_per_wave < ntiles ? t0 + tiles_per_wave : ntiles;
   if (t0 >= t1) return;
