@@ -420,8 +420,8 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H, I8>::NT)) void qk_cache(
 // travel global -> LDS by LDS-DMA loads (16 bytes per lane, no registers)
 // into three buffers, so tiles t + 1 and t + 2 load while tile t is
 // computed; one barrier per tile.  Rows are unpadded, with their 16-byte
-// slots XOR-swizzled by the row's low bits so that a fragment read (16
-// consecutive rows, one slot each) meets distinct banks.  Each tile has its
+// slots XOR-swizzled by the row's low bits, so that the 16 consecutive rows
+// of a fragment read start their slot in 16 different bank groups.  Each tile has its
 // own buffer descriptors for the item rows it reads and the cache rows it
 // writes: rows past the catalogue load as 0 and their stores are dropped,
 // so every wave issues the same loads and stores for every tile and the
