@@ -517,10 +517,12 @@ __global__ __launch_bounds__((QkCfg<ELL, D, H, false>::NT)) void qk_cache_dma(
       const int nb = nb0 + nbi;
       const int row = nb * 16 + r;
       const int sw = qk_swz(row, Q::SPR);
+      // all of the block's fragment reads in flight before its products
       bf16x8 bf[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
         bf[kb] = *reinterpret_cast<const bf16x8*>(buf + row * Q::ROWB + ((kb * 4 + g) ^ sw) * 16);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int hh = 0; hh < C::HPW; ++hh) {
         floatx4 acc[C::MB];
