@@ -1518,8 +1518,10 @@ __global__ __launch_bounds__(256) void ln_rows_kernel(Rows X, int64_t R, bf16_t*
 }
 
 // DO_E: the layer also updates history rows (the E-branch).  Without it
-// (a last layer) Q_E, K_L and V_L are dead, and the freed registers hold a
-// second operand buffer: the rows are loaded two chunks ahead.
+// (a last layer) Q_E, K_L and V_L are dead, and at l = 32 the freed
+// registers hold a second operand buffer: the rows are loaded two chunks
+// ahead (at l = 64 the second buffer would not fit the 256 registers of a
+// wave without spilling).
 template <int ELL, bool LNX, bool DO_E>
 __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __restrict__ W,
                                                   const void* __restrict__ lops, bf16_t* __restrict__ Y,
@@ -1617,7 +1619,7 @@ __global__ __launch_bounds__(512) void xor_attn_h(Rows src, const bf16_t* __rest
       l_branch<ELL, SM>(st, o, ci, c0, lo, hi, r, g);
       __builtin_amdgcn_s_setprio(0);
     };
-    if constexpr (DO_E) {
+    if constexpr (DO_E || ELL > 32) {
       // one chunk ahead, into the operand registers the projections have
       // just freed, while this chunk's attention runs
       Ops hb;
